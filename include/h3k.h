@@ -1,0 +1,228 @@
+/*
+ * h3k — W8A8 DiT block forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library libh3k.so. The operation is the forward pass of one DiT
+ * transformer block of the MiniMax-H3 video/audio denoiser, run at every denoising
+ * step, as described by the pages:
+ *   - "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "Int8 양자화"
+ *     (native int8 MLP with dynamic activation quantisation and per-output-channel
+ *     weight scales; int8 QKV; the QKV and MLP activation quantisers folded into the
+ *     preceding gated AdaLN kernel), section "Metal 4 및 TensorOps" (QKV and
+ *     attention-output projections routed straight into head-major attention inputs),
+ *     and the "속도 및 품질 트레이드오프" table (50 blocks; token reduction pairs
+ *     horizontal video tokens in the middle blocks);
+ *   - "맥북에서 AI 영상 생성 모델 돌리기 - MiniMax H3 로컬 실행과 30초 애니메이션 만들기",
+ *     section "int8 이 뭔가요" (one F32 scale per weight output channel, activations
+ *     quantised on the fly with one F32 scale per row);
+ *   - "MiniMax-H3在Apple Silicon上的兩種推理實現工程取舍", section 性能上限 (AdaLN gating,
+ *     RoPE and quantisation folded into the preceding kernel).
+ *
+ * Block equations (the pages name the parts; the plainest consistent reading is used):
+ *   m = W_ada c = [shift1 | scale1 | gate1 | shift2 | scale2 | gate2]      (6 x d)
+ *   h  = LN(x)(1 + scale1) + shift1;     (qa, sa) = quant(h)
+ *   [Q|K|V] = (qa Wqkv^T) sa sw;  Q, K <- 3D RoPE;  O = softmax(Q K^T / sqrt(Dh)) V
+ *   x1 = x + gate1 * dequant(quant(O) Wo^T)
+ *   h2 = LN(x1)(1 + scale2) + shift2;    g = GELU(dequant(quant(h2) Wup^T))
+ *   x2 = x1 + gate2 * dequant(quant(g) Wdown^T)
+ * LN: LayerNorm without affine, eps from h3k_dims. quant: symmetric per-row int8,
+ * s = max|v| / 127 (fp32), q = clamp(rint(v * (127 / max|v|)), -127, 127); a zero row
+ * gets s = 0. GELU: exact erf form. RoPE: interleaved pairs (2i, 2i+1); the Dh/2 pairs
+ * are split over the token's (t, h, w) grid position: t takes Dh/2 - 2*floor(Dh/6)
+ * pairs, h and w floor(Dh/6) each; pair j of an axis with P pairs turns by
+ * pos * theta^(-j/P). Tokens are ordered l = (t*Hg + h)*Wg + w.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must be device memory of the current HIP device
+ *     (for example torch allocations), 16-byte aligned. The caller owns every buffer;
+ *     the library allocates no caller-visible memory and keeps no state between calls
+ *     except its profiling records.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work and return
+ *     at once; results are ready when the stream reaches them.
+ *   - Arguments are validated on the host before any launch. A failed call returns a
+ *     negative code, enqueues nothing and sets a thread-local message readable with
+ *     h3k_last_error(). NaN and Inf are not checked; they propagate.
+ *   - Matrices are row-major. Weights are [N_out, K_in] (K contiguous). bf16 is stored as
+ *     its 16-bit pattern (uint16); fp32 as IEEE float.
+ *   - Calls on different streams are independent only if their outputs and workspaces
+ *     are disjoint.
+ */
+#ifndef H3K_H
+#define H3K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+enum {
+  H3K_OK = 0,
+  H3K_EINVAL = -1,       /* null or misaligned pointer, inconsistent sizes           */
+  H3K_EUNSUPPORTED = -2, /* valid but unsupported shape (head_dim, d % 256, ...)     */
+  H3K_ENOSPC = -3,       /* workspace smaller than h3k_workspace_bytes() asks         */
+  H3K_EHIP = -4          /* a HIP runtime call or kernel launch failed               */
+};
+
+/* flags for the block and stack calls */
+enum {
+  H3K_F_BF16_GEMM = 1u,  /* no activation quantisation: bf16 x bf16 GEMMs on the dense
+                            bf16 weights wb_* (the pages' BF16 baseline)              */
+  H3K_F_FP32_DEBUG = 2u, /* fp32 activations end to end (x_in/x_out fp32), same int8
+                            GEMMs, fp32 attention without matrix cores               */
+  H3K_F_SYNC = 4u        /* synchronise the stream and check for errors after every
+                            launch (debugging)                                        */
+};
+
+/* element types */
+enum { H3K_DT_F32 = 0, H3K_DT_BF16 = 1 };
+
+typedef struct {
+  int32_t d;          /* model width = n_heads * head_dim; multiple of 256            */
+  int32_t n_heads;
+  int32_t head_dim;   /* 64 or 128                                                     */
+  int32_t d_ff;       /* MLP width; multiple of 256                                    */
+  int32_t d_cond;     /* conditioning width; multiple of 8, at most 8192              */
+  int32_t grid_t, grid_h, grid_w; /* token grid; L must equal their product          */
+  float rope_theta;   /* 10000                                                          */
+  float ln_eps;       /* 1e-6                                                           */
+} h3k_dims;
+
+/* One block's weights: all device pointers. */
+typedef struct {
+  const uint16_t *w_ada;   /* bf16 [6d, d_cond]: the AdaLN modulation linear layer     */
+  const int8_t *w_qkv;     /* int8 [3d, d]: rows Q | K | V; head e owns rows
+                              e*Dh..(e+1)*Dh-1 of each part                             */
+  const float *s_qkv;      /* fp32 [3d]: per-output-channel scales                      */
+  const int8_t *w_o;       /* int8 [d, d]   */
+  const float *s_o;        /* fp32 [d]      */
+  const int8_t *w_up;      /* int8 [F, d]   */
+  const float *s_up;       /* fp32 [F]      */
+  const int8_t *w_down;    /* int8 [d, F]   */
+  const float *s_down;     /* fp32 [d]      */
+  const uint16_t *wb_qkv;  /* bf16 originals, read only under H3K_F_BF16_GEMM; else NULL */
+  const uint16_t *wb_o;
+  const uint16_t *wb_up;
+  const uint16_t *wb_down;
+} h3k_block_weights;
+
+/* Byte offsets of the intermediates inside a block workspace (for inspection). Arrays
+ * use the block's activation type T (bf16, or fp32 under H3K_F_FP32_DEBUG). */
+typedef struct {
+  size_t m;          /* fp32 [6d] modulation                                          */
+  size_t rope;       /* fp32 rotation table (internal layout)                         */
+  size_t s_a, s_o, s_a2, s_g;   /* fp32 [L] per-token scales of the four quantisers     */
+  size_t qa, qo, qa2;           /* int8 [L, d]                                          */
+  size_t qg;                    /* int8 [L, F]                                          */
+  size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied                */
+  size_t vt;                    /* T [H, Dh, L] head-major, transposed                  */
+  size_t o;                     /* T [L, d] attention output, head e in columns e*Dh..  */
+  size_t g;                     /* T [L, F] GELU output                                 */
+  size_t h, h2;                 /* bf16 [L, d] modulated activations (H3K_F_BF16_GEMM) */
+  size_t total;                 /* bytes needed (= h3k_workspace_bytes)                */
+} h3k_ws_layout;
+
+/* S0. Per-output-channel int8 weight quantisation of w [n_out, k_in] (device; bf16 or
+ * fp32 per w_dtype): scale_out[n] = max_k |w[n,k]| / 127, q_out[n,k] =
+ * clamp(rint(w[n,k] * (127 / max_k |w[n,k]|)), -127, 127), decisions in fp32.
+ * q_out int8 [n_out, k_in], scale_out fp32 [n_out] (device). k_in % 8 == 0. */
+int h3k_quantize_weights(const void *w, int w_dtype, int64_t n_out, int64_t k_in,
+                         int8_t *q_out, float *scale_out, void *stream);
+
+/* Workspace bytes one h3k_block_forward call needs for L tokens under `flags`
+ * (0 on invalid dims). */
+size_t h3k_workspace_bytes(const h3k_dims *dm, int64_t L, uint32_t flags);
+
+/* Fills *out with the workspace layout for (dm, L, flags). Returns H3K_OK or an error. */
+int h3k_workspace_layout(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *out);
+
+/* One DiT block forward. x_in, x_out: [L, d] bf16 (fp32 under H3K_F_FP32_DEBUG),
+ * device; x_out may alias x_in. cond: fp32 [d_cond] device. w: host pointer to a struct
+ * of device pointers. L == grid_t*grid_h*grid_w. ws: device workspace of at least
+ * h3k_workspace_bytes(dm, L, flags) bytes; after the call it holds the intermediates at
+ * the offsets of h3k_workspace_layout. */
+int h3k_block_forward(const void *x_in, void *x_out, const float *cond,
+                      const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
+                      uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* S4. Multi-head softmax attention without mask, bf16 MFMA with fp32 online softmax:
+ * o[l, e*Dh + j] = sum_k softmax_k(q[e,l,:] . k[e,k,:] * softmax_scale) v[e,k,j].
+ * q, k: bf16 [H, L, Dh]; v: bf16 [H, Dh, L] (transposed, as the QKV projection writes
+ * it); o: bf16 [L, H*Dh]. All device. head_dim 64 or 128. With H3K_F_FP32_DEBUG in
+ * flags every array is fp32 instead and no matrix cores are used. */
+int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
+                  int64_t L, int32_t head_dim, float softmax_scale, uint32_t flags,
+                  void *stream);
+
+/* Workspace bytes for h3k_stack_forward (block workspace plus two reduced-token
+ * buffers when tr_begin < tr_end). */
+size_t h3k_stack_workspace_bytes(const h3k_dims *dm, int64_t L, int32_t tr_begin,
+                                 int32_t tr_end, uint32_t flags);
+
+/* A stack of n_blocks blocks sharing cond; blocks: host array of n_blocks weight structs.
+ * Blocks [tr_begin, tr_end) run on horizontally paired tokens: before tr_begin,
+ * xr[t,h,j] = (x[t,h,2j] + x[t,h,2j+1]) / 2 on the (T, Hg, Wg/2) grid with w positions
+ * 2j + 0.5; after tr_end - 1, x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out - xr_in)[t,h,j].
+ * tr_begin == tr_end disables pairing; it needs an even grid_w and
+ * 0 <= tr_begin <= tr_end <= n_blocks. x_out may alias x_in. */
+int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
+                      const h3k_block_weights *blocks, int32_t n_blocks,
+                      const h3k_dims *dm, int64_t L, int32_t tr_begin, int32_t tr_end,
+                      uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- single steps of the block (the same kernels the block call launches) ---- */
+
+/* S1. m[i] = sum_j w_ada[i, j] * cond[j], fp32 accumulation. w_ada bf16 [n_out, d_cond],
+ * cond fp32 [d_cond], m fp32 [n_out]; device. d_cond % 8 == 0, d_cond <= 8192. */
+int h3k_adaln_modulation(const uint16_t *w_ada, const float *cond, float *m,
+                         int64_t n_out, int32_t d_cond, void *stream);
+
+/* S2/S7. Per row l of x [rows, cols] (x_dtype): h = LN(x_l)(1 + scale) + shift in fp32,
+ * then per-row int8 quantisation of h: q_out int8 [rows, cols], s_out fp32 [rows].
+ * shift, scale: fp32 [cols]. cols % 256 == 0, cols <= 8192. */
+int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift,
+                          const float *scale, int64_t rows, int32_t cols, float eps,
+                          int8_t *q_out, float *s_out, void *stream);
+
+/* S5/S9. Per-row int8 quantisation of x [rows, cols] (x_dtype) into q_out, s_out.
+ * cols % 8 == 0, cols <= 32768. */
+int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols,
+                     int8_t *q_out, float *s_out, void *stream);
+
+/* The int8 GEMM main loop with a raw epilogue: c[m, n] = sum_k a[m, k] * b[n, k] in
+ * int32 (exact). a int8 [M, K], b int8 [N, K], c int32 [M, N]; device. N % 256 == 0,
+ * K % 128 == 0, M >= 1. */
+int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
+                    int64_t K, void *stream);
+
+/* S11. Horizontal pairing of x [T*Hg*Wg, d] (x_dtype) into xr and xr_copy
+ * [T*Hg*(Wg/2), d]: xr[t,h,j] = (x[t,h,2j] + x[t,h,2j+1]) / 2 (fp32 add, rounded once). */
+int h3k_token_pair(const void *x, void *xr, void *xr_copy, int x_dtype, int32_t T,
+                   int32_t Hg, int32_t Wg, int32_t d, void *stream);
+
+/* S12. x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out[t,h,j] - xr_in[t,h,j]) for s in {0,1},
+ * in place on x_pre (fp32 arithmetic, rounded once). */
+int h3k_token_unpair(void *x_pre, const void *xr_out, const void *xr_in, int x_dtype,
+                     int32_t T, int32_t Hg, int32_t Wg, int32_t d, void *stream);
+
+/* Thread-local message describing the last failed call on this thread ("" if none). */
+const char *h3k_last_error(void);
+
+/* ---- profiling: per-kernel HIP event timing inside block and stack calls ---- */
+enum {
+  H3K_K_ADALN = 0, H3K_K_ROPE_TABLE, H3K_K_LN_QUANT, H3K_K_GEMM_QKV, H3K_K_ATTENTION,
+  H3K_K_ROWQUANT_O, H3K_K_GEMM_O, H3K_K_GEMM_UP, H3K_K_ROWQUANT_G, H3K_K_GEMM_DOWN,
+  H3K_K_TOKEN_PAIR, H3K_K_TOKEN_UNPAIR, H3K_K_COUNT
+};
+/* While enabled, every kernel the block and stack calls launch is bracketed by two HIP
+ * events recorded on the call's stream. Enabling clears earlier records. */
+int h3k_profile_enable(int on);
+/* Waits for the recorded events and returns, for kernel kind `kind`, the number of
+ * launches recorded and their summed duration in milliseconds. */
+int h3k_profile_read(int kind, int64_t *count, double *total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H3K_H */

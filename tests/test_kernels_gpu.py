@@ -1,0 +1,170 @@
+"""Per-kernel parity of the HIP path against the CPU oracle on identical seeded inputs.
+Quantisers: codes identical on >= 99.99% of elements (off by at most one step), scales
+within 1e-6 relative. int32 GEMM accumulators: bit-exact. Attention: relative L2."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests._util import code_match, np64, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+h3k = pytest.importorskip("video_diffusion_transformer_03_amd.h3k")
+
+
+def _gen(seed):
+    g = torch.Generator()
+    g.manual_seed(seed)
+    return g
+
+
+def randn(shape, seed, std=1.0, dtype=torch.bfloat16):
+    return (torch.randn(*shape, generator=_gen(seed)) * std).to(dtype)
+
+
+# ----------------------------------------------------------------------------- S0 weights
+@pytest.mark.parametrize("n,k,dtype", [(384, 5120, torch.bfloat16), (256, 20480, torch.bfloat16),
+                                       (97, 1000, torch.float32), (3, 8, torch.bfloat16)])
+def test_quantize_weights(n, k, dtype):
+    w = randn((n, k), 11, 0.02, dtype)
+    w[1 % n] = 0  # zero row
+    w[0, 5] = 0.7  # outlier
+    q, s = h3k.quantize_weights(w.cuda())
+    qr, sr = O.quantize_weights(np64(w))
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+def test_quantize_golden_ties():
+    rows = [[127, 62.5, -61.5, 0.5, 1.5, -2.5, 3.25, -0.75],
+            [-127, 126.5, -126.5, 63.5, -63.5, 0, 0, 0]]
+    q, s = h3k.quantize_weights(torch.tensor(rows, dtype=torch.float32).cuda())
+    assert q.cpu().tolist() == [[127, 62, -62, 0, 2, -2, 3, -1], [-127, 126, -126, 64, -64, 0, 0, 0]]
+    assert s.cpu().tolist() == [1.0, 1.0]
+
+
+# ----------------------------------------------------------------------------- S1 AdaLN
+@pytest.mark.parametrize("n_out,dc", [(6 * 256, 256), (6 * 5120, 5120), (40, 8)])
+def test_adaln_modulation(n_out, dc):
+    w = randn((n_out, dc), 3, 0.02)
+    c = randn((dc,), 4, 1.0, torch.float32)
+    m = h3k.adaln_modulation(w.cuda(), c.cuda()).cpu().numpy()
+    mr = O.adaln_modulation(np64(w), np64(c))
+    assert rel_l2(m, mr) < 1e-6
+    assert np.max(np.abs(m - mr)) < 1e-5 * max(1.0, np.abs(mr).max())
+
+
+# ----------------------------------------------------------------------------- S2/S7 LN + quant
+@pytest.mark.parametrize("rows,cols,dtype", [(300, 256, torch.bfloat16), (257, 5120, torch.bfloat16),
+                                             (64, 8192, torch.bfloat16), (100, 5120, torch.float32)])
+def test_ln_modulate_quant(rows, cols, dtype):
+    x = randn((rows, cols), 5, 1.0, dtype)
+    x[:, 7] *= 20  # outlier channel
+    x[3] = 2.5     # constant row: LN gives 0, h = shift
+    sh = randn((cols,), 6, 1.4, torch.float32)
+    sc = randn((cols,), 7, 1.4, torch.float32)
+    q, s = h3k.ln_modulate_quant(x.cuda(), sh.cuda(), sc.cuda(), 1e-6)
+    h = O.modulate(O.layer_norm(np64(x)), np64(sh), np64(sc))
+    qr, sr = O.quantize_rows(h)
+    frac, mx = code_match(q.cpu().numpy(), qr)
+    assert frac >= 0.9999 and mx <= 1, (frac, mx)
+    assert np.allclose(s.cpu().numpy(), sr, rtol=1e-6, atol=0)
+
+
+# ----------------------------------------------------------------------------- S5/S9 row quant
+@pytest.mark.parametrize("rows,cols,dtype", [(129, 5120, torch.bfloat16), (33, 20480, torch.bfloat16),
+                                             (50, 1024, torch.float32), (5, 32768, torch.bfloat16)])
+def test_row_quantize(rows, cols, dtype):
+    x = randn((rows, cols), 8, 3.0, dtype)
+    x[2] = 0
+    q, s = h3k.row_quantize(x.cuda())
+    qr, sr = O.quantize_rows(np64(x))
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(s.cpu().numpy(), sr)
+
+
+# ----------------------------------------------------------------------------- int8 GEMM
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (100, 768, 640), (1000, 512, 5120),
+                                   (4096, 1536, 1024), (333, 256, 20480)])
+def test_gemm_i8_exact(M, N, K):
+    g = _gen(M * 7 + N)
+    a = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int8)
+    b = torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8)
+    c = h3k.gemm_i8_i32(a.cuda(), b.cuda()).cpu().numpy()
+    ref = O.int8_matmul(a.numpy(), b.numpy())
+    assert np.array_equal(c.astype(np.int64), ref)
+
+
+def test_gemm_i8_extremes():
+    K = 20480
+    a = torch.full((17, K), -127, dtype=torch.int8)
+    b = torch.full((256, K), 127, dtype=torch.int8)
+    b[1, ::2] = -127
+    c = h3k.gemm_i8_i32(a.cuda(), b.cuda()).cpu().numpy()
+    assert np.all(c[:, 0] == -127 * 127 * K) and np.all(c[:, 1] == 0)
+    assert np.array_equal(c.astype(np.int64), O.int8_matmul(a.numpy(), b.numpy()))
+
+
+# ----------------------------------------------------------------------------- attention
+@pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 200, 128), (3, 1000, 64), (1, 4096, 128)])
+def test_attention_bf16(H, L, Dh):
+    q = randn((H, L, Dh), 21, 1.0)
+    k = randn((H, L, Dh), 22, 1.0)
+    v = randn((H, L, Dh), 23, 1.0)
+    vt = v.transpose(1, 2).contiguous()
+    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).float().cpu().numpy()
+    ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
+                      np64(v).transpose(1, 0, 2)).reshape(L, H * Dh)
+    err = rel_l2(o, ref)
+    assert err < 1e-2, err
+
+
+@pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 264, 128)])
+def test_attention_fp32(H, L, Dh):
+    q = randn((H, L, Dh), 31, 1.0, torch.float32)
+    k = randn((H, L, Dh), 32, 1.0, torch.float32)
+    v = randn((H, L, Dh), 33, 1.0, torch.float32)
+    o = h3k.attention(q.cuda(), k.cuda(), v.transpose(1, 2).contiguous().cuda(),
+                      flags=h3k.F_FP32_DEBUG).cpu().numpy()
+    ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
+                      np64(v).transpose(1, 0, 2)).reshape(L, H * Dh)
+    assert rel_l2(o, ref) < 1e-5
+
+
+def test_attention_constant_v():
+    H, L, Dh = 2, 136, 64
+    q = randn((H, L, Dh), 41, 2.0)
+    k = randn((H, L, Dh), 42, 2.0)
+    row = randn((H, 1, Dh), 43, 1.0)
+    vt = row.expand(H, L, Dh).transpose(1, 2).contiguous()
+    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).float().cpu().numpy().reshape(L, H, Dh)
+    want = np64(row)[:, 0, :]
+    assert np.allclose(o, np.broadcast_to(want, o.shape), rtol=1e-2, atol=1e-2)
+
+
+# ----------------------------------------------------------------------------- token pairing
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_token_pair_unpair(dtype):
+    grid = (3, 5, 8)
+    d = 256
+    x = randn((120, d), 51, 1.0, dtype)
+    xr, xr2 = h3k.token_pair(x.cuda(), grid)
+    ref = O.token_pair(np64(x), grid)
+    want = torch.tensor(ref, dtype=torch.float32).to(dtype).float().numpy()
+    got = xr.float().cpu().numpy()
+    assert np.mean(got == want) >= 0.9999
+    assert np.allclose(got, want, rtol=1e-2 if dtype == torch.bfloat16 else 1e-6, atol=0)
+    assert torch.equal(xr, xr2)
+    # unpair with an unchanged reduced state is the identity, bit for bit
+    xp = x.cuda().clone()
+    h3k.token_unpair(xp, xr, xr2, grid)
+    assert torch.equal(xp.cpu(), x)
+    delta = randn((60, d), 52, 0.1, dtype)
+    xo = (xr.float() + delta.cuda().float()).to(dtype)
+    xp = x.cuda().clone()
+    h3k.token_unpair(xp, xo, xr, grid)
+    ref = O.token_unpair(np64(x), np64(xo), np64(xr), grid)
+    assert rel_l2(xp.float().cpu().numpy(), ref) < (4e-3 if dtype == torch.bfloat16 else 1e-7)

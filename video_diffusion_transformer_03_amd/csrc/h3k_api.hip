@@ -1,0 +1,605 @@
+// Host side of libh3k.so: argument validation, workspace planning, the block and stack
+// sequences, and per-kernel event profiling. Every entry point validates all arguments
+// before the first launch and reports failures through h3k_last_error().
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/h3k.h"
+#include "h3k_internal.h"
+
+using namespace h3k;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define H3K_CHECK_PTR(p)                                                  \
+  do {                                                                    \
+    if (!(p)) return fail(H3K_EINVAL, "%s: %s is NULL", fn, #p);          \
+    if (!aligned16(p)) return fail(H3K_EINVAL, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+// ------------------------------------------------------------------ profiling
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;     // records of the current profiling window
+std::vector<hipEvent_t> g_pool;  // spare events
+
+hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct Launch {
+  // brackets one kernel launch with profiling events and optional sync
+  int kind;
+  hipStream_t s;
+  uint32_t flags;
+  hipEvent_t a = nullptr, b = nullptr;
+  Launch(int k, hipStream_t st, uint32_t f) : kind(k), s(st), flags(f) {
+    if (g_prof_on) {
+      a = pool_event();
+      b = pool_event();
+      if (a && b) hipEventRecord(a, s);
+    }
+  }
+  int done(hipError_t e, const char *fn, const char *what) {
+    if (e != hipSuccess) return fail(H3K_EHIP, "%s: %s launch failed: %s", fn, what, hipGetErrorString(e));
+    if (a && b) {
+      hipEventRecord(b, s);
+      g_prof.push_back({kind, a, b});
+    }
+    if (flags & H3K_F_SYNC) {
+      hipError_t e2 = hipStreamSynchronize(s);
+      if (e2 == hipSuccess) e2 = hipGetLastError();
+      if (e2 != hipSuccess) return fail(H3K_EHIP, "%s: %s failed: %s", fn, what, hipGetErrorString(e2));
+    }
+    return H3K_OK;
+  }
+};
+
+// ------------------------------------------------------------------ dims / workspace
+int check_dims(const char *fn, const h3k_dims *dm, int64_t L) {
+  if (!dm) return fail(H3K_EINVAL, "%s: dims is NULL", fn);
+  if (dm->d <= 0 || dm->n_heads <= 0 || dm->head_dim <= 0 || dm->d_ff <= 0 || dm->d_cond <= 0)
+    return fail(H3K_EINVAL, "%s: dims must be positive", fn);
+  if (dm->d != dm->n_heads * dm->head_dim)
+    return fail(H3K_EINVAL, "%s: d (%d) != n_heads (%d) * head_dim (%d)", fn, dm->d, dm->n_heads, dm->head_dim);
+  if (dm->grid_t <= 0 || dm->grid_h <= 0 || dm->grid_w <= 0)
+    return fail(H3K_EINVAL, "%s: grid sizes must be positive", fn);
+  if (L <= 0) return fail(H3K_EINVAL, "%s: L must be positive", fn);
+  if ((int64_t)dm->grid_t * dm->grid_h * dm->grid_w != L)
+    return fail(H3K_EINVAL, "%s: L (%lld) != grid_t*grid_h*grid_w", fn, (long long)L);
+  if (!(dm->ln_eps > 0.f) || !(dm->rope_theta > 0.f))
+    return fail(H3K_EINVAL, "%s: ln_eps and rope_theta must be positive", fn);
+  if (dm->head_dim != 64 && dm->head_dim != 128)
+    return fail(H3K_EUNSUPPORTED, "%s: head_dim %d unsupported (64 or 128)", fn, dm->head_dim);
+  if (dm->d % 256 || dm->d_ff % 256)
+    return fail(H3K_EUNSUPPORTED, "%s: d and d_ff must be multiples of 256", fn);
+  if (dm->d > 8192) return fail(H3K_EUNSUPPORTED, "%s: d > 8192 unsupported", fn);
+  if (dm->d_ff > 32768) return fail(H3K_EUNSUPPORTED, "%s: d_ff > 32768 unsupported", fn);
+  if (dm->d_cond % 8 || dm->d_cond > 8192)
+    return fail(H3K_EUNSUPPORTED, "%s: d_cond must be a multiple of 8 and <= 8192", fn);
+  if (L % 8) return fail(H3K_EUNSUPPORTED, "%s: L must be a multiple of 8", fn);
+  if (L > (int64_t)1 << 24) return fail(H3K_EUNSUPPORTED, "%s: L > 2^24 unsupported", fn);
+  return H3K_OK;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
+  const size_t d = dm->d, F = dm->d_ff, H = dm->n_heads, Dh = dm->head_dim;
+  const size_t T = (flags & H3K_F_FP32_DEBUG) ? 4 : 2;
+  const bool bf = (flags & H3K_F_BF16_GEMM) != 0;
+  const size_t Lz = (size_t)L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += up256(bytes);
+    return o;
+  };
+  w->m = take(6 * d * 4);
+  w->rope = take((size_t)(dm->grid_t + dm->grid_h + dm->grid_w) * (Dh / 2) * 8);
+  w->s_a = take(Lz * 4);
+  w->s_o = take(Lz * 4);
+  w->s_a2 = take(Lz * 4);
+  w->s_g = take(Lz * 4);
+  w->qa = bf ? 0 : take(Lz * d);
+  w->qo = bf ? 0 : take(Lz * d);
+  w->qa2 = bf ? 0 : take(Lz * d);
+  w->qg = bf ? 0 : take(Lz * F);
+  w->q = take(H * Lz * Dh * T);
+  w->k = take(H * Lz * Dh * T);
+  w->vt = take(H * Lz * Dh * T);
+  w->o = take(Lz * d * T);
+  w->g = take(Lz * F * T);
+  w->h = bf ? take(Lz * d * 2) : 0;
+  w->h2 = bf ? take(Lz * d * 2) : 0;
+  w->total = off;
+}
+
+template <typename P>
+P *at(void *ws, size_t off) {
+  return (P *)((uint8_t *)ws + off);
+}
+
+int check_weights(const char *fn, const h3k_block_weights *w, uint32_t flags) {
+  if (!w) return fail(H3K_EINVAL, "%s: weights is NULL", fn);
+  H3K_CHECK_PTR(w->w_ada);
+  if (flags & H3K_F_BF16_GEMM) {
+    H3K_CHECK_PTR(w->wb_qkv);
+    H3K_CHECK_PTR(w->wb_o);
+    H3K_CHECK_PTR(w->wb_up);
+    H3K_CHECK_PTR(w->wb_down);
+  } else {
+    H3K_CHECK_PTR(w->w_qkv);
+    H3K_CHECK_PTR(w->s_qkv);
+    H3K_CHECK_PTR(w->w_o);
+    H3K_CHECK_PTR(w->s_o);
+    H3K_CHECK_PTR(w->w_up);
+    H3K_CHECK_PTR(w->s_up);
+    H3K_CHECK_PTR(w->w_down);
+    H3K_CHECK_PTR(w->s_down);
+  }
+  return H3K_OK;
+}
+
+int check_flags(const char *fn, uint32_t flags) {
+  if (flags & ~(uint32_t)(H3K_F_BF16_GEMM | H3K_F_FP32_DEBUG | H3K_F_SYNC))
+    return fail(H3K_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
+  if ((flags & H3K_F_BF16_GEMM) && (flags & H3K_F_FP32_DEBUG))
+    return fail(H3K_EUNSUPPORTED, "%s: H3K_F_BF16_GEMM with H3K_F_FP32_DEBUG is unsupported", fn);
+  return H3K_OK;
+}
+
+// One block on grid (T, Hg, Wg) with w positions w * w_scale + w_offset. Arguments are
+// already validated.
+int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
+               const h3k_block_weights *w, const h3k_dims *dm, int T, int Hg, int Wg,
+               float w_scale, float w_offset, uint32_t flags, void *ws, hipStream_t s) {
+  const int64_t L = (int64_t)T * Hg * Wg;
+  const int d = dm->d, F = dm->d_ff, H = dm->n_heads, Dh = dm->head_dim;
+  const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
+  const bool bf = (flags & H3K_F_BF16_GEMM) != 0;
+  h3k_ws_layout lay;
+  plan(dm, L, flags, &lay);
+  float *m = at<float>(ws, lay.m);
+  float2 *rope = at<float2>(ws, lay.rope);
+  int rc;
+
+  {
+    Launch l(H3K_K_ADALN, s, flags);
+    if ((rc = l.done(launch_adaln(w->w_ada, cond, m, 6 * (int64_t)d, dm->d_cond, s), fn, "adaln"))) return rc;
+  }
+  RopeGeom rg = rope_geom(Dh, T, Hg, Wg, w_scale, w_offset);
+  {
+    Launch l(H3K_K_ROPE_TABLE, s, flags);
+    if ((rc = l.done(launch_rope_table(rope, rg, dm->rope_theta, s), fn, "rope_table"))) return rc;
+  }
+  const float *shift1 = m, *scale1 = m + d, *gate1 = m + 2 * d;
+  const float *shift2 = m + 3 * d, *scale2 = m + 4 * d, *gate2 = m + 5 * d;
+
+  // S2: LN + modulate (+ quant)
+  {
+    Launch l(H3K_K_LN_QUANT, s, flags);
+    hipError_t e = bf ? launch_rows(1, x_in, false, shift1, scale1, L, d, dm->ln_eps, nullptr, nullptr,
+                                    at<uint16_t>(ws, lay.h), s)
+                      : launch_rows(0, x_in, f32, shift1, scale1, L, d, dm->ln_eps,
+                                    at<int8_t>(ws, lay.qa), at<float>(ws, lay.s_a), nullptr, s);
+    if ((rc = l.done(e, fn, "ln_modulate_quant"))) return rc;
+  }
+  // S3: QKV + RoPE + head-major scatter
+  GemmArgs ga{};
+  ga.M = L;
+  ga.bf16_ops = bf;
+  ga.out_f32 = f32;
+  {
+    GemmArgs a = ga;
+    a.A = bf ? (const void *)at<uint16_t>(ws, lay.h) : (const void *)at<int8_t>(ws, lay.qa);
+    a.B = bf ? (const void *)w->wb_qkv : (const void *)w->w_qkv;
+    a.N = 3 * d;
+    a.K = d;
+    a.sa = at<float>(ws, lay.s_a);
+    a.sw = w->s_qkv;
+    a.q = at<void>(ws, lay.q);
+    a.k = at<void>(ws, lay.k);
+    a.vt = at<void>(ws, lay.vt);
+    a.d = d;
+    a.H = H;
+    a.Dh = Dh;
+    a.rope = rope;
+    a.rg = rg;
+    Launch l(H3K_K_GEMM_QKV, s, flags);
+    if ((rc = l.done(launch_gemm(EPI_QKV, a, s), fn, "gemm_qkv"))) return rc;
+  }
+  // S4: attention
+  {
+    Launch l(H3K_K_ATTENTION, s, flags);
+    hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, s);
+    if ((rc = l.done(e, fn, "attention"))) return rc;
+  }
+  // S5: quantise O
+  if (!bf) {
+    Launch l(H3K_K_ROWQUANT_O, s, flags);
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), f32, nullptr, nullptr, L, d, 0.f,
+                                 at<int8_t>(ws, lay.qo), at<float>(ws, lay.s_o), nullptr, s),
+                     fn, "rowquant_o")))
+      return rc;
+  }
+  // S6: out-proj + gated residual -> x_out holds x1
+  {
+    GemmArgs a = ga;
+    a.A = bf ? (const void *)at<uint16_t>(ws, lay.o) : (const void *)at<int8_t>(ws, lay.qo);
+    a.B = bf ? (const void *)w->wb_o : (const void *)w->w_o;
+    a.N = d;
+    a.K = d;
+    a.sa = at<float>(ws, lay.s_o);
+    a.sw = w->s_o;
+    a.out = x_out;
+    a.res = x_in;
+    a.gate = gate1;
+    Launch l(H3K_K_GEMM_O, s, flags);
+    if ((rc = l.done(launch_gemm(EPI_RESID, a, s), fn, "gemm_o"))) return rc;
+  }
+  // S7: LN + modulate (+ quant) of x1
+  {
+    Launch l(H3K_K_LN_QUANT, s, flags);
+    hipError_t e = bf ? launch_rows(1, x_out, false, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
+                                    at<uint16_t>(ws, lay.h2), s)
+                      : launch_rows(0, x_out, f32, shift2, scale2, L, d, dm->ln_eps,
+                                    at<int8_t>(ws, lay.qa2), at<float>(ws, lay.s_a2), nullptr, s);
+    if ((rc = l.done(e, fn, "ln_modulate_quant_2"))) return rc;
+  }
+  // S8: MLP up + GELU
+  {
+    GemmArgs a = ga;
+    a.A = bf ? (const void *)at<uint16_t>(ws, lay.h2) : (const void *)at<int8_t>(ws, lay.qa2);
+    a.B = bf ? (const void *)w->wb_up : (const void *)w->w_up;
+    a.N = F;
+    a.K = d;
+    a.sa = at<float>(ws, lay.s_a2);
+    a.sw = w->s_up;
+    a.out = at<void>(ws, lay.g);
+    Launch l(H3K_K_GEMM_UP, s, flags);
+    if ((rc = l.done(launch_gemm(EPI_GELU, a, s), fn, "gemm_up"))) return rc;
+  }
+  // S9: quantise g
+  if (!bf) {
+    Launch l(H3K_K_ROWQUANT_G, s, flags);
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), f32, nullptr, nullptr, L, F, 0.f,
+                                 at<int8_t>(ws, lay.qg), at<float>(ws, lay.s_g), nullptr, s),
+                     fn, "rowquant_g")))
+      return rc;
+  }
+  // S10: MLP down + gated residual, in place on x_out
+  {
+    GemmArgs a = ga;
+    a.A = bf ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
+    a.B = bf ? (const void *)w->wb_down : (const void *)w->w_down;
+    a.N = d;
+    a.K = F;
+    a.sa = at<float>(ws, lay.s_g);
+    a.sw = w->s_down;
+    a.out = x_out;
+    a.res = x_out;
+    a.gate = gate2;
+    Launch l(H3K_K_GEMM_DOWN, s, flags);
+    if ((rc = l.done(launch_gemm(EPI_RESID, a, s), fn, "gemm_down"))) return rc;
+  }
+  return H3K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *h3k_last_error(void) { return g_err.c_str(); }
+
+int h3k_quantize_weights(const void *w, int w_dtype, int64_t n_out, int64_t k_in,
+                         int8_t *q_out, float *scale_out, void *stream) {
+  const char *fn = "h3k_quantize_weights";
+  H3K_CHECK_PTR(w);
+  H3K_CHECK_PTR(q_out);
+  H3K_CHECK_PTR(scale_out);
+  if (w_dtype != H3K_DT_F32 && w_dtype != H3K_DT_BF16) return fail(H3K_EINVAL, "%s: bad w_dtype %d", fn, w_dtype);
+  if (n_out <= 0 || k_in <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (k_in % 8) return fail(H3K_EUNSUPPORTED, "%s: k_in must be a multiple of 8", fn);
+  if (k_in > 32768) return fail(H3K_EUNSUPPORTED, "%s: k_in > 32768 unsupported", fn);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_rows(2, w, w_dtype == H3K_DT_F32, nullptr, nullptr, n_out, (int)k_in, 0.f,
+                             q_out, scale_out, nullptr, s);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+size_t h3k_workspace_bytes(const h3k_dims *dm, int64_t L, uint32_t flags) {
+  std::string keep = g_err;
+  if (check_dims("h3k_workspace_bytes", dm, L) != H3K_OK) return 0;
+  h3k_ws_layout w;
+  plan(dm, L, flags, &w);
+  g_err = keep;
+  return w.total;
+}
+
+int h3k_workspace_layout(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *out) {
+  const char *fn = "h3k_workspace_layout";
+  if (!out) return fail(H3K_EINVAL, "%s: out is NULL", fn);
+  int rc = check_dims(fn, dm, L);
+  if (rc) return rc;
+  if ((rc = check_flags(fn, flags))) return rc;
+  plan(dm, L, flags, out);
+  return H3K_OK;
+}
+
+int h3k_block_forward(const void *x_in, void *x_out, const float *cond,
+                      const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
+                      uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "h3k_block_forward";
+  int rc;
+  if ((rc = check_flags(fn, flags))) return rc;
+  if ((rc = check_dims(fn, dm, L))) return rc;
+  H3K_CHECK_PTR(x_in);
+  H3K_CHECK_PTR(x_out);
+  H3K_CHECK_PTR(cond);
+  H3K_CHECK_PTR(ws);
+  if ((rc = check_weights(fn, w, flags))) return rc;
+  h3k_ws_layout lay;
+  plan(dm, L, flags, &lay);
+  if (ws_bytes < lay.total)
+    return fail(H3K_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, lay.total);
+  return block_impl(fn, x_in, x_out, cond, w, dm, dm->grid_t, dm->grid_h, dm->grid_w, 1.f, 0.f,
+                    flags, ws, (hipStream_t)stream);
+}
+
+int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
+                  int64_t L, int32_t head_dim, float softmax_scale, uint32_t flags,
+                  void *stream) {
+  const char *fn = "h3k_attention";
+  H3K_CHECK_PTR(q);
+  H3K_CHECK_PTR(k);
+  H3K_CHECK_PTR(v);
+  H3K_CHECK_PTR(o);
+  if (flags & ~(uint32_t)(H3K_F_FP32_DEBUG | H3K_F_SYNC)) return fail(H3K_EINVAL, "%s: bad flags", fn);
+  if (n_heads <= 0 || L <= 0) return fail(H3K_EINVAL, "%s: n_heads and L must be positive", fn);
+  if (head_dim != 64 && head_dim != 128) return fail(H3K_EUNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
+  if (L % 8) return fail(H3K_EUNSUPPORTED, "%s: L must be a multiple of 8", fn);
+  if (L > (int64_t)1 << 24 || n_heads > 65535) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
+  if (!(softmax_scale > 0.f)) return fail(H3K_EINVAL, "%s: softmax_scale must be positive", fn);
+  hipStream_t s = (hipStream_t)stream;
+  Launch l(H3K_K_ATTENTION, s, flags);
+  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale,
+                                 (flags & H3K_F_FP32_DEBUG) != 0, s),
+                fn, "attention");
+}
+
+size_t h3k_stack_workspace_bytes(const h3k_dims *dm, int64_t L, int32_t tr_begin,
+                                 int32_t tr_end, uint32_t flags) {
+  size_t b = h3k_workspace_bytes(dm, L, flags);
+  if (!b) return 0;
+  if (tr_end > tr_begin) {
+    const size_t T = (flags & H3K_F_FP32_DEBUG) ? 4 : 2;
+    b += 2 * up256((size_t)(L / 2) * dm->d * T);
+  }
+  return b;
+}
+
+int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
+                      const h3k_block_weights *blocks, int32_t n_blocks,
+                      const h3k_dims *dm, int64_t L, int32_t tr_begin, int32_t tr_end,
+                      uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "h3k_stack_forward";
+  int rc;
+  if ((rc = check_flags(fn, flags))) return rc;
+  if ((rc = check_dims(fn, dm, L))) return rc;
+  H3K_CHECK_PTR(x_in);
+  H3K_CHECK_PTR(x_out);
+  H3K_CHECK_PTR(cond);
+  H3K_CHECK_PTR(ws);
+  if (!blocks) return fail(H3K_EINVAL, "%s: blocks is NULL", fn);
+  if (n_blocks <= 0) return fail(H3K_EINVAL, "%s: n_blocks must be positive", fn);
+  if (tr_begin < 0 || tr_end < tr_begin || tr_end > n_blocks)
+    return fail(H3K_EINVAL, "%s: need 0 <= tr_begin <= tr_end <= n_blocks", fn);
+  const bool tr = tr_end > tr_begin;
+  if (tr && (dm->grid_w % 2))
+    return fail(H3K_EINVAL, "%s: token pairing needs an even grid_w", fn);
+  if (tr && ((L / 2) % 8))
+    return fail(H3K_EUNSUPPORTED, "%s: paired token count L/2 must be a multiple of 8", fn);
+  for (int b = 0; b < n_blocks; ++b)
+    if ((rc = check_weights(fn, &blocks[b], flags))) return rc;
+  const size_t need = h3k_stack_workspace_bytes(dm, L, tr_begin, tr_end, flags);
+  if (ws_bytes < need) return fail(H3K_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
+  const size_t esz = f32 ? 4 : 2;
+  h3k_ws_layout lay;
+  plan(dm, L, flags, &lay);
+  uint8_t *xr = (uint8_t *)ws + lay.total;
+  uint8_t *xr_in = xr + up256((size_t)(L / 2) * dm->d * esz);
+  const int T = dm->grid_t, Hg = dm->grid_h, Wg = dm->grid_w;
+
+  const void *src = x_in;
+  for (int b = 0; b < n_blocks; ++b) {
+    if (tr && b == tr_begin) {
+      // x_out holds the full-resolution state x_pre until the unpair
+      if (src != x_out) {
+        hipError_t e = hipMemcpyAsync(x_out, src, (size_t)L * dm->d * esz, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(H3K_EHIP, "%s: copy failed: %s", fn, hipGetErrorString(e));
+        src = x_out;
+      }
+      Launch l(H3K_K_TOKEN_PAIR, s, flags);
+      if ((rc = l.done(launch_token_pair(x_out, xr, xr_in, f32, T, Hg, Wg, dm->d, s), fn, "token_pair")))
+        return rc;
+    }
+    if (tr && b >= tr_begin && b < tr_end) {
+      rc = block_impl(fn, xr, xr, cond, &blocks[b], dm, T, Hg, Wg / 2, 2.f, 0.5f, flags, ws, s);
+    } else {
+      rc = block_impl(fn, src, x_out, cond, &blocks[b], dm, T, Hg, Wg, 1.f, 0.f, flags, ws, s);
+      src = x_out;
+    }
+    if (rc) return rc;
+    if (tr && b == tr_end - 1) {
+      Launch l(H3K_K_TOKEN_UNPAIR, s, flags);
+      if ((rc = l.done(launch_token_unpair(x_out, xr, xr_in, f32, T, Hg, Wg, dm->d, s), fn, "token_unpair")))
+        return rc;
+    }
+  }
+  return H3K_OK;
+}
+
+int h3k_adaln_modulation(const uint16_t *w_ada, const float *cond, float *m, int64_t n_out,
+                         int32_t d_cond, void *stream) {
+  const char *fn = "h3k_adaln_modulation";
+  H3K_CHECK_PTR(w_ada);
+  H3K_CHECK_PTR(cond);
+  H3K_CHECK_PTR(m);
+  if (n_out <= 0 || d_cond <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (d_cond % 8 || d_cond > 8192) return fail(H3K_EUNSUPPORTED, "%s: d_cond must be a multiple of 8, <= 8192", fn);
+  hipError_t e = launch_adaln(w_ada, cond, m, n_out, d_cond, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift, const float *scale,
+                          int64_t rows, int32_t cols, float eps, int8_t *q_out, float *s_out,
+                          void *stream) {
+  const char *fn = "h3k_ln_modulate_quant";
+  H3K_CHECK_PTR(x);
+  H3K_CHECK_PTR(shift);
+  H3K_CHECK_PTR(scale);
+  H3K_CHECK_PTR(q_out);
+  H3K_CHECK_PTR(s_out);
+  if (x_dtype != H3K_DT_F32 && x_dtype != H3K_DT_BF16) return fail(H3K_EINVAL, "%s: bad x_dtype", fn);
+  if (rows <= 0 || cols <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (cols % 256 || cols > 8192) return fail(H3K_EUNSUPPORTED, "%s: cols must be a multiple of 256, <= 8192", fn);
+  if (!(eps > 0.f)) return fail(H3K_EINVAL, "%s: eps must be positive", fn);
+  hipError_t e = launch_rows(0, x, x_dtype == H3K_DT_F32, shift, scale, rows, cols, eps, q_out, s_out,
+                             nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols, int8_t *q_out,
+                     float *s_out, void *stream) {
+  const char *fn = "h3k_row_quantize";
+  H3K_CHECK_PTR(x);
+  H3K_CHECK_PTR(q_out);
+  H3K_CHECK_PTR(s_out);
+  if (x_dtype != H3K_DT_F32 && x_dtype != H3K_DT_BF16) return fail(H3K_EINVAL, "%s: bad x_dtype", fn);
+  if (rows <= 0 || cols <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (cols % 8 || cols > 32768) return fail(H3K_EUNSUPPORTED, "%s: cols must be a multiple of 8, <= 32768", fn);
+  hipError_t e = launch_rows(2, x, x_dtype == H3K_DT_F32, nullptr, nullptr, rows, cols, 0.f, q_out, s_out,
+                             nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
+                    int64_t K, void *stream) {
+  const char *fn = "h3k_gemm_i8_i32";
+  H3K_CHECK_PTR(a);
+  H3K_CHECK_PTR(b);
+  H3K_CHECK_PTR(c);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (N % 256 || K % 128) return fail(H3K_EUNSUPPORTED, "%s: need N %% 256 == 0 and K %% 128 == 0", fn);
+  if (N > (1 << 20) || K > (1 << 20) || M > ((int64_t)1 << 26)) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
+  GemmArgs g{};
+  g.A = a;
+  g.B = b;
+  g.M = M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.c32 = c;
+  hipError_t e = launch_gemm(EPI_RAW_I32, g, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_token_pair(const void *x, void *xr, void *xr_copy, int x_dtype, int32_t T, int32_t Hg,
+                   int32_t Wg, int32_t d, void *stream) {
+  const char *fn = "h3k_token_pair";
+  H3K_CHECK_PTR(x);
+  H3K_CHECK_PTR(xr);
+  H3K_CHECK_PTR(xr_copy);
+  if (x_dtype != H3K_DT_F32 && x_dtype != H3K_DT_BF16) return fail(H3K_EINVAL, "%s: bad x_dtype", fn);
+  if (T <= 0 || Hg <= 0 || Wg <= 0 || d <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (Wg % 2) return fail(H3K_EINVAL, "%s: Wg must be even", fn);
+  if (d % 8) return fail(H3K_EUNSUPPORTED, "%s: d must be a multiple of 8", fn);
+  hipError_t e = launch_token_pair(x, xr, xr_copy, x_dtype == H3K_DT_F32, T, Hg, Wg, d, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_token_unpair(void *x_pre, const void *xr_out, const void *xr_in, int x_dtype, int32_t T,
+                     int32_t Hg, int32_t Wg, int32_t d, void *stream) {
+  const char *fn = "h3k_token_unpair";
+  H3K_CHECK_PTR(x_pre);
+  H3K_CHECK_PTR(xr_out);
+  H3K_CHECK_PTR(xr_in);
+  if (x_dtype != H3K_DT_F32 && x_dtype != H3K_DT_BF16) return fail(H3K_EINVAL, "%s: bad x_dtype", fn);
+  if (T <= 0 || Hg <= 0 || Wg <= 0 || d <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (Wg % 2) return fail(H3K_EINVAL, "%s: Wg must be even", fn);
+  if (d % 8) return fail(H3K_EUNSUPPORTED, "%s: d must be a multiple of 8", fn);
+  hipError_t e = launch_token_unpair(x_pre, xr_out, xr_in, x_dtype == H3K_DT_F32, T, Hg, Wg, d,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_profile_enable(int on) {
+  for (auto &r : g_prof) {
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  g_prof_on = on != 0;
+  return H3K_OK;
+}
+
+int h3k_profile_read(int kind, int64_t *count, double *total_ms) {
+  const char *fn = "h3k_profile_read";
+  if (kind < 0 || kind >= H3K_K_COUNT) return fail(H3K_EINVAL, "%s: bad kind %d", fn, kind);
+  if (!count || !total_ms) return fail(H3K_EINVAL, "%s: NULL output", fn);
+  int64_t n = 0;
+  double t = 0.0;
+  for (auto &r : g_prof) {
+    if (r.kind != kind) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return fail(H3K_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(H3K_EHIP, "%s: %s", fn, hipGetErrorString(e));
+    ++n;
+    t += ms;
+  }
+  *count = n;
+  *total_ms = t;
+  return H3K_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal declarations shared by the HIP translation units of libh3k.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3k {
+
+// ---------------------------------------------------------------- device helpers
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// symmetric int8 code of v given the fp32 reciprocal inv = 127 / absmax
+__device__ __forceinline__ int quant_code(float v, float inv) {
+  float r = __builtin_rintf(v * inv);
+  r = fminf(fmaxf(r, -127.f), 127.f);
+  return (int)r;
+}
+
+// ---------------------------------------------------------------- rope table
+struct RopeGeom {
+  int Pt, Ph, Pw;          // pairs per axis
+  int T, Hg, Wg;           // grid
+  int base_h, base_w;      // table offsets (entries) of the h and w axes; t starts at 0
+  float w_scale, w_offset; // w position = w * w_scale + w_offset
+};
+RopeGeom rope_geom(int head_dim, int T, int Hg, int Wg, float w_scale, float w_offset);
+size_t rope_table_entries(const RopeGeom &g);
+
+// ---------------------------------------------------------------- launchers
+// all return hipError_t of the launch (hipGetLastError)
+hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStream_t s);
+hipError_t launch_adaln(const uint16_t *w, const float *c, float *m, int64_t n_out, int dc,
+                        hipStream_t s);
+// mode: 0 = LN + modulate + int8 quant, 1 = LN + modulate -> bf16, 2 = int8 quant only
+hipError_t launch_rows(int mode, const void *x, bool x_f32, const float *shift,
+                       const float *scale, int64_t rows, int cols, float eps, int8_t *q,
+                       float *sc, uint16_t *hout, hipStream_t s);
+hipError_t launch_token_pair(const void *x, void *xr, void *xr2, bool f32, int T, int Hg,
+                             int Wg, int d, hipStream_t s);
+hipError_t launch_token_unpair(void *x, const void *xo, const void *xi, bool f32, int T,
+                               int Hg, int Wg, int d, hipStream_t s);
+
+// GEMM: out = epilogue(A[M,K] . B[N,K]^T). A = activations (tokens), B = weights.
+enum EpiKind { EPI_RAW_I32 = 0, EPI_QKV = 1, EPI_GELU = 2, EPI_RESID = 3 };
+struct GemmArgs {
+  const void *A;       // int8 or bf16 [M, K]
+  const void *B;       // int8 or bf16 [N, K]
+  int64_t M;
+  int N, K;            // K in elements
+  bool bf16_ops;       // bf16 operands (fp32 accumulation, no dequant scales)
+  bool out_f32;        // fp32 outputs (debug path) instead of bf16
+  const float *sa;     // per-row (token) scales [M]     (int8 only)
+  const float *sw;     // per-column (channel) scales [N] (int8 only)
+  // EPI_RAW_I32
+  int32_t *c32;
+  // EPI_QKV: q, k [H, M, Dh], vt [H, Dh, M]
+  void *q, *k, *vt;
+  int d, H, Dh;
+  const float2 *rope;
+  RopeGeom rg;
+  // EPI_GELU: out [M, N]; EPI_RESID: out[m,n] = res[m,n] + gate[n] * y
+  void *out;
+  const void *res;
+  const float *gate;
+};
+hipError_t launch_gemm(EpiKind kind, const GemmArgs &a, hipStream_t s);
+
+// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]
+hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
+                            int64_t L, int Dh, float scale, bool f32, hipStream_t s);
+
+}  // namespace h3k

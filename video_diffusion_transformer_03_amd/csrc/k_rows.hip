@@ -1,0 +1,407 @@
+// Bandwidth-bound kernels of the block: AdaLN modulation GEMV, the fused
+// LayerNorm + modulate + per-token int8 quantiser, the plain per-row quantiser, the RoPE
+// rotation table, and horizontal token pairing / unpairing.
+//
+// Pages: "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "Int8 양자화"
+// (the QKV and MLP activation quantisers folded into the gated AdaLN kernel, dynamic
+// per-row activation scales) and the "속도 및 품질 트레이드오프" table (token reduction
+// pairs horizontal video tokens in the middle blocks).
+#include "h3k_internal.h"
+
+#include <math.h>
+
+namespace h3k {
+
+// ============================================================== RoPE table
+RopeGeom rope_geom(int head_dim, int T, int Hg, int Wg, float w_scale, float w_offset) {
+  RopeGeom g;
+  int P = head_dim / 2, p3 = P / 3;
+  g.Pt = P - 2 * p3;
+  g.Ph = p3;
+  g.Pw = p3;
+  g.T = T;
+  g.Hg = Hg;
+  g.Wg = Wg;
+  g.base_h = T * g.Pt;
+  g.base_w = g.base_h + Hg * g.Ph;
+  g.w_scale = w_scale;
+  g.w_offset = w_offset;
+  return g;
+}
+size_t rope_table_entries(const RopeGeom &g) {
+  return (size_t)g.T * g.Pt + (size_t)g.Hg * g.Ph + (size_t)g.Wg * g.Pw;
+}
+
+// entry (axis a, position p, pair j) -> (cos, sin) of p * theta^(-j / P_a), in fp64
+__global__ void rope_table_kernel(float2 *tbl, RopeGeom g, double theta) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  int n = g.T * g.Pt + g.Hg * g.Ph + g.Wg * g.Pw;
+  if (e >= n) return;
+  double pos;
+  int j, P;
+  if (e < g.base_h) {
+    P = g.Pt; pos = e / P; j = e % P;
+  } else if (e < g.base_w) {
+    int r = e - g.base_h;
+    P = g.Ph; pos = r / P; j = r % P;
+  } else {
+    int r = e - g.base_w;
+    P = g.Pw; j = r % P;
+    pos = (double)(r / P) * (double)g.w_scale + (double)g.w_offset;
+  }
+  double ang = pos * pow(theta, -(double)j / (double)P);
+  tbl[e] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStream_t s) {
+  int n = (int)rope_table_entries(g);
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(tbl, g, (double)theta);
+  return hipGetLastError();
+}
+
+// ============================================================== AdaLN GEMV
+// m[i] = sum_j W[i, j] c[j]. One wave per output row; each lane keeps the slice of c
+// it multiplies in registers (MAXC 16-byte chunks of W per lane).
+template <int MAXC>
+__global__ __launch_bounds__(256) void adaln_kernel(const uint16_t *__restrict__ W,
+                                                    const float *__restrict__ c,
+                                                    float *__restrict__ m, int64_t n_out,
+                                                    int dc, int rows_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nch = dc / 8;
+  float cv[MAXC][8];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    int ch = lane + 64 * i;
+    if (ch < nch) {
+      float4 a = *(const float4 *)(c + ch * 8);
+      float4 b = *(const float4 *)(c + ch * 8 + 4);
+      cv[i][0] = a.x; cv[i][1] = a.y; cv[i][2] = a.z; cv[i][3] = a.w;
+      cv[i][4] = b.x; cv[i][5] = b.y; cv[i][6] = b.z; cv[i][7] = b.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cv[i][t] = 0.f;
+    }
+  }
+  for (int r = 0; r < rows_per_wave; ++r) {
+    int64_t row = wave * rows_per_wave + r;
+    if (row >= n_out) break;
+    const uint16_t *wr = W + row * dc;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      int ch = lane + 64 * i;
+      if (ch < nch) {
+        uint4 u = *(const uint4 *)(wr + ch * 8);
+        uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc = fmaf(__uint_as_float(w4[t] << 16), cv[i][2 * t], acc);
+          acc = fmaf(__uint_as_float(w4[t] & 0xffff0000u), cv[i][2 * t + 1], acc);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) m[row] = acc;
+  }
+}
+
+hipError_t launch_adaln(const uint16_t *w, const float *c, float *m, int64_t n_out, int dc,
+                        hipStream_t s) {
+  const int rpw = 4;
+  int64_t waves = (n_out + rpw - 1) / rpw;
+  dim3 grid((unsigned)((waves + 3) / 4));
+  int maxc = (dc / 8 + 63) / 64;
+  if (maxc <= 4)
+    adaln_kernel<4><<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
+  else if (maxc <= 10)
+    adaln_kernel<10><<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
+  else
+    adaln_kernel<16><<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
+  return hipGetLastError();
+}
+
+// ============================================================== per-row kernels
+// One row per WPR waves; 256 threads = 4 waves per block, so 4 / WPR rows per block.
+// Each thread holds up to MAXV vectors of 8 elements of its row in registers; the row is
+// read from HBM once and written once.
+__device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
+  uint4 u = *(const uint4 *)p;
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[2 * t] = __uint_as_float(w[t] << 16);
+    v[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float *p, float v[8]) {
+  float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <int WPR>
+__device__ __forceinline__ float group_reduce(float v, bool is_max, float *red) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  if constexpr (WPR == 1) {
+    return v;
+  } else {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();  // earlier readers of red are done
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const int g0 = (wave / WPR) * WPR;
+    float r = red[g0];
+#pragma unroll
+    for (int j = 1; j < WPR; ++j) r = is_max ? fmaxf(r, red[g0 + j]) : r + red[g0 + j];
+    return r;
+  }
+}
+
+enum { RM_LNQ = 0, RM_LN_BF16 = 1, RM_Q = 2 };
+
+template <int MODE, typename Tin, int WPR, int MAXV>
+__global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
+                                                  const float *__restrict__ shift,
+                                                  const float *__restrict__ scale,
+                                                  int64_t rows, int cols, float eps,
+                                                  int8_t *__restrict__ q,
+                                                  float *__restrict__ sc,
+                                                  uint16_t *__restrict__ hout) {
+  __shared__ float red[4];
+  constexpr int NT = WPR * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+  const int tid = (wave % WPR) * 64 + lane;
+  const bool active = row < rows;
+  const int nvec = cols / 8;
+  const Tin *xr = x + (active ? row : 0) * (int64_t)cols;
+
+  float v[MAXV][8];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    int c = tid + i * NT;
+    if (active && c < nvec) {
+      load8(xr + (int64_t)c * 8, v[i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[i][t] = 0.f;
+    }
+  }
+
+  if constexpr (MODE == RM_LNQ || MODE == RM_LN_BF16) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) s += v[i][t];
+    const float mean = group_reduce<WPR>(s, false, red) / (float)cols;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      int c = tid + i * NT;
+      if (c < nvec) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          float dlt = v[i][t] - mean;
+          ss = fmaf(dlt, dlt, ss);
+        }
+      }
+    }
+    const float var = group_reduce<WPR>(ss, false, red) / (float)cols;
+    const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      int c = tid + i * NT;
+      if (c < nvec) {
+        float sh[8], sca[8];
+        load8(shift + c * 8, sh);
+        load8(scale + c * 8, sca);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[i][t] = (v[i][t] - mean) * rstd * (1.0f + sca[t]) + sh[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[i][t] = 0.f;
+      }
+    }
+  }
+
+  if constexpr (MODE == RM_LN_BF16) {
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        int c = tid + i * NT;
+        if (c < nvec) {
+          uint4 o;
+          o.x = pack_bf2(v[i][0], v[i][1]);
+          o.y = pack_bf2(v[i][2], v[i][3]);
+          o.z = pack_bf2(v[i][4], v[i][5]);
+          o.w = pack_bf2(v[i][6], v[i][7]);
+          *(uint4 *)(hout + row * (int64_t)cols + (int64_t)c * 8) = o;
+        }
+      }
+    }
+  } else {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(v[i][t]));
+    a = group_reduce<WPR>(a, true, red);
+    const float inv = a > 0.f ? 127.0f / a : 0.f;
+    if (active) {
+      if (tid == 0) sc[row] = a / 127.0f;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        int c = tid + i * NT;
+        if (c < nvec) {
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            lo |= ((uint32_t)quant_code(v[i][t], inv) & 0xffu) << (8 * t);
+            hi |= ((uint32_t)quant_code(v[i][t + 4], inv) & 0xffu) << (8 * t);
+          }
+          *(uint2 *)(q + row * (int64_t)cols + (int64_t)c * 8) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, typename Tin, int WPR>
+static hipError_t rows_dispatch(const Tin *x, const float *shift, const float *scale,
+                                int64_t rows, int cols, float eps, int8_t *q, float *sc,
+                                uint16_t *hout, hipStream_t s) {
+  const int nvec = cols / 8;
+  const int need = (nvec + WPR * 64 - 1) / (WPR * 64);
+  dim3 grid((unsigned)((rows + (4 / WPR) - 1) / (4 / WPR)));
+#define H3K_ROWS(MV)                                                                    \
+  row_kernel<MODE, Tin, WPR, MV><<<grid, 256, 0, s>>>(x, shift, scale, rows, cols, eps, q, \
+                                                      sc, hout)
+  if (need <= 1) H3K_ROWS(1);
+  else if (need <= 2) H3K_ROWS(2);
+  else if (need <= 4) H3K_ROWS(4);
+  else if (need <= 8) H3K_ROWS(8);
+  else if (need <= 10) H3K_ROWS(10);
+  else H3K_ROWS(16);
+#undef H3K_ROWS
+  return hipGetLastError();
+}
+
+template <int MODE, typename Tin>
+static hipError_t rows_wpr(const Tin *x, const float *shift, const float *scale,
+                           int64_t rows, int cols, float eps, int8_t *q, float *sc,
+                           uint16_t *hout, hipStream_t s) {
+  // one wave per row while a lane needs at most 10 vectors, else four waves per row
+  if (cols / 8 <= 640)
+    return rows_dispatch<MODE, Tin, 1>(x, shift, scale, rows, cols, eps, q, sc, hout, s);
+  return rows_dispatch<MODE, Tin, 4>(x, shift, scale, rows, cols, eps, q, sc, hout, s);
+}
+
+hipError_t launch_rows(int mode, const void *x, bool x_f32, const float *shift,
+                       const float *scale, int64_t rows, int cols, float eps, int8_t *q,
+                       float *sc, uint16_t *hout, hipStream_t s) {
+  if (x_f32) {
+    const float *xf = (const float *)x;
+    if (mode == RM_LNQ) return rows_wpr<RM_LNQ, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);
+    if (mode == RM_Q) return rows_wpr<RM_Q, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);
+    return hipErrorInvalidValue;
+  }
+  const uint16_t *xb = (const uint16_t *)x;
+  if (mode == RM_LNQ) return rows_wpr<RM_LNQ, uint16_t>(xb, shift, scale, rows, cols, eps, q, sc, hout, s);
+  if (mode == RM_LN_BF16) return rows_wpr<RM_LN_BF16, uint16_t>(xb, shift, scale, rows, cols, eps, q, sc, hout, s);
+  return rows_wpr<RM_Q, uint16_t>(xb, shift, scale, rows, cols, eps, q, sc, hout, s);
+}
+
+// ============================================================== token pairing
+// One thread per 8 channels of one output (paired) token.
+template <typename T>
+__global__ __launch_bounds__(256) void token_pair_kernel(const T *__restrict__ x,
+                                                         T *__restrict__ xr,
+                                                         T *__restrict__ xr2, int64_t n_out,
+                                                         int d) {
+  const int nv = d / 8;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_out * nv) return;
+  int64_t tok = i / nv;  // paired token index: ((t*Hg + h) * Wg/2 + j)
+  int c = (int)(i % nv) * 8;
+  // source tokens 2*tok and 2*tok + 1 (same (t, h), w = 2j and 2j + 1)
+  float a[8], b[8], r[8];
+  load8(x + (2 * tok) * (int64_t)d + c, a);
+  load8(x + (2 * tok + 1) * (int64_t)d + c, b);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (a[t] + b[t]) * 0.5f;
+  T *o1 = xr + tok * (int64_t)d + c;
+  T *o2 = xr2 + tok * (int64_t)d + c;
+  if constexpr (sizeof(T) == 2) {
+    uint4 o = make_uint4(pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3]), pack_bf2(r[4], r[5]),
+                         pack_bf2(r[6], r[7]));
+    *(uint4 *)o1 = o;
+    *(uint4 *)o2 = o;
+  } else {
+    float4 p = make_float4(r[0], r[1], r[2], r[3]), q = make_float4(r[4], r[5], r[6], r[7]);
+    ((float4 *)o1)[0] = p; ((float4 *)o1)[1] = q;
+    ((float4 *)o2)[0] = p; ((float4 *)o2)[1] = q;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void token_unpair_kernel(T *__restrict__ x,
+                                                           const T *__restrict__ xo,
+                                                           const T *__restrict__ xi,
+                                                           int64_t n_out, int d) {
+  const int nv = d / 8;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_out * nv) return;
+  int64_t tok = i / nv;
+  int c = (int)(i % nv) * 8;
+  float o[8], in[8], delta[8];
+  load8(xo + tok * (int64_t)d + c, o);
+  load8(xi + tok * (int64_t)d + c, in);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) delta[t] = o[t] - in[t];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    T *p = x + (2 * tok + s2) * (int64_t)d + c;
+    float v[8];
+    load8(p, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] += delta[t];
+    if constexpr (sizeof(T) == 2) {
+      *(uint4 *)p = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                               pack_bf2(v[6], v[7]));
+    } else {
+      ((float4 *)p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      ((float4 *)p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+hipError_t launch_token_pair(const void *x, void *xr, void *xr2, bool f32, int T, int Hg,
+                             int Wg, int d, hipStream_t s) {
+  int64_t n_out = (int64_t)T * Hg * (Wg / 2);
+  int64_t n = n_out * (d / 8);
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (f32)
+    token_pair_kernel<float><<<grid, 256, 0, s>>>((const float *)x, (float *)xr, (float *)xr2, n_out, d);
+  else
+    token_pair_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)x, (uint16_t *)xr,
+                                                     (uint16_t *)xr2, n_out, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_unpair(void *x, const void *xo, const void *xi, bool f32, int T,
+                               int Hg, int Wg, int d, hipStream_t s) {
+  int64_t n_out = (int64_t)T * Hg * (Wg / 2);
+  int64_t n = n_out * (d / 8);
+  dim3 grid((unsigned)((n + 255) / 256));
+  if (f32)
+    token_unpair_kernel<float><<<grid, 256, 0, s>>>((float *)x, (const float *)xo, (const float *)xi, n_out, d);
+  else
+    token_unpair_kernel<uint16_t><<<grid, 256, 0, s>>>((uint16_t *)x, (const uint16_t *)xo,
+                                                       (const uint16_t *)xi, n_out, d);
+  return hipGetLastError();
+}
+
+}  // namespace h3k
