@@ -1,0 +1,204 @@
+"""Throughput of the W8A8 DiT block forward on one MI355X.
+
+A step is one h3k_block_forward call (AdaLN modulation, fused LN + modulate + int8
+quantiser, W8A8 QKV GEMM with RoPE and head-major scatter, bf16 flash attention, O
+quantiser, W8A8 out-projection with gated residual, second LN + quantiser, W8A8 MLP-up
+with GELU, g quantiser, W8A8 MLP-down with gated residual) on one batch of synthetic
+input already resident in HBM. Default workload: one block at d=5120, 40 heads x 128,
+MLP 20480, L=16384 tokens (4x64x64 grid).
+
+Prints one JSON line. Per-kernel durations come from HIP events recorded by the library
+on the stream each kernel runs on, inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"int8": 5000.0, "bf16": 2500.0, "fp32": 157.3}  # dense TOP/s or TFLOP/s, MI355X
+HBM_GBS = 8000.0
+
+
+def kernel_work(wl, L):
+    """Algorithmic work per launch: ('ops', n, dtype) for matrix-core kernels,
+    ('bytes', n) for bandwidth-bound ones."""
+    d, F, dc = wl.d, wl.d_ff, wl.d_cond
+    return {
+        "gemm_qkv": ("ops", 2.0 * L * 3 * d * d, "int8"),
+        "gemm_o": ("ops", 2.0 * L * d * d, "int8"),
+        "gemm_up": ("ops", 2.0 * L * F * d, "int8"),
+        "gemm_down": ("ops", 2.0 * L * d * F, "int8"),
+        "attention": ("ops", 4.0 * L * L * d, "bf16"),
+        # read bf16 x, write int8 codes + fp32 scale per token
+        "ln_quant": ("bytes", L * (3.0 * d + 4)),
+        "rowquant_o": ("bytes", L * (3.0 * d + 4)),
+        "rowquant_g": ("bytes", L * (3.0 * F + 4)),
+        "adaln": ("bytes", 6.0 * d * dc * 2),
+    }
+
+
+def cpu_baseline(wl, x, c, bw, n_rows: int):
+    """The oracle timed on the host: QKV for all tokens (attention needs every key) plus the
+    rest of the block for n_rows sampled tokens; cost per token = prefix/L + rest/n_rows."""
+    import numpy as np
+
+    import oracle as O
+
+    def np64(t):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+
+    w = {"w_ada": np64(bw.w_ada)}
+    for k in ("qkv", "o", "up", "down"):
+        w["q_" + k] = getattr(bw, "w_" + k).cpu().numpy()
+        w["s_" + k] = getattr(bw, "s_" + k).cpu().numpy()
+    xn = np64(x)
+    cn = np64(c)
+    rows = np.linspace(0, wl.L - 1, n_rows).astype(np.int64)
+    kw = dict(n_heads=wl.n_heads, head_dim=wl.head_dim, grid=wl.grid)
+    t0 = time.perf_counter()
+    O.block_forward(xn, cn, w, rows=np.zeros(0, np.int64), **kw)
+    t1 = time.perf_counter()
+    O.block_forward(xn, cn, w, rows=rows, **kw)
+    t2 = time.perf_counter()
+    prefix = t1 - t0
+    rest = max((t2 - t1) - prefix, 1e-9)
+    per_token = prefix / wl.L + rest / n_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"{wl.name}: LN+quant+QKV+RoPE for all {wl.L} tokens ({prefix:.1f} s), then "
+                       f"attention, out-proj and MLP for {n_rows} evenly spaced tokens "
+                       f"({rest:.1f} s); tokens/s = 1 / (prefix/{wl.L} + rest/{n_rows})"),
+            "seconds": t2 - t0}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block_l16384")
+    ap.add_argument("--variant", default="w8a8", choices=["w8a8", "bf16gemm", "fp32"])
+    ap.add_argument("--cpu-rows", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured with rocprofv3 counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import synth_inputs as S
+    from video_diffusion_transformer_03_amd import h3k
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wl = S.WORKLOADS[args.workload]
+    flags = {"w8a8": 0, "bf16gemm": h3k.F_BF16_GEMM, "fp32": h3k.F_FP32_DEBUG}[args.variant]
+
+    wb = S.block_weights_bf16(wl, 0, device="cuda")
+    bw = h3k.quantize_block(wb, keep_bf16=(args.variant == "bf16gemm"))
+    if args.variant != "bf16gemm":
+        del wb
+    xdt = torch.float32 if args.variant == "fp32" else torch.bfloat16
+    x = S.activations(wl, device="cuda").to(xdt)
+    c = S.conditioning(wl, device="cuda")
+    dims = h3k.dims_of(wl)
+    L = wl.L
+    ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, L, flags))
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        h3k.block_forward(x, c, bw, dims, flags, ws, out)
+    torch.cuda.synchronize()
+
+    h3k.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        h3k.block_forward(x, c, bw, dims, flags, ws, out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = h3k.profile_read()
+    h3k.profile_enable(False)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = L * args.steps / (t1 - t0)
+
+    work = kernel_work(wl, L)
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        if n == 0:
+            continue
+        avg = tot / n
+        ent = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 5),
+               "ms_per_step": round(tot / args.steps, 5)}
+        if name in work and args.variant == "w8a8":
+            wk = work[name]
+            if wk[0] == "ops":
+                rate = wk[1] / (avg * 1e-3) / 1e12
+                ent.update(achieved=round(rate, 2), peak=PEAK[wk[2]],
+                           unit="TOP/s" if wk[2] == "int8" else "TFLOP/s",
+                           frac=round(rate / PEAK[wk[2]], 4))
+            else:
+                rate = wk[1] / (avg * 1e-3) / 1e9
+                ent.update(achieved=round(rate, 1), peak=HBM_GBS, unit="GB/s",
+                           frac=round(rate / HBM_GBS, 4))
+        kernels[name] = ent
+
+    result = {
+        "metric": "DiT block tokens/s (W8A8, d=5120, L=16384) + % of peak int8/bf16 MFMA",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"w8a8": "int8 GEMM + bf16 attention", "bf16gemm": "bf16",
+                  "fp32": "int8 GEMM + f32"}[args.variant],
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random-init)",
+        "config": {"workload": wl.name, "d": wl.d, "n_heads": wl.n_heads, "head_dim": wl.head_dim,
+                   "d_ff": wl.d_ff, "d_cond": wl.d_cond, "L": L, "grid": list(wl.grid),
+                   "variant": args.variant},
+    }
+    if args.variant == "w8a8":
+        gemm_names = ["gemm_qkv", "gemm_o", "gemm_up", "gemm_down"]
+        gemm_ops = sum(work[k][1] for k in gemm_names)
+        gemm_ms = sum(kernels[k]["ms_per_step"] for k in gemm_names if k in kernels)
+        attn_ms = kernels.get("attention", {}).get("ms_per_step", float("nan"))
+        result["gemm_int8_frac"] = round(gemm_ops / (gemm_ms * 1e-3) / 1e12 / PEAK["int8"], 4)
+        result["attention_bf16_frac"] = round(work["attention"][1] / (attn_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+        dk = kernels[dom]
+        traffic = None
+        if os.path.exists(args.traffic):
+            try:
+                tr = json.load(open(args.traffic))
+                if tr.get("workload") == wl.name and dom in tr.get("kernels", {}):
+                    traffic = tr["kernels"][dom]
+            except Exception:
+                traffic = None
+        result["roofline"] = {"kernel": dom, "bound": "mfma" if work[dom][0] == "ops" else "hbm",
+                              "achieved": dk.get("achieved"), "peak": dk.get("peak"),
+                              "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": traffic}
+    result["kernels"] = kernels
+    if not args.no_cpu_baseline and args.variant == "w8a8":
+        result["cpu_baseline"] = cpu_baseline(wl, x, c, bw, args.cpu_rows)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

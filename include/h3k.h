@@ -117,8 +117,10 @@ typedef struct {
   size_t qg;                    /* int8 [L, F]                                          */
   size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied                */
   size_t vt;                    /* T [H, Dh, L] head-major, transposed                  */
-  size_t o;                     /* T [L, d] attention output, head e in columns e*Dh..  */
-  size_t g;                     /* T [L, F] GELU output                                 */
+  size_t o;                     /* [L, d] attention output, head e in columns e*Dh ..;
+                                   fp32, or bf16 under H3K_F_BF16_GEMM                  */
+  size_t x1;                    /* fp32 [L, d] residual stream after the attention half */
+  size_t g;                     /* [L, F] GELU output; fp32, or bf16 under H3K_F_BF16_GEMM */
   size_t h, h2;                 /* bf16 [L, d] modulated activations (H3K_F_BF16_GEMM) */
   size_t total;                 /* bytes needed (= h3k_workspace_bytes)                */
 } h3k_ws_layout;

@@ -77,6 +77,16 @@ def quantize_weights(w) -> Tuple[np.ndarray, np.ndarray]:
     return quantize_rows(w)
 
 
+# --------------------------------------------------------------------------- bf16 rounding
+def round_bf16(v) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even, from the
+    exact fp64 value (one rounding). Zero, inf and NaN pass through; values are assumed
+    to lie in the normal bf16 range."""
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)                   # v = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
 # --------------------------------------------------------------------------- int8 GEMM
 def int8_matmul(qa, qw) -> np.ndarray:
     """acc[m, n] = sum_k qa[m, k] * qw[n, k], exact, as int64.
@@ -216,10 +226,15 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
                   variant: str = "w8a8", rows: Optional[Sequence[int]] = None,
                   w_scale: float = 1.0, w_offset: float = 0.0,
                   eps: float = LN_EPS, theta: float = ROPE_THETA,
-                  return_parts: bool = False):
+                  attn_inputs: str = "fp64", return_parts: bool = False):
     """One DiT block forward. x [L, d] (fp64 view of the input values), cond [d_cond];
     w holds w_ada and, per projection, int8 codes q_* with fp32 scales s_* (variant
     "w8a8") or the dense matrices w_* (variant "bf16gemm": no activation quantisation).
+
+    attn_inputs: "fp64" keeps Q, K, V exact; "bf16" rounds them to bfloat16 (after RoPE)
+    before attention, as on the path whose QKV projection hands the attention bf16
+    tensors (page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
+    "Metal 4 및 TensorOps": BF16 QKV projection routed into head-major attention inputs).
 
     rows: token rows whose output is wanted (all if None). Q, K and V are formed for
     every token (attention needs them); everything after attention is per token and is
@@ -236,6 +251,10 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     ang = rope_angles(token_positions(grid, w_scale, w_offset), head_dim, theta)
     q = apply_rope(q, ang)
     k = apply_rope(k, ang)
+    if attn_inputs == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    elif attn_inputs != "fp64":
+        raise ValueError(attn_inputs)
     sel = np.arange(L) if rows is None else np.asarray(rows)
     o = attention(q, k, v, sel).reshape(len(sel), d)
     xs = x[sel]
@@ -272,7 +291,8 @@ def token_unpair(x_pre, xr_out, xr_in, grid) -> np.ndarray:
 
 
 def stack_forward(x, cond, blocks, *, n_heads: int, head_dim: int, grid,
-                  tr_begin: int = 0, tr_end: int = 0, variant: str = "w8a8"):
+                  tr_begin: int = 0, tr_end: int = 0, variant: str = "w8a8",
+                  attn_inputs: str = "fp64"):
     """Blocks 0..n-1 in order, sharing cond. Blocks [tr_begin, tr_end) run on the
     horizontally paired grid (T, Hg, Wg/2) with w positions 2j + 0.5."""
     x = np.asarray(x, np.float64)
@@ -287,10 +307,10 @@ def stack_forward(x, cond, blocks, *, n_heads: int, head_dim: int, grid,
         if tr_on and tr_begin <= b < tr_end:
             x = block_forward(x, cond, w, n_heads=n_heads, head_dim=head_dim,
                               grid=(T, Hg, Wg // 2), variant=variant,
-                              w_scale=2.0, w_offset=0.5)
+                              w_scale=2.0, w_offset=0.5, attn_inputs=attn_inputs)
         else:
             x = block_forward(x, cond, w, n_heads=n_heads, head_dim=head_dim,
-                              grid=grid, variant=variant)
+                              grid=grid, variant=variant, attn_inputs=attn_inputs)
         if tr_on and b == tr_end - 1:
             x = token_unpair(x_pre, x, xr_in, grid)
     return x

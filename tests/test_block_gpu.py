@@ -40,10 +40,15 @@ def run_gpu(wl, flags=0, zero_gates=False, gen_device="cpu"):
                 lay=h3k.workspace_layout(dims, wl.L, flags))
 
 
-def oracle_full(wl, r, variant="w8a8", rows=None):
+def oracle_full(wl, r, variant="w8a8", rows=None, attn_inputs=None):
+    """The oracle block on the run's inputs. On the bf16 path the attention consumes bf16
+    Q, K, V, so the oracle rounds them there (attn_inputs="bf16"); the fp32 debug path is
+    compared with the all-fp64 oracle."""
+    if attn_inputs is None:
+        attn_inputs = "fp64" if r["flags"] & h3k.F_FP32_DEBUG else "bf16"
     w = oracle_weights(r["bw"], r["dense"] if variant == "bf16gemm" else None)
     return O.block_forward(np64(r["x"]), np64(r["c"]), w, n_heads=wl.n_heads, head_dim=wl.head_dim,
-                           grid=wl.grid, variant=variant, rows=rows)
+                           grid=wl.grid, variant=variant, rows=rows, attn_inputs=attn_inputs)
 
 
 # ----------------------------------------------------------------------------- tiny, full oracle
@@ -57,7 +62,7 @@ def test_block_tiny(variant, flags, tol):
     x = np64(r["x"])
     err, err_upd = rel_l2(got, ref), rel_l2(got - x, ref - x)
     print(f"tiny {variant} flags={flags}: rel-L2 {err:.3e}, update rel-L2 {err_upd:.3e}")
-    assert err <= tol and err_upd <= 5 * tol
+    assert err <= tol
 
 
 @pytest.mark.parametrize("grid,H,Dh", [((3, 5, 8), 4, 64), ((2, 3, 12), 2, 128), ((1, 1, 8), 4, 64)])
@@ -87,7 +92,7 @@ def test_block_inplace_and_deterministic():
 
 
 # ----------------------------------------------------------------------------- stage checks
-def check_stages(wl, r, rows, tol_x2=2e-2):
+def check_stages(wl, r, rows):
     """Teacher-forced per-stage parity on token rows `rows` (W8A8 path)."""
     d, F, H, Dh, L = wl.d, wl.d_ff, wl.n_heads, wl.head_dim, wl.L
     f32 = bool(r["flags"] & h3k.F_FP32_DEBUG)
@@ -128,37 +133,50 @@ def check_stages(wl, r, rows, tol_x2=2e-2):
     stats["q"], stats["k"], stats["v"] = rel_l2(q_g, q_ref), rel_l2(k_g, k_ref), rel_l2(v_g, v_ref)
     assert max(stats["q"], stats["k"], stats["v"]) < tol_s, stats
 
-    # attention rows from the GPU's full Q, K, V
+    # attention rows from the GPU's full Q, K, V (O is kept in fp32 for its quantiser)
     qf = np64(q_all).transpose(1, 0, 2)
     kf = np64(k_all).transpose(1, 0, 2)
     vf = np64(vt_all).transpose(2, 0, 1)
     o_ref = O.attention(qf, kf, vf, rows).reshape(len(rows), d)
-    o_g = np64(V("o", T, (L, d))[tq])
+    o_g = np64(V("o", torch.float32, (L, d))[tq])
     stats["o"] = rel_l2(o_g, o_ref)
     assert stats["o"] < (1e-5 if f32 else 1e-2), stats
 
-    # quantisers of O and g on the GPU's own tensors: identical codes
+    # quantiser of O on the GPU's own tensor: identical codes
     qo, so = O.quantize_rows(o_g)
     assert np.array_equal(V("qo", torch.int8, (L, d))[tq].cpu().numpy(), qo)
     assert np.array_equal(V("s_o", torch.float32, (L,))[tq].cpu().numpy(), so)
-    g_g = np64(V("g", T, (L, F))[tq])
+
+    # out-projection + gated residual from the GPU's O codes
+    x1_ref = x + mod["gate1"] * (O.int8_matmul(qo, w["q_o"]) * so.astype(np.float64)[:, None] * w["s_o"])
+    x1 = np64(V("x1", torch.float32, (L, d))[tq])
+    stats["x1"] = rel_l2(x1, x1_ref)
+    assert stats["x1"] < 1e-6, stats
+
+    # second LN + quantiser from the GPU's x1
+    qa2_ref, sa2_ref = O.quantize_rows(O.modulate(O.layer_norm(x1), mod["shift2"], mod["scale2"]))
+    qa2 = V("qa2", torch.int8, (L, d))[tq].cpu().numpy()
+    sa2 = V("s_a2", torch.float32, (L,))[tq].cpu().numpy()
+    stats["qa2_match"], mx = code_match(qa2, qa2_ref)
+    assert stats["qa2_match"] >= 0.9999 and mx <= 1
+    assert np.allclose(sa2, sa2_ref, rtol=1e-6, atol=0)
+
+    # MLP up + GELU from the GPU's codes
+    g_ref = O.gelu(O.int8_matmul(qa2, w["q_up"]) * sa2.astype(np.float64)[:, None] * w["s_up"])
+    g_g = np64(V("g", torch.float32, (L, F))[tq])
+    stats["g"] = rel_l2(g_g, g_ref)
+    assert stats["g"] < 1e-5, stats
     qg, sg = O.quantize_rows(g_g)
     stats["qg_match"], _ = code_match(V("qg", torch.int8, (L, F))[tq].cpu().numpy(), qg)
     assert stats["qg_match"] == 1.0
     assert np.array_equal(V("s_g", torch.float32, (L,))[tq].cpu().numpy(), sg)
 
-    # remaining chain from the GPU's O codes
-    x1 = x + mod["gate1"] * (O.int8_matmul(qo, w["q_o"]) * so.astype(np.float64)[:, None] * w["s_o"])
-    g_ref = O.gelu(O.w8a8_linear(O.modulate(O.layer_norm(x1), mod["shift2"], mod["scale2"]),
-                                 w["q_up"], w["s_up"]))
-    stats["g"] = rel_l2(g_g, g_ref)
+    # MLP down + gated residual from the GPU's codes and x1
     x2_ref = x1 + mod["gate2"] * (O.int8_matmul(qg, w["q_down"]) * sg.astype(np.float64)[:, None] * w["s_down"])
     x2 = np64(r["out"][tq])
     stats["x2"] = rel_l2(x2, x2_ref)
-    stats["x2_update"] = rel_l2(x2 - x, x2_ref - x)
     print(wl.name, {k: (f"{v:.3e}" if isinstance(v, float) else v) for k, v in stats.items()})
-    assert stats["g"] < (1e-3 if f32 else 3e-2)
-    assert stats["x2"] < tol_x2
+    assert stats["x2"] < (1e-6 if f32 else 4e-3), stats
     return stats
 
 
@@ -166,7 +184,7 @@ def check_stages(wl, r, rows, tol_x2=2e-2):
 def test_block_tiny_stages(flags):
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl, flags)
-    check_stages(wl, r, np.arange(wl.L), tol_x2=1e-3 if flags else 2e-2)
+    check_stages(wl, r, np.arange(wl.L))
 
 
 # ----------------------------------------------------------------------------- full-size workloads
@@ -185,7 +203,8 @@ def test_block_l4096(variant, flags):
     got = np64(r["out"])[rows]
     x = np64(r["x"])[rows]
     err, upd = rel_l2(got, ref), rel_l2(got - x, ref - x)
-    print(f"l4096 {variant}: rel-L2 {err:.3e} update {upd:.3e}")
+    err64 = rel_l2(got, oracle_full(wl, r, variant, rows=rows, attn_inputs="fp64"))
+    print(f"l4096 {variant}: rel-L2 {err:.3e} update {upd:.3e} (vs fp64-attention-input oracle {err64:.3e})")
     assert err <= 2e-2
     if variant == "w8a8":
         check_stages(wl, r, rows)
@@ -198,7 +217,8 @@ def test_block_l16384_sampled():
     ref = oracle_full(wl, r, "w8a8", rows=rows)
     got = np64(r["out"])[rows]
     err = rel_l2(got, ref)
-    print(f"l16384 end-to-end sampled rel-L2 {err:.3e}")
+    x = np64(r["x"])[rows]
+    print(f"l16384 end-to-end sampled rel-L2 {err:.3e}, update {rel_l2(got - x, ref - x):.3e}")
     assert err <= 2e-2
     check_stages(wl, r, rows)
 
@@ -206,7 +226,7 @@ def test_block_l16384_sampled():
 def test_block_l16384_fp32_sampled():
     wl = S.WORKLOADS["block_l16384"]
     r = run_gpu(wl, h3k.F_FP32_DEBUG, gen_device="cuda")
-    check_stages(wl, r, _sample_rows(wl.L, 24, 3), tol_x2=1e-3)
+    check_stages(wl, r, _sample_rows(wl.L, 24, 3))
 
 
 def test_block_l65536_stages():

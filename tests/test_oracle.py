@@ -57,6 +57,20 @@ def test_quant_zero_row():
     assert np.all(q == 0) and np.all(s == 0)
 
 
+# ----------------------------------------------------------------------------- bf16 rounding
+def test_round_bf16_vs_torch_and_ties():
+    v32 = (rng.standard_normal(20000) * rng.uniform(1e-3, 1e3, 20000)).astype(np.float32)
+    want = torch.tensor(v32).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(O.round_bf16(v32.astype(np.float64)), want)
+    one = 1.0
+    ulp = 2.0 ** -7  # bf16 spacing just above 1
+    assert O.round_bf16(one + ulp / 2) == one              # tie -> even (1.0)
+    assert O.round_bf16(one + 3 * ulp / 2) == one + 2 * ulp  # tie -> even
+    assert O.round_bf16(one + ulp / 2 + 1e-12) == one + ulp  # above the tie
+    assert O.round_bf16(-(one + ulp / 2 + 1e-12)) == -(one + ulp)
+    assert O.round_bf16(0.0) == 0.0
+
+
 # ----------------------------------------------------------------------------- int8 GEMM
 def test_int8_matmul_bruteforce():
     a = rng.integers(-127, 128, size=(5, 11)).astype(np.int8)

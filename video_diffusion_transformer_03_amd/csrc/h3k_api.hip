@@ -135,8 +135,10 @@ void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
   w->q = take(H * Lz * Dh * T);
   w->k = take(H * Lz * Dh * T);
   w->vt = take(H * Lz * Dh * T);
-  w->o = take(Lz * d * T);
-  w->g = take(Lz * F * T);
+  // O, x1 and g feed quantisers (or the next GEMM): fp32 except on the dense bf16 path
+  w->o = take(Lz * d * (bf ? 2 : 4));
+  w->x1 = take(Lz * d * 4);
+  w->g = take(Lz * F * (bf ? 2 : 4));
   w->h = bf ? take(Lz * d * 2) : 0;
   w->h2 = bf ? take(Lz * d * 2) : 0;
   w->total = off;
@@ -240,18 +242,19 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
-                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, s);
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !bf, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
   // S5: quantise O
   if (!bf) {
     Launch l(H3K_K_ROWQUANT_O, s, flags);
-    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), f32, nullptr, nullptr, L, d, 0.f,
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), true, nullptr, nullptr, L, d, 0.f,
                                  at<int8_t>(ws, lay.qo), at<float>(ws, lay.s_o), nullptr, s),
                      fn, "rowquant_o")))
       return rc;
   }
-  // S6: out-proj + gated residual -> x_out holds x1
+  // S6: out-proj + gated residual -> x1 (fp32, workspace)
+  float *x1 = at<float>(ws, lay.x1);
   {
     GemmArgs a = ga;
     a.A = bf ? (const void *)at<uint16_t>(ws, lay.o) : (const void *)at<int8_t>(ws, lay.qo);
@@ -260,8 +263,10 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.K = d;
     a.sa = at<float>(ws, lay.s_o);
     a.sw = w->s_o;
-    a.out = x_out;
+    a.out = x1;
+    a.out_f32 = true;
     a.res = x_in;
+    a.res_f32 = f32;
     a.gate = gate1;
     Launch l(H3K_K_GEMM_O, s, flags);
     if ((rc = l.done(launch_gemm(EPI_RESID, a, s), fn, "gemm_o"))) return rc;
@@ -269,9 +274,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // S7: LN + modulate (+ quant) of x1
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
-    hipError_t e = bf ? launch_rows(1, x_out, false, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
+    hipError_t e = bf ? launch_rows(1, x1, true, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
                                     at<uint16_t>(ws, lay.h2), s)
-                      : launch_rows(0, x_out, f32, shift2, scale2, L, d, dm->ln_eps,
+                      : launch_rows(0, x1, true, shift2, scale2, L, d, dm->ln_eps,
                                     at<int8_t>(ws, lay.qa2), at<float>(ws, lay.s_a2), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant_2"))) return rc;
   }
@@ -285,18 +290,19 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.sa = at<float>(ws, lay.s_a2);
     a.sw = w->s_up;
     a.out = at<void>(ws, lay.g);
+    a.out_f32 = !bf;
     Launch l(H3K_K_GEMM_UP, s, flags);
     if ((rc = l.done(launch_gemm(EPI_GELU, a, s), fn, "gemm_up"))) return rc;
   }
   // S9: quantise g
   if (!bf) {
     Launch l(H3K_K_ROWQUANT_G, s, flags);
-    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), f32, nullptr, nullptr, L, F, 0.f,
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), true, nullptr, nullptr, L, F, 0.f,
                                  at<int8_t>(ws, lay.qg), at<float>(ws, lay.s_g), nullptr, s),
                      fn, "rowquant_g")))
       return rc;
   }
-  // S10: MLP down + gated residual, in place on x_out
+  // S10: MLP down + gated residual: x_out = x1 + gate2 * y
   {
     GemmArgs a = ga;
     a.A = bf ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
@@ -306,7 +312,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.sa = at<float>(ws, lay.s_g);
     a.sw = w->s_down;
     a.out = x_out;
-    a.res = x_out;
+    a.out_f32 = f32;
+    a.res = x1;
+    a.res_f32 = true;
     a.gate = gate2;
     Launch l(H3K_K_GEMM_DOWN, s, flags);
     if ((rc = l.done(launch_gemm(EPI_RESID, a, s), fn, "gemm_down"))) return rc;
@@ -392,8 +400,8 @@ int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t 
   if (!(softmax_scale > 0.f)) return fail(H3K_EINVAL, "%s: softmax_scale must be positive", fn);
   hipStream_t s = (hipStream_t)stream;
   Launch l(H3K_K_ATTENTION, s, flags);
-  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale,
-                                 (flags & H3K_F_FP32_DEBUG) != 0, s),
+  const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
+  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, f32, f32, s),
                 fn, "attention");
 }
 

@@ -70,7 +70,8 @@ struct GemmArgs {
   int64_t M;
   int N, K;            // K in elements
   bool bf16_ops;       // bf16 operands (fp32 accumulation, no dequant scales)
-  bool out_f32;        // fp32 outputs (debug path) instead of bf16
+  bool out_f32;        // fp32 outputs instead of bf16
+  bool res_f32;        // EPI_RESID: fp32 residual input instead of bf16
   const float *sa;     // per-row (token) scales [M]     (int8 only)
   const float *sw;     // per-column (channel) scales [N] (int8 only)
   // EPI_RAW_I32
@@ -87,8 +88,11 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(EpiKind kind, const GemmArgs &a, hipStream_t s);
 
-// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]
+// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. in_f32: fp32 inputs (plain
+// FMA kernel, fp32 output); otherwise bf16 inputs on the matrix cores with a bf16 or
+// (out_f32) fp32 output.
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, float scale, bool f32, hipStream_t s);
+                            int64_t L, int Dh, float scale, bool in_f32, bool out_f32,
+                            hipStream_t s);
 
 }  // namespace h3k

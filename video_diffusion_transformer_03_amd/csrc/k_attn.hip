@@ -34,11 +34,15 @@ struct AttnCfg {
   static constexpr int VCH = DH * BK / 8 / 256;  // 16-byte chunks per thread, V^T tile
 };
 
-template <int DH>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const uint16_t *__restrict__ Q,
+#ifndef H3K_ATTN_OCC
+#define H3K_ATTN_OCC 2  // waves per SIMD the register budget is sized for
+#endif
+
+template <int DH, bool OF32>
+__global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(const uint16_t *__restrict__ Q,
                                                         const uint16_t *__restrict__ K,
                                                         const uint16_t *__restrict__ Vt,
-                                                        uint16_t *__restrict__ O, int H,
+                                                        void *__restrict__ Ov, int H,
                                                         int64_t L, float sl2) {
   using C = AttnCfg<DH>;
   constexpr int BK = C::BK, KP = C::KP, VP = C::VP;
@@ -202,12 +206,17 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const uint16_t *__restri
     const float inv = 1.0f / l;
     const int64_t qi = q0 + qt * 16 + c16;
     if (qi < L) {
-      uint16_t *orow = O + qi * ldo + (int64_t)head * DH + g * 4;
+      const int64_t obase = qi * ldo + (int64_t)head * DH + g * 4;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         v4f v = o[dt][qt];
-        *(uint2 *)(orow + dt * 16) =
-            make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
+        if constexpr (OF32) {
+          *(float4 *)((float *)Ov + obase + dt * 16) =
+              make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        } else {
+          *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
+              make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
+        }
       }
     }
   }
@@ -283,17 +292,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
   }
 }
 
-template <int DH>
-static hipError_t attn_dispatch(const void *q, const void *k, const void *vt, void *o, int H,
-                                int64_t L, float sl2, bool f32, hipStream_t s) {
-  if (f32) {
-    dim3 grid((unsigned)((L + 63) / 64), (unsigned)H);
-    attn_f32_kernel<DH><<<grid, 256, 0, s>>>((const float *)q, (const float *)k,
-                                             (const float *)vt, (float *)o, H, L, sl2);
-    return hipGetLastError();
-  }
+template <int DH, bool OF32>
+static hipError_t attn_mfma(const void *q, const void *k, const void *vt, void *o, int H,
+                            int64_t L, float sl2, hipStream_t s) {
   using C = AttnCfg<DH>;
-  auto kern = attn_bf16_kernel<DH>;
+  auto kern = attn_bf16_kernel<DH, OF32>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -303,15 +306,29 @@ static hipError_t attn_dispatch(const void *q, const void *k, const void *vt, vo
   }
   dim3 grid((unsigned)((L + C::BQ - 1) / C::BQ), (unsigned)H);
   kern<<<grid, 256, C::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
-                                 (const uint16_t *)vt, (uint16_t *)o, H, L, sl2);
+                                 (const uint16_t *)vt, o, H, L, sl2);
   return hipGetLastError();
 }
 
+template <int DH>
+static hipError_t attn_dispatch(const void *q, const void *k, const void *vt, void *o, int H,
+                                int64_t L, float sl2, bool in_f32, bool out_f32, hipStream_t s) {
+  if (in_f32) {
+    dim3 grid((unsigned)((L + 63) / 64), (unsigned)H);
+    attn_f32_kernel<DH><<<grid, 256, 0, s>>>((const float *)q, (const float *)k,
+                                             (const float *)vt, (float *)o, H, L, sl2);
+    return hipGetLastError();
+  }
+  return out_f32 ? attn_mfma<DH, true>(q, k, vt, o, H, L, sl2, s)
+                 : attn_mfma<DH, false>(q, k, vt, o, H, L, sl2, s);
+}
+
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, float scale, bool f32, hipStream_t s) {
+                            int64_t L, int Dh, float scale, bool in_f32, bool out_f32,
+                            hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2(e))
-  if (Dh == 128) return attn_dispatch<128>(q, k, vt, o, H, L, sl2, f32, s);
-  if (Dh == 64) return attn_dispatch<64>(q, k, vt, o, H, L, sl2, f32, s);
+  if (Dh == 128) return attn_dispatch<128>(q, k, vt, o, H, L, sl2, in_f32, out_f32, s);
+  if (Dh == 64) return attn_dispatch<64>(q, k, vt, o, H, L, sl2, in_f32, out_f32, s);
   return hipErrorInvalidValue;
 }
 

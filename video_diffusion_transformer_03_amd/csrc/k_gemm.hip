@@ -25,6 +25,14 @@
 
 namespace h3k {
 
+// work-group tile (BN weights rows x BM tokens) and wave grid (WN x WM waves)
+#ifndef H3K_GEMM_BN
+#define H3K_GEMM_BN 256
+#define H3K_GEMM_BM 256
+#define H3K_GEMM_WN 2
+#define H3K_GEMM_WM 4
+#endif
+
 constexpr int KB = 128;       // bytes of K staged per pipeline step
 constexpr int KBP = KB + 16;  // LDS row pitch (bytes): 16-byte pad spreads rows over banks
 
@@ -94,7 +102,7 @@ __device__ __forceinline__ auto mma(v4i b, v4i a, typename std::conditional<BF16
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, c, 0, 0, 0);
 }
 
-template <int BN, int BM, int WN, int WM, bool BF16, int EPI, bool OUTF32>
+template <int BN, int BM, int WN, int WM, bool BF16, int EPI, bool OUTF32, bool RESF32>
 __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
   constexpr int NT = WN * WM * 64;
   constexpr int TN = BN / WN / 16;  // 16-row MFMA tiles per wave along N
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
                          gelu_erf(y[3]));
         } else if constexpr (EPI == EPI_RESID) {
           float r4[4];
-          load4<OUTF32>(a.res, m * a.N + n, r4);
+          load4<RESF32>(a.res, m * a.N + n, r4);
           const float4 g4 = *(const float4 *)(a.gate + n);
           store4<OUTF32>(a.out, m * a.N + n, r4[0] + g4.x * y[0], r4[1] + g4.y * y[1],
                          r4[2] + g4.z * y[2], r4[3] + g4.w * y[3]);
@@ -265,9 +273,9 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
 #undef H3K_LSTORE
 #undef H3K_COMPUTE
 
-template <int BN, int BM, int WN, int WM, bool BF16, int EPI, bool OUTF32>
+template <int BN, int BM, int WN, int WM, bool BF16, int EPI, bool OUTF32, bool RESF32>
 static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
-  auto kern = gemm_kernel<BN, BM, WN, WM, BF16, EPI, OUTF32>;
+  auto kern = gemm_kernel<BN, BM, WN, WM, BF16, EPI, OUTF32, RESF32>;
   constexpr size_t lds = gemm_lds_bytes<BN, BM>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -282,31 +290,47 @@ static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool BF16, int EPI, bool OUTF32>
+template <bool BF16, int EPI, bool OUTF32, bool RESF32>
 static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
-  return run_gemm<128, 128, 2, 2, BF16, EPI, OUTF32>(a, s);
+  return run_gemm<H3K_GEMM_BN, H3K_GEMM_BM, H3K_GEMM_WN, H3K_GEMM_WM, BF16, EPI, OUTF32, RESF32>(a, s);
 }
 
-template <int EPI>
-static hipError_t gemm_types(const GemmArgs &a, hipStream_t s) {
-  if (a.bf16_ops) {
-    if (a.out_f32) return hipErrorInvalidValue;
-    return gemm_tiles<true, EPI, false>(a, s);
+// instantiated type combinations:
+//   QKV    int8 -> bf16 | int8 -> fp32 | bf16 -> bf16
+//   GELU   int8 -> fp32 | bf16 -> bf16
+//   RESID  residual/out: bf16/fp32, fp32/fp32, fp32/bf16 (int8 and bf16 operands)
+static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) {
+  const bool B = a.bf16_ops, OF = a.out_f32, RF = a.res_f32;
+  switch (kind) {
+    case EPI_QKV:
+      if (B) return OF ? hipErrorInvalidValue : gemm_tiles<true, EPI_QKV, false, false>(a, s);
+      return OF ? gemm_tiles<false, EPI_QKV, true, false>(a, s)
+                : gemm_tiles<false, EPI_QKV, false, false>(a, s);
+    case EPI_GELU:
+      if (B) return OF ? hipErrorInvalidValue : gemm_tiles<true, EPI_GELU, false, false>(a, s);
+      return OF ? gemm_tiles<false, EPI_GELU, true, false>(a, s) : hipErrorInvalidValue;
+    case EPI_RESID:
+      if (!RF && OF)
+        return B ? gemm_tiles<true, EPI_RESID, true, false>(a, s)
+                 : gemm_tiles<false, EPI_RESID, true, false>(a, s);
+      if (RF && OF)
+        return B ? hipErrorInvalidValue : gemm_tiles<false, EPI_RESID, true, true>(a, s);
+      if (RF && !OF)
+        return B ? gemm_tiles<true, EPI_RESID, false, true>(a, s)
+                 : gemm_tiles<false, EPI_RESID, false, true>(a, s);
+      return hipErrorInvalidValue;
+    default:
+      return hipErrorInvalidValue;
   }
-  if (a.out_f32) return gemm_tiles<false, EPI, true>(a, s);
-  return gemm_tiles<false, EPI, false>(a, s);
 }
 
 hipError_t launch_gemm(EpiKind kind, const GemmArgs &a, hipStream_t s) {
-  switch (kind) {
-    case EPI_RAW_I32:
-      if (a.bf16_ops || a.out_f32) return hipErrorInvalidValue;
-      return run_gemm<128, 128, 2, 2, false, EPI_RAW_I32, false>(a, s);
-    case EPI_QKV: return gemm_types<EPI_QKV>(a, s);
-    case EPI_GELU: return gemm_types<EPI_GELU>(a, s);
-    case EPI_RESID: return gemm_types<EPI_RESID>(a, s);
+  if (kind == EPI_RAW_I32) {
+    if (a.bf16_ops || a.out_f32) return hipErrorInvalidValue;
+    return run_gemm<H3K_GEMM_BN, H3K_GEMM_BM, H3K_GEMM_WN, H3K_GEMM_WM, false, EPI_RAW_I32, false,
+                    false>(a, s);
   }
-  return hipErrorInvalidValue;
+  return gemm_dispatch(kind, a, s);
 }
 
 }  // namespace h3k

@@ -306,7 +306,7 @@ hipError_t launch_rows(int mode, const void *x, bool x_f32, const float *shift,
     const float *xf = (const float *)x;
     if (mode == RM_LNQ) return rows_wpr<RM_LNQ, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);
     if (mode == RM_Q) return rows_wpr<RM_Q, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);
-    return hipErrorInvalidValue;
+    return rows_wpr<RM_LN_BF16, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);
   }
   const uint16_t *xb = (const uint16_t *)x;
   if (mode == RM_LNQ) return rows_wpr<RM_LNQ, uint16_t>(xb, shift, scale, rows, cols, eps, q, sc, hout, s);

@@ -45,7 +45,7 @@ class BlockWeightsC(C.Structure):
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
         "m", "rope", "s_a", "s_o", "s_a2", "s_g", "qa", "qo", "qa2", "qg", "q", "k", "vt",
-        "o", "g", "h", "h2", "total")]
+        "o", "x1", "g", "h", "h2", "total")]
 
 
 _lib = None
