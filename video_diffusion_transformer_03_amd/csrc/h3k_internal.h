@@ -3,6 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace h3k {
 
 // ---------------------------------------------------------------- device helpers
@@ -10,14 +13,29 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, every index a
+// constant at inlining time (keeps small register arrays out of scratch memory).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // fp32 -> bf16, round to nearest even (hardware conversion on gfx950)
 __device__ __forceinline__ uint16_t f2bf(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 pair (a in the low half), round to nearest even
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  v2bf h = __builtin_convertvector((v2f){a, b}, v2bf);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -21,12 +21,22 @@ namespace h3k {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
+#ifndef H3K_ATTN_OCC
+#define H3K_ATTN_OCC 2  // waves per SIMD the register budget is sized for
+#endif
+#ifndef H3K_ATTN_KPAD
+#define H3K_ATTN_KPAD 16  // elements of padding per K-tile row in LDS
+#endif
+#ifndef H3K_ATTN_VPAD
+#define H3K_ATTN_VPAD 16  // elements of padding per V^T-tile row in LDS
+#endif
+
 template <int DH>
 struct AttnCfg {
-  static constexpr int BQ = 128;        // queries per work-group (4 waves x 32)
-  static constexpr int BK = 64;         // keys per tile
-  static constexpr int KP = DH + 8;     // K tile row pitch (elements)
-  static constexpr int VP = BK + 8;     // V^T tile row pitch (elements)
+  static constexpr int BQ = 128;                  // queries per work-group (4 waves x 32)
+  static constexpr int BK = 64;                   // keys per tile
+  static constexpr int KP = DH + H3K_ATTN_KPAD;   // K tile row pitch (elements)
+  static constexpr int VP = BK + H3K_ATTN_VPAD;   // V^T tile row pitch (elements)
   static constexpr int K_ELEMS = BK * KP;
   static constexpr int V_ELEMS = DH * VP;
   static constexpr size_t LDS = (size_t)2 * (K_ELEMS + V_ELEMS) * 2;
@@ -34,20 +44,121 @@ struct AttnCfg {
   static constexpr int VCH = DH * BK / 8 / 256;  // 16-byte chunks per thread, V^T tile
 };
 
-#ifndef H3K_ATTN_OCC
-#define H3K_ATTN_OCC 2  // waves per SIMD the register budget is sized for
-#endif
+// Lazy rescaling: the running maximum used for exp2 is only moved when a row's true
+// maximum exceeds it by more than 2^8 -- P stays <= 256 and the O/l rescale (one multiply
+// per accumulator) is skipped in most tiles. Softmax is invariant to the subtracted
+// constant, so the result is unchanged.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Key order inside a 32-key block: S^T tile t (16 rows) takes key 8*(i/4) + 4*t + i%4 in
+// its row i, so the 8 P^T slots a lane group g holds (rows 4g..4g+3 of tiles 0 and 1) are
+// the 8 consecutive keys 8g..8g+7 -- one 16-byte V^T read per operand. The permutation is
+// applied when the K tile is written to LDS (key k of a block goes to row krow_of(k)), so
+// the fragment reads walk LDS rows in natural order (bank-conflict free at this pitch).
+__device__ __forceinline__ int kperm(int t, int i) { return 8 * (i >> 2) + 4 * t + (i & 3); }
+__device__ __forceinline__ int krow_of(int key) {  // inverse of kperm within 32-key blocks
+  const int k = key & 31;
+  return (key & ~31) + ((k >> 2) & 1) * 16 + (k >> 3) * 4 + (k & 3);
+}
+
+struct AttnState {
+  v4f o[8][2];   // O^T accumulators (dh tile, query tile); up to DH = 128
+  float m[2];    // running max (log2 domain, scaled) per query tile
+  float l[2];    // per-lane partial row sums
+};
+
+// one K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T
+template <int DH, bool MASK>
+__device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH / 32],
+                                          const uint16_t *cK, const uint16_t *cV, int lane,
+                                          int64_t k0, int64_t L, float sl2) {
+  using C = AttnCfg<DH>;
+  constexpr int KP = C::KP, VP = C::VP, NKK = DH / 32, NDT = DH / 16;
+  const int g = lane >> 4, c16 = lane & 15;
+  v4f s[4][2];
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4) s[t4][0] = s[t4][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      v8bf kf = __builtin_bit_cast(v8bf, ld16(cK + (t4 * 16 + c16) * KP + kk * 32 + g * 8));
+      s[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], s[t4][0], 0, 0, 0);
+      s[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], s[t4][1], 0, 0, 0);
+    }
+  }
+  // lane holds S^T for query c16 and keys k0 + (t4/2)*32 + kperm(t4&1, 4g + r)
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    if constexpr (MASK) {
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + (t4 >> 1) * 32 + kperm(t4 & 1, 4 * g + r) >= L) s[t4][qt][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
+#pragma unroll
+    for (int t4 = 1; t4 < 4; ++t4)
+      mx = fmaxf(mx, fmaxf(fmaxf(s[t4][qt][0], s[t4][qt][1]), fmaxf(s[t4][qt][2], s[t4][qt][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = mx * sl2;
+    const bool grow = mnew > st.m[qt] + kRescaleLog2;
+    if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
+      const float mref = grow ? mnew : st.m[qt];
+      const float alpha = __builtin_amdgcn_exp2f(st.m[qt] - mref);
+      st.m[qt] = mref;
+      st.l[qt] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) st.o[i][qt] *= alpha;
+    }
+    const float mneg = -st.m[qt];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s[t4][qt][r] = __builtin_amdgcn_exp2f(fmaf(s[t4][qt][r], sl2, mneg));
+  }
+  // O^T += V^T P^T over two 32-key steps; slots of lane group g = keys 8g .. 8g+7. The
+  // row sum l accumulates the same bf16-rounded P the matrix cores consume (one dot2 per
+  // packed pair against (1, 1)), so O = sum(p v) / sum(p) is normalised consistently.
+  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    v8bf pb[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      uint4 u;
+      u.x = pack_bf2(s[2 * ks][qt][0], s[2 * ks][qt][1]);
+      u.y = pack_bf2(s[2 * ks][qt][2], s[2 * ks][qt][3]);
+      u.z = pack_bf2(s[2 * ks + 1][qt][0], s[2 * ks + 1][qt][1]);
+      u.w = pack_bf2(s[2 * ks + 1][qt][2], s[2 * ks + 1][qt][3]);
+      float l = st.l[qt];
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.x), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.y), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.z), ones, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.w), ones, l, false);
+      st.l[qt] = l;
+      pb[qt] = __builtin_bit_cast(v8bf, u);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      v8bf vf = __builtin_bit_cast(v8bf, ld16(cV + (dt * 16 + c16) * VP + ks * 32 + g * 8));
+      st.o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0], st.o[dt][0], 0, 0, 0);
+      st.o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1], st.o[dt][1], 0, 0, 0);
+    }
+  }
+}
 
 template <int DH, bool OF32>
-__global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(const uint16_t *__restrict__ Q,
-                                                        const uint16_t *__restrict__ K,
-                                                        const uint16_t *__restrict__ Vt,
-                                                        void *__restrict__ Ov, int H,
-                                                        int64_t L, float sl2) {
+__global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ Vt, void *__restrict__ Ov, int H, int64_t L, float sl2) {
   using C = AttnCfg<DH>;
   constexpr int BK = C::BK, KP = C::KP, VP = C::VP;
-  constexpr int NKK = DH / 32;  // K-steps of the QK^T product (32 head dims each)
-  constexpr int NDT = DH / 16;  // 16-row output tiles along the head dim
+  constexpr int NKK = DH / 32;
+  constexpr int NDT = DH / 16;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   uint16_t *sK = lds;                   // [2][BK][KP]
   uint16_t *sV = lds + 2 * C::K_ELEMS;  // [2][DH][VP]
@@ -59,148 +170,83 @@ __global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(const uint
   const uint16_t *Kh = K + (int64_t)head * L * DH;
   const uint16_t *Vh = Vt + (int64_t)head * DH * L;
   const int g = lane >> 4, c16 = lane & 15;
+  const uint32_t Lu = (uint32_t)L;
 
-  // Q^T operand: lane supplies query (q0 + qt*16 + c16), head dims kk*32 + g*8 .. +8
+  // Q^T operand: lane supplies query (q0 + qt*16 + c16), head dims kk*32 + g*8 .. +8;
+  // query rows past L read row L-1 and are not stored
   v8bf qf[2][NKK];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    // query rows past L read row L-1; their outputs are not stored
     const int64_t qi = (q0 + qt * 16 + c16) < L ? (q0 + qt * 16 + c16) : (L - 1);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      uint4 u = ld16(Qh + qi * DH + kk * 32 + g * 8);
-      qf[qt][kk] = __builtin_bit_cast(v8bf, u);
-    }
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[qt][kk] = __builtin_bit_cast(v8bf, ld16(Qh + qi * DH + kk * 32 + g * 8));
   }
 
-  v4f o[NDT][2];
+  AttnState st;
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) o[i][0] = o[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  for (int i = 0; i < 8; ++i) st.o[i][0] = st.o[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  st.m[0] = st.m[1] = -INFINITY;
+  st.l[0] = st.l[1] = 0.f;
 
+  // staged-tile coordinates: thread tid moves 16-byte chunk tid + 256*i of each tile.
+  // K tile [BK][DH]: row kr0 + i*KRI, column kc; V^T tile [DH][BK]: row vr0 + i*VRI,
+  // column vc. Element offsets are 32-bit (L*DH < 2^31).
+  constexpr int KCPR = DH / 8, VCPR = BK / 8;   // chunks per row
+  constexpr int KRI = 256 / KCPR, VRI = 256 / VCPR;
+  const int kr0 = tid / KCPR, kc = (tid % KCPR) * 8;
+  const int vr0 = tid / VCPR, vc = (tid % VCPR) * 8;
   uint4 rk[C::KCH], rv[C::VCH];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int c = tid + i * 256, row = c / (DH / 8), col = c % (DH / 8);
-      // keys past L read key L-1: their scores are masked to -inf, so p = 0
-      const int64_t key = (k0 + row) < L ? (k0 + row) : (L - 1);
-      rk[i] = ld16(Kh + key * DH + col * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int c = tid + i * 256, row = c / (BK / 8), col = c % (BK / 8);
-      // L % 8 == 0: a chunk is all valid or all past L; chunks past L read the last valid
-      // chunk, whose finite values meet p = 0
-      const int64_t key = (k0 + col * 8) < L ? (k0 + col * 8) : (L - 8);
-      rv[i] = ld16(Vh + (int64_t)row * L + key);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int c = tid + i * 256, row = c / (DH / 8), col = c % (DH / 8);
-      *(uint4 *)(sK + buf * C::K_ELEMS + row * KP + col * 8) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int c = tid + i * 256, row = c / (BK / 8), col = c % (BK / 8);
-      *(uint4 *)(sV + buf * C::V_ELEMS + row * VP + col * 8) = rv[i];
-    }
-  };
+  // keys past L read key L-1 (K) or the last valid 8-key chunk (V^T; L % 8 == 0): their
+  // scores are masked to -inf, so their p = 0 meets finite values
+#define H3K_ATTN_GLOAD(kt_)                                                                    \
+  {                                                                                            \
+    const uint32_t k0_ = (uint32_t)(kt_) * BK;                                                 \
+    _Pragma("unroll") for (int i = 0; i < C::KCH; ++i) {                                       \
+      const uint32_t key = min(k0_ + (uint32_t)(kr0 + i * KRI), Lu - 1u);                      \
+      rk[i] = ld16(Kh + key * DH + kc);                                                        \
+    }                                                                                          \
+    const uint32_t vkey = min(k0_ + (uint32_t)vc, Lu - 8u);                                    \
+    _Pragma("unroll") for (int i = 0; i < C::VCH; ++i)                                         \
+        rv[i] = ld16(Vh + (uint32_t)(vr0 + i * VRI) * Lu + vkey);                              \
+  }
+#define H3K_ATTN_LSTORE(buf_)                                                                  \
+  {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < C::KCH; ++i)                                         \
+        *(uint4 *)(sK + (buf_) * C::K_ELEMS + krow_of(kr0 + i * KRI) * KP + kc) = rk[i];     \
+    _Pragma("unroll") for (int i = 0; i < C::VCH; ++i)                                         \
+        *(uint4 *)(sV + (buf_) * C::V_ELEMS + (vr0 + i * VRI) * VP + vc) = rv[i];              \
+  }
 
   const int nkt = (int)((L + BK - 1) / BK);
-  gload(0);
-  lstore(0);
+  const bool tail = (L % BK) != 0;
+  H3K_ATTN_GLOAD(0);
+  H3K_ATTN_LSTORE(0);
   __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = 0; kt + 1 < nkt; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const uint16_t *cK = sK + cur * C::K_ELEMS;
-    const uint16_t *cV = sV + cur * C::V_ELEMS;
-
-    // S^T[key][query] for 4 key tiles x 2 query tiles
-    v4f s[4][2];
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) s[t4][0] = s[t4][1] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        v8bf kf = __builtin_bit_cast(v8bf, ld16(cK + (t4 * 16 + c16) * KP + kk * 32 + g * 8));
-        s[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], s[t4][0], 0, 0, 0);
-        s[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], s[t4][1], 0, 0, 0);
-      }
-    }
-
-    // online softmax; lane holds keys kt*BK + t4*16 + g*4 + r of query c16
-    const int64_t kbase = (int64_t)kt * BK + g * 4;
-    const bool tail = (int64_t)(kt + 1) * BK > L;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = s[t4][qt][r] * sl2;
-          if (tail && kbase + t4 * 16 + r >= L) v = -INFINITY;
-          s[t4][qt][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrow[qt], mx);
-      const float alpha = exp2f(mrow[qt] - mnew);
-      mrow[qt] = mnew;
-      float ps = 0.f;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[t4][qt][r] - mnew);
-          s[t4][qt][r] = p;
-          ps += p;
-        }
-      lsum[qt] = lsum[qt] * alpha + ps;
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) o[i][qt] *= alpha;
-    }
-
-    // O^T += V^T P^T over two 32-key steps
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8bf pb[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        uint4 u;
-        u.x = pack_bf2(s[2 * ks][qt][0], s[2 * ks][qt][1]);
-        u.y = pack_bf2(s[2 * ks][qt][2], s[2 * ks][qt][3]);
-        u.z = pack_bf2(s[2 * ks + 1][qt][0], s[2 * ks + 1][qt][1]);
-        u.w = pack_bf2(s[2 * ks + 1][qt][2], s[2 * ks + 1][qt][3]);
-        pb[qt] = __builtin_bit_cast(v8bf, u);
-      }
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint16_t *vr = cV + (dt * 16 + c16) * VP + g * 4;
-        uint2 v0 = *(const uint2 *)(vr + (2 * ks) * 16);
-        uint2 v1 = *(const uint2 *)(vr + (2 * ks + 1) * 16);
-        v8bf vf = __builtin_bit_cast(v8bf, make_uint4(v0.x, v0.y, v1.x, v1.y));
-        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0], o[dt][0], 0, 0, 0);
-        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1], o[dt][1], 0, 0, 0);
-      }
-    }
-
-    if (kt + 1 < nkt) lstore(cur ^ 1);
+    H3K_ATTN_GLOAD(kt + 1);
+    attn_tile<DH, false>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
+                         (int64_t)kt * BK, L, sl2);
+    H3K_ATTN_LSTORE(cur ^ 1);
     __syncthreads();
   }
+  {
+    const int cur = (nkt - 1) & 1;
+    if (tail)
+      attn_tile<DH, true>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
+                          (int64_t)(nkt - 1) * BK, L, sl2);
+    else
+      attn_tile<DH, false>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
+                           (int64_t)(nkt - 1) * BK, L, sl2);
+  }
+#undef H3K_ATTN_GLOAD
+#undef H3K_ATTN_LSTORE
 
   const int64_t ldo = (int64_t)H * DH;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    float l = lsum[qt];
+    float l = st.l[qt];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float inv = 1.0f / l;
@@ -209,7 +255,7 @@ __global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(const uint
       const int64_t obase = qi * ldo + (int64_t)head * DH + g * 4;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        v4f v = o[dt][qt];
+        v4f v = st.o[dt][qt];
         if constexpr (OF32) {
           *(float4 *)((float *)Ov + obase + dt * 16) =
               make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);

@@ -33,8 +33,12 @@ namespace h3k {
 #define H3K_GEMM_WM 4
 #endif
 
-constexpr int KB = 128;       // bytes of K staged per pipeline step
-constexpr int KBP = KB + 16;  // LDS row pitch (bytes): 16-byte pad spreads rows over banks
+#ifndef H3K_GEMM_PAD
+#define H3K_GEMM_PAD 32  // 160-byte pitch: conflict-free 16-byte fragment reads on gfx950
+#endif
+
+constexpr int KB = 128;                 // bytes of K staged per pipeline step
+constexpr int KBP = KB + H3K_GEMM_PAD;  // LDS row pitch (bytes): the pad spreads rows over banks
 
 template <int BN, int BM>
 constexpr size_t gemm_lds_bytes() {
@@ -93,6 +97,14 @@ __device__ __forceinline__ float2 rope_cs(const float2 *tbl, const RopeGeom &g, 
   return tbl[e];
 }
 
+template <int I, typename T>
+__device__ __forceinline__ T &pick(T &a, T &b, T &c, T &d) {
+  if constexpr (I == 0) return a;
+  else if constexpr (I == 1) return b;
+  else if constexpr (I == 2) return c;
+  else return d;
+}
+
 template <bool BF16>
 __device__ __forceinline__ auto mma(v4i b, v4i a, typename std::conditional<BF16, v4f, v4i>::type c) {
   if constexpr (BF16)
@@ -143,31 +155,33 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
   const uint8_t *gB = (const uint8_t *)a.B;
   const int nk = (int)(Kb / KB);
 
-  uint4 rb[CH_B], ra[CH_A];
+  // staging registers (named scalars, not arrays: they stay in VGPRs across iterations)
+  static_assert(CH_B <= 4 && CH_A <= 4, "at most 4 staged chunks per thread and operand");
+  uint4 rb0, rb1, rb2, rb3, ra0, ra1, ra2, ra3;
 #define H3K_GLOAD(kt_)                                                                       \
   {                                                                                          \
     const int64_t kof = (int64_t)(kt_) * KB;                                                 \
-    _Pragma("unroll") for (int i = 0; i < CH_B; ++i) {                                       \
-      const int c = tid + i * NT, row = c / CPR, col = c % CPR;                              \
-      rb[i] = *(const uint4 *)(gB + (int64_t)(n0 + row) * Kb + kof + col * 16);              \
-    }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < CH_A; ++i) {                                       \
-      const int c = tid + i * NT, row = c / CPR, col = c % CPR;                              \
-      /* rows past M read row M-1: they only feed output rows that are never stored */   \
+    static_for<CH_B>([&](auto I) {                                                           \
+      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
+      pick<I>(rb0, rb1, rb2, rb3) = *(const uint4 *)(gB + (int64_t)(n0 + row) * Kb + kof + col * 16);              \
+    });                                                                                      \
+    static_for<CH_A>([&](auto I) {                                                           \
+      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
+      /* rows past M read row M-1: they only feed output rows that are never stored */       \
       const int64_t m = (m0 + row) < a.M ? (m0 + row) : (a.M - 1);                           \
-      ra[i] = *(const uint4 *)(gA + m * Kb + kof + col * 16);                                \
-    }                                                                                        \
+      pick<I>(ra0, ra1, ra2, ra3) = *(const uint4 *)(gA + m * Kb + kof + col * 16);                                \
+    });                                                                                      \
   }
 #define H3K_LSTORE(buf_)                                                                     \
   {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < CH_B; ++i) {                                       \
-      const int c = tid + i * NT, row = c / CPR, col = c % CPR;                              \
-      *(uint4 *)(sB + ((buf_) * BN + row) * KBP + col * 16) = rb[i];                         \
-    }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < CH_A; ++i) {                                       \
-      const int c = tid + i * NT, row = c / CPR, col = c % CPR;                              \
-      *(uint4 *)(sA + ((buf_) * BM + row) * KBP + col * 16) = ra[i];                         \
-    }                                                                                        \
+    static_for<CH_B>([&](auto I) {                                                           \
+      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
+      *(uint4 *)(sB + ((buf_) * BN + row) * KBP + col * 16) = pick<I>(rb0, rb1, rb2, rb3);                         \
+    });                                                                                      \
+    static_for<CH_A>([&](auto I) {                                                           \
+      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
+      *(uint4 *)(sA + ((buf_) * BM + row) * KBP + col * 16) = pick<I>(ra0, ra1, ra2, ra3);                         \
+    });                                                                                      \
   }
 
   AccT acc[TN][TM];
@@ -175,10 +189,6 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = AccT{0, 0, 0, 0};
-
-  H3K_GLOAD(0);
-  H3K_LSTORE(0);
-  __syncthreads();
 
   const int frow = lane & 15, fk = (lane >> 4) * 16;
   // one pipeline step: MFMAs over the KB bytes of K staged in LDS buffer cur_
@@ -196,14 +206,42 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
       _Pragma("unroll") for (int j = 0; j < TM; ++j) acc[i][j] = mma<BF16>(fb[i], fa[j], acc[i][j]); \
     }                                                                                        \
   }
-  // software pipeline: the global loads of step kt+1 are in flight while step kt runs
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    H3K_GLOAD(kt + 1);
-    H3K_COMPUTE(kt & 1);
+  // Software pipeline, prefetch distance 2. Iteration kt: store the registers holding
+  // tile kt+1 (loaded one iteration earlier) into LDS buffer (kt+1)&1, issue the global
+  // loads of tile kt+2, then run the MFMAs of tile kt from buffer kt&1. The barrier that
+  // ends iteration kt-1 separates both the reads of buffer (kt+1)&1 in iteration kt-1
+  // from its rewrite here, and the rewrite of buffer kt&1 from the reads below.
+  H3K_GLOAD(0);
+  H3K_LSTORE(0);
+  H3K_GLOAD(nk > 1 ? 1 : 0);  // (re-reads tile 0 when there is no tile 1; unused then)
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) {
     H3K_LSTORE((kt + 1) & 1);
+    H3K_GLOAD(kt + 2);
+    H3K_COMPUTE(kt & 1);
+#ifdef H3K_GEMM_SGB2
+    // issue order for the scheduler: LDS stores, global loads, then the second K step's
+    // fragment reads spread over the first K step's MFMAs
+    static_assert(KB == 128, "schedule written for two 64-byte K steps");
+    __builtin_amdgcn_sched_group_barrier(0x200, CH_A + CH_B, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, CH_A + CH_B, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);
+    static_for<TN + TM>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, TN * TM * 2 - 2 * (TN + TM), 0);
+#endif
     __syncthreads();
   }
-  H3K_COMPUTE((nk - 1) & 1);
+  if (kt + 1 < nk) {
+    H3K_LSTORE((kt + 1) & 1);
+    H3K_COMPUTE(kt & 1);
+    __syncthreads();
+    ++kt;
+  }
+  H3K_COMPUTE(kt & 1);
 
   // ---- epilogue. acc[i][j][r] = C[m][n] with m = token (lane & 15 within tile j),
   // n = channel (4 * (lane >> 4) + r within tile i).
