@@ -148,6 +148,16 @@ int h3k_block_forward(const void *x_in, void *x_out, const float *cond,
                       const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
                       uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
+/* One block on an explicit token grid (T, Hg, Wg) whose w positions are
+ * w * w_pos_scale + w_pos_offset in RoPE; dm's own grid fields are ignored and
+ * L = T*Hg*Wg. This is the call the stack makes for its horizontally paired middle
+ * blocks (T, Hg, Wg/2 with scale 2 and offset 0.5); h3k_block_forward is the case
+ * (dm grid, 1, 0). Other arguments as for h3k_block_forward. */
+int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
+                           const h3k_block_weights *w, const h3k_dims *dm, int32_t T,
+                           int32_t Hg, int32_t Wg, float w_pos_scale, float w_pos_offset,
+                           uint32_t flags, void *ws, size_t ws_bytes, void *stream);
+
 /* S4. Multi-head softmax attention without mask, bf16 MFMA with fp32 online softmax:
  * o[l, e*Dh + j] = sum_k softmax_k(q[e,l,:] . k[e,k,:] * softmax_scale) v[e,k,j].
  * q, k: bf16 [H, L, Dh]; v: bf16 [H, Dh, L] (transposed, as the QKV projection writes

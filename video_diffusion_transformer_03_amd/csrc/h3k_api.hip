@@ -384,6 +384,35 @@ int h3k_block_forward(const void *x_in, void *x_out, const float *cond,
                     flags, ws, (hipStream_t)stream);
 }
 
+int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
+                           const h3k_block_weights *w, const h3k_dims *dm, int32_t T,
+                           int32_t Hg, int32_t Wg, float w_pos_scale, float w_pos_offset,
+                           uint32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "h3k_block_forward_grid";
+  int rc;
+  if ((rc = check_flags(fn, flags))) return rc;
+  if (!dm) return fail(H3K_EINVAL, "%s: dims is NULL", fn);
+  h3k_dims g = *dm;
+  g.grid_t = T;
+  g.grid_h = Hg;
+  g.grid_w = Wg;
+  const int64_t L = (int64_t)T * Hg * Wg;
+  if ((rc = check_dims(fn, &g, L))) return rc;
+  if (!(w_pos_scale == w_pos_scale) || !(w_pos_offset == w_pos_offset))
+    return fail(H3K_EINVAL, "%s: w position mapping is NaN", fn);
+  H3K_CHECK_PTR(x_in);
+  H3K_CHECK_PTR(x_out);
+  H3K_CHECK_PTR(cond);
+  H3K_CHECK_PTR(ws);
+  if ((rc = check_weights(fn, w, flags))) return rc;
+  h3k_ws_layout lay;
+  plan(&g, L, flags, &lay);
+  if (ws_bytes < lay.total)
+    return fail(H3K_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, lay.total);
+  return block_impl(fn, x_in, x_out, cond, w, &g, T, Hg, Wg, w_pos_scale, w_pos_offset, flags, ws,
+                    (hipStream_t)stream);
+}
+
 int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
                   int64_t L, int32_t head_dim, float softmax_scale, uint32_t flags,
                   void *stream) {

@@ -66,6 +66,8 @@ def lib() -> C.CDLL:
             "h3k_workspace_layout": (C.c_int, [C.POINTER(Dims), i64, u32, C.POINTER(WsLayout)]),
             "h3k_block_forward": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), C.POINTER(Dims),
                                             i64, u32, vp, sz, vp]),
+            "h3k_block_forward_grid": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), C.POINTER(Dims),
+                                                 i32, i32, i32, f32, f32, u32, vp, sz, vp]),
             "h3k_attention": (C.c_int, [vp, vp, vp, vp, i32, i64, i32, f32, u32, vp]),
             "h3k_stack_workspace_bytes": (sz, [C.POINTER(Dims), i64, i32, i32, u32]),
             "h3k_stack_forward": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), i32,
@@ -202,6 +204,26 @@ def block_forward(x: torch.Tensor, cond: torch.Tensor, w: BlockWeights, dims: Di
     _check(lib().h3k_block_forward(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), C.byref(wc),
                                    C.byref(dims), L, flags, _dev(ws, "ws"), ws.numel(),
                                    _stream(stream)))
+    return out
+
+
+def block_forward_grid(x: torch.Tensor, cond: torch.Tensor, w: BlockWeights, dims: Dims, grid,
+                       w_pos_scale: float = 1.0, w_pos_offset: float = 0.0, flags: int = 0,
+                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """One block on the token grid `grid` with w positions w * scale + offset."""
+    T, Hg, Wg = grid
+    L = x.shape[0]
+    if ws is None:
+        g = Dims.from_buffer_copy(dims)
+        g.grid_t, g.grid_h, g.grid_w = T, Hg, Wg
+        ws = alloc_workspace(workspace_bytes(g, L, flags), x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    wc = w.c_struct()
+    _check(lib().h3k_block_forward_grid(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), C.byref(wc),
+                                        C.byref(dims), T, Hg, Wg, float(w_pos_scale), float(w_pos_offset),
+                                        flags, _dev(ws, "ws"), ws.numel(), _stream(stream)))
     return out
 
 
