@@ -88,8 +88,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block_l16384")
     ap.add_argument("--variant", default="w8a8", choices=["w8a8", "bf16gemm", "fp32"])
-    ap.add_argument("--cpu-rows", type=int, default=32)
+    ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the 50-block stack and L=65536 measurements")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB on the device twice (counter calibration) and exit")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters")
     args = ap.parse_args()
@@ -108,6 +112,15 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 2}))
+        return
     wl = S.WORKLOADS[args.workload]
     flags = {"w8a8": 0, "bf16gemm": h3k.F_BF16_GEMM, "fp32": h3k.F_FP32_DEBUG}[args.variant]
 
@@ -183,21 +196,98 @@ def main():
         result["attention_bf16_frac"] = round(work["attention"][1] / (attn_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)
         dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
         dk = kernels[dom]
-        traffic = None
-        if os.path.exists(args.traffic):
-            try:
-                tr = json.load(open(args.traffic))
-                if tr.get("workload") == wl.name and dom in tr.get("kernels", {}):
-                    traffic = tr["kernels"][dom]
-            except Exception:
-                traffic = None
+        traffic = measured_traffic(args.traffic, wl.name, dom)
         result["roofline"] = {"kernel": dom, "bound": "mfma" if work[dom][0] == "ops" else "hbm",
                               "achieved": dk.get("achieved"), "peak": dk.get("peak"),
                               "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": traffic}
     result["kernels"] = kernels
+    if not args.no_extras and args.variant == "w8a8" and args.workload == "block_l16384":
+        del ws, out
+        torch.cuda.empty_cache()
+        result["extras"] = extras(S, h3k, torch)
     if not args.no_cpu_baseline and args.variant == "w8a8":
         result["cpu_baseline"] = cpu_baseline(wl, x, c, bw, args.cpu_rows)
     print(json.dumps(result))
+
+
+def measured_traffic(path, workload, kernel):
+    """HBM bytes per launch of `kernel` from the counter summary (FETCH_SIZE + WRITE_SIZE,
+    each scaled by its copy-calibration factor), or None when there is no summary for this
+    workload or the kernel's source changed since the counters were taken."""
+    if not os.path.exists(path):
+        return None
+    try:
+        tr = json.load(open(path))
+    except ValueError:
+        return None
+    if tr.get("workload") != workload:
+        return None
+    key = {"attention": "attn_bf16_kernel"}.get(kernel)
+    if key is None:
+        return None
+    import hashlib
+    here = os.path.join(ROOT, "video_diffusion_transformer_03_amd", "csrc")
+    for name, ent in tr.get("kernels", {}).items():
+        if key in name:
+            src = ent["source"]
+            h = hashlib.sha256(open(os.path.join(here, src), "rb").read()).hexdigest()[:16]
+            if tr.get("sources", {}).get(src) != h:
+                return None
+            return round(ent["read_bytes"] + ent["write_bytes"])
+    return None
+
+
+def _time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def extras(S, h3k, torch):
+    """The 50-block stack at L=16384 (ms per denoising step, with and without horizontal
+    token pairing in blocks [10, 40)) and one block at L=65536 (tokens/s)."""
+    out = {}
+    wl = S.WORKLOADS["stack50_l16384"]
+    blocks = []
+    for b in range(wl.n_blocks):
+        wb = S.block_weights_bf16(wl, b, device="cuda")
+        blocks.append(h3k.quantize_block(wb))
+        del wb
+    x = S.activations(wl, device="cuda")
+    c = S.conditioning(wl, device="cuda")
+    dims = h3k.dims_of(wl)
+    res = {}
+    for tr in [(0, 0), wl.tr_range]:
+        ws = h3k.alloc_workspace(h3k.stack_workspace_bytes(dims, wl.L, *tr))
+        y = torch.empty_like(x)
+        t = _time_steps(torch, lambda: h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y), 2, 1)
+        res["token_reduction" if tr[1] > tr[0] else "full"] = round(t * 1e3, 2)
+        del ws, y
+    out["stack50_l16384_ms_per_denoise_step"] = res
+    del blocks
+    torch.cuda.empty_cache()
+    wl = S.WORKLOADS["block_l65536"]
+    bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"))
+    x = S.activations(wl, device="cuda")
+    c = S.conditioning(wl, device="cuda")
+    dims = h3k.dims_of(wl)
+    ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, wl.L, 0))
+    y = torch.empty_like(x)
+    h3k.profile_enable(True)
+    t = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, 0, ws, y), 3, 1)
+    prof = h3k.profile_read()
+    h3k.profile_enable(False)
+    n, tot = prof["attention"]
+    attn_ms = tot / n
+    out["block_l65536"] = {"ms_per_step": round(t * 1e3, 3), "tokens_per_s": round(wl.L / t, 1),
+                           "attention_ms": round(attn_ms, 3),
+                           "attention_bf16_frac": round(4.0 * wl.L * wl.L * wl.d / (attn_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+    return out
 
 
 if __name__ == "__main__":
