@@ -134,6 +134,19 @@ def test_attention_fp32(H, L, Dh):
     assert rel_l2(o, ref) < 1e-5
 
 
+@pytest.mark.parametrize("L,Dh", [(16384, 128), (4104, 64)])
+def test_attention_deterministic(L, Dh):
+    """Two runs are bitwise identical at full size (LDS races and uninitialised reads
+    show up here)."""
+    H = 8
+    q = torch.randn(H, L, Dh, device="cuda").to(torch.bfloat16)
+    k = torch.randn(H, L, Dh, device="cuda").to(torch.bfloat16)
+    vt = torch.randn(H, Dh, L, device="cuda").to(torch.bfloat16)
+    o1 = h3k.attention(q, k, vt)
+    for _ in range(3):
+        assert torch.equal(h3k.attention(q, k, vt), o1)
+
+
 def test_attention_constant_v():
     H, L, Dh = 2, 136, 64
     q = randn((H, L, Dh), 41, 2.0)

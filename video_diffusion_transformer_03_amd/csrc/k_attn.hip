@@ -97,10 +97,16 @@ __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH 
         for (int r = 0; r < 4; ++r)
           if (k0 + (t4 >> 1) * 32 + kperm(t4 & 1, 4 * g + r) >= L) s[t4][qt][r] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
-#pragma unroll
-    for (int t4 = 1; t4 < 4; ++t4)
-      mx = fmaxf(mx, fmaxf(fmaxf(s[t4][qt][0], s[t4][qt][1]), fmaxf(s[t4][qt][2], s[t4][qt][3])));
+    // running max of the lane's 16 scores as a chain of three-input maxima (v_max3_f32;
+    // this file is compiled without NaN quieting, see build.py)
+    float mx = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), s[0][qt][2]);
+    mx = fmaxf(fmaxf(mx, s[0][qt][3]), s[1][qt][0]);
+    mx = fmaxf(fmaxf(mx, s[1][qt][1]), s[1][qt][2]);
+    mx = fmaxf(fmaxf(mx, s[1][qt][3]), s[2][qt][0]);
+    mx = fmaxf(fmaxf(mx, s[2][qt][1]), s[2][qt][2]);
+    mx = fmaxf(fmaxf(mx, s[2][qt][3]), s[3][qt][0]);
+    mx = fmaxf(fmaxf(mx, s[3][qt][1]), s[3][qt][2]);
+    mx = fmaxf(mx, s[3][qt][3]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = mx * sl2;
