@@ -125,7 +125,7 @@ typedef struct {
   size_t total;                 /* bytes needed (= h3k_workspace_bytes)                */
 } h3k_ws_layout;
 
-/* S0. Per-output-channel int8 weight quantisation of w [n_out, k_in] (device; bf16 or
+/* Per-output-channel int8 weight quantisation of w [n_out, k_in] (device; bf16 or
  * fp32 per w_dtype): scale_out[n] = max_k |w[n,k]| / 127, q_out[n,k] =
  * clamp(rint(w[n,k] * (127 / max_k |w[n,k]|)), -127, 127), decisions in fp32.
  * q_out int8 [n_out, k_in], scale_out fp32 [n_out] (device). k_in % 8 == 0. */
@@ -158,7 +158,7 @@ int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
                            int32_t Hg, int32_t Wg, float w_pos_scale, float w_pos_offset,
                            uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
-/* S4. Multi-head softmax attention without mask, bf16 MFMA with fp32 online softmax:
+/* Multi-head softmax attention without mask, bf16 MFMA with fp32 online softmax:
  * o[l, e*Dh + j] = sum_k softmax_k(q[e,l,:] . k[e,k,:] * softmax_scale) v[e,k,j].
  * q, k: bf16 [H, L, Dh]; v: bf16 [H, Dh, L] (transposed, as the QKV projection writes
  * it); o: bf16 [L, H*Dh]. All device. head_dim 64 or 128. With H3K_F_FP32_DEBUG in
@@ -185,19 +185,19 @@ int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
 
 /* ---- single steps of the block (the same kernels the block call launches) ---- */
 
-/* S1. m[i] = sum_j w_ada[i, j] * cond[j], fp32 accumulation. w_ada bf16 [n_out, d_cond],
+/* m[i] = sum_j w_ada[i, j] * cond[j], fp32 accumulation. w_ada bf16 [n_out, d_cond],
  * cond fp32 [d_cond], m fp32 [n_out]; device. d_cond % 8 == 0, d_cond <= 8192. */
 int h3k_adaln_modulation(const uint16_t *w_ada, const float *cond, float *m,
                          int64_t n_out, int32_t d_cond, void *stream);
 
-/* S2/S7. Per row l of x [rows, cols] (x_dtype): h = LN(x_l)(1 + scale) + shift in fp32,
+/* Per row l of x [rows, cols] (x_dtype): h = LN(x_l)(1 + scale) + shift in fp32,
  * then per-row int8 quantisation of h: q_out int8 [rows, cols], s_out fp32 [rows].
  * shift, scale: fp32 [cols]. cols % 256 == 0, cols <= 8192. */
 int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift,
                           const float *scale, int64_t rows, int32_t cols, float eps,
                           int8_t *q_out, float *s_out, void *stream);
 
-/* S5/S9. Per-row int8 quantisation of x [rows, cols] (x_dtype) into q_out, s_out.
+/* Per-row int8 quantisation of x [rows, cols] (x_dtype) into q_out, s_out.
  * cols % 8 == 0, cols <= 32768. */
 int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols,
                      int8_t *q_out, float *s_out, void *stream);
@@ -208,12 +208,12 @@ int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols,
 int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream);
 
-/* S11. Horizontal pairing of x [T*Hg*Wg, d] (x_dtype) into xr and xr_copy
+/* Horizontal pairing of x [T*Hg*Wg, d] (x_dtype) into xr and xr_copy
  * [T*Hg*(Wg/2), d]: xr[t,h,j] = (x[t,h,2j] + x[t,h,2j+1]) / 2 (fp32 add, rounded once). */
 int h3k_token_pair(const void *x, void *xr, void *xr_copy, int x_dtype, int32_t T,
                    int32_t Hg, int32_t Wg, int32_t d, void *stream);
 
-/* S12. x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out[t,h,j] - xr_in[t,h,j]) for s in {0,1},
+/* x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out[t,h,j] - xr_in[t,h,j]) for s in {0,1},
  * in place on x_pre (fp32 arithmetic, rounded once). */
 int h3k_token_unpair(void *x_pre, const void *xr_out, const void *xr_in, int x_dtype,
                      int32_t T, int32_t Hg, int32_t Wg, int32_t d, void *stream);

@@ -25,7 +25,7 @@ def randn(shape, seed, std=1.0, dtype=torch.bfloat16):
     return (torch.randn(*shape, generator=_gen(seed)) * std).to(dtype)
 
 
-# ----------------------------------------------------------------------------- S0 weights
+# ----------------------------------------------------------------------------- weights
 @pytest.mark.parametrize("n,k,dtype", [(384, 5120, torch.bfloat16), (256, 20480, torch.bfloat16),
                                        (97, 1000, torch.float32), (3, 8, torch.bfloat16)])
 def test_quantize_weights(n, k, dtype):
@@ -46,7 +46,7 @@ def test_quantize_golden_ties():
     assert s.cpu().tolist() == [1.0, 1.0]
 
 
-# ----------------------------------------------------------------------------- S1 AdaLN
+# ----------------------------------------------------------------------------- AdaLN
 @pytest.mark.parametrize("n_out,dc", [(6 * 256, 256), (6 * 5120, 5120), (40, 8)])
 def test_adaln_modulation(n_out, dc):
     w = randn((n_out, dc), 3, 0.02)
@@ -57,7 +57,7 @@ def test_adaln_modulation(n_out, dc):
     assert np.max(np.abs(m - mr)) < 1e-5 * max(1.0, np.abs(mr).max())
 
 
-# ----------------------------------------------------------------------------- S2/S7 LN + quant
+# ----------------------------------------------------------------------------- LN + quant
 @pytest.mark.parametrize("rows,cols,dtype", [(300, 256, torch.bfloat16), (257, 5120, torch.bfloat16),
                                              (64, 8192, torch.bfloat16), (100, 5120, torch.float32)])
 def test_ln_modulate_quant(rows, cols, dtype):
@@ -74,7 +74,7 @@ def test_ln_modulate_quant(rows, cols, dtype):
     assert np.allclose(s.cpu().numpy(), sr, rtol=1e-6, atol=0)
 
 
-# ----------------------------------------------------------------------------- S5/S9 row quant
+# ----------------------------------------------------------------------------- row quant
 @pytest.mark.parametrize("rows,cols,dtype", [(129, 5120, torch.bfloat16), (33, 20480, torch.bfloat16),
                                              (50, 1024, torch.float32), (5, 32768, torch.bfloat16)])
 def test_row_quantize(rows, cols, dtype):

@@ -205,7 +205,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   const float *shift1 = m, *scale1 = m + d, *gate1 = m + 2 * d;
   const float *shift2 = m + 3 * d, *scale2 = m + 4 * d, *gate2 = m + 5 * d;
 
-  // S2: LN + modulate (+ quant)
+  // LN + modulate (+ quant)
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
     hipError_t e = bf ? launch_rows(1, x_in, false, shift1, scale1, L, d, dm->ln_eps, nullptr, nullptr,
@@ -214,7 +214,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
                                     at<int8_t>(ws, lay.qa), at<float>(ws, lay.s_a), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant"))) return rc;
   }
-  // S3: QKV + RoPE + head-major scatter
+  // QKV + RoPE + head-major scatter
   GemmArgs ga{};
   ga.M = L;
   ga.bf16_ops = bf;
@@ -238,14 +238,14 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     Launch l(H3K_K_GEMM_QKV, s, flags);
     if ((rc = l.done(launch_gemm(EPI_QKV, a, s), fn, "gemm_qkv"))) return rc;
   }
-  // S4: attention
+  // attention
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
                                     at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !bf, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
-  // S5: quantise O
+  // quantise O
   if (!bf) {
     Launch l(H3K_K_ROWQUANT_O, s, flags);
     if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), true, nullptr, nullptr, L, d, 0.f,
@@ -253,7 +253,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
                      fn, "rowquant_o")))
       return rc;
   }
-  // S6: out-proj + gated residual -> x1 (fp32, workspace)
+  // out-proj + gated residual -> x1 (fp32, workspace)
   float *x1 = at<float>(ws, lay.x1);
   {
     GemmArgs a = ga;
@@ -271,7 +271,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     Launch l(H3K_K_GEMM_O, s, flags);
     if ((rc = l.done(launch_gemm(EPI_RESID, a, s), fn, "gemm_o"))) return rc;
   }
-  // S7: LN + modulate (+ quant) of x1
+  // LN + modulate (+ quant) of x1
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
     hipError_t e = bf ? launch_rows(1, x1, true, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
@@ -280,7 +280,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
                                     at<int8_t>(ws, lay.qa2), at<float>(ws, lay.s_a2), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant_2"))) return rc;
   }
-  // S8: MLP up + GELU
+  // MLP up + GELU
   {
     GemmArgs a = ga;
     a.A = bf ? (const void *)at<uint16_t>(ws, lay.h2) : (const void *)at<int8_t>(ws, lay.qa2);
@@ -294,7 +294,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     Launch l(H3K_K_GEMM_UP, s, flags);
     if ((rc = l.done(launch_gemm(EPI_GELU, a, s), fn, "gemm_up"))) return rc;
   }
-  // S9: quantise g
+  // quantise g
   if (!bf) {
     Launch l(H3K_K_ROWQUANT_G, s, flags);
     if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), true, nullptr, nullptr, L, F, 0.f,
@@ -302,7 +302,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
                      fn, "rowquant_g")))
       return rc;
   }
-  // S10: MLP down + gated residual: x_out = x1 + gate2 * y
+  // MLP down + gated residual: x_out = x1 + gate2 * y
   {
     GemmArgs a = ga;
     a.A = bf ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
