@@ -25,26 +25,6 @@
 
 namespace h3k {
 
-// work-group tile (BN weights rows x BM tokens) and wave grid (WN x WM waves)
-#ifndef H3K_GEMM_BN
-#define H3K_GEMM_BN 256
-#define H3K_GEMM_BM 256
-#define H3K_GEMM_WN 2
-#define H3K_GEMM_WM 4
-#endif
-
-#ifndef H3K_GEMM_PAD
-#define H3K_GEMM_PAD 32  // 160-byte pitch: conflict-free 16-byte fragment reads on gfx950
-#endif
-
-constexpr int KB = 128;                 // bytes of K staged per pipeline step
-constexpr int KBP = KB + H3K_GEMM_PAD;  // LDS row pitch (bytes): the pad spreads rows over banks
-
-template <int BN, int BM>
-constexpr size_t gemm_lds_bytes() {
-  return (size_t)2 * (BN + BM) * KBP;
-}
-
 template <bool OUTF32>
 __device__ __forceinline__ void store4(void *base, int64_t idx, float y0, float y1, float y2,
                                        float y3) {
@@ -97,14 +77,6 @@ __device__ __forceinline__ float2 rope_cs(const float2 *tbl, const RopeGeom &g, 
   return tbl[e];
 }
 
-template <int I, typename T>
-__device__ __forceinline__ T &pick(T &a, T &b, T &c, T &d) {
-  if constexpr (I == 0) return a;
-  else if constexpr (I == 1) return b;
-  else if constexpr (I == 2) return c;
-  else return d;
-}
-
 template <bool BF16>
 __device__ __forceinline__ auto mma(v4i b, v4i a, typename std::conditional<BF16, v4f, v4i>::type c) {
   if constexpr (BF16)
@@ -114,27 +86,11 @@ __device__ __forceinline__ auto mma(v4i b, v4i a, typename std::conditional<BF16
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, c, 0, 0, 0);
 }
 
-template <int BN, int BM, int WN, int WM, bool BF16, int EPI, bool OUTF32, bool RESF32>
-__global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
-  constexpr int NT = WN * WM * 64;
-  constexpr int TN = BN / WN / 16;  // 16-row MFMA tiles per wave along N
-  constexpr int TM = BM / WM / 16;  // 16-col MFMA tiles per wave along M
-  constexpr int CPR = KB / 16;      // 16-byte chunks per staged row
-  constexpr int CH_B = BN * CPR / NT;
-  constexpr int CH_A = BM * CPR / NT;
-  static_assert(BN * CPR % NT == 0 && BM * CPR % NT == 0, "tile/threads mismatch");
-  using AccT = typename std::conditional<BF16, v4f, v4i>::type;
-
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t *sB = smem;                  // [2][BN][KBP] weights
-  uint8_t *sA = smem + 2 * BN * KBP;   // [2][BM][KBP] activations
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave / WM, wm = wave % WM;
-
-  // ---- tile schedule: the work-groups the hardware places on one XCD (bid % 8) get a
-  // contiguous range of logical tiles, walked in groups of 8 M-tiles so that concurrent
-  // work-groups of an XCD share weight and activation tiles in that XCD's L2.
+// Work-group tile origin. The work-groups the hardware places on one XCD (bid % 8) get a
+// contiguous range of logical tiles, walked in groups of 8 M-tiles so that concurrent
+// work-groups of an XCD share weight and activation tiles in that XCD's L2.
+template <int BN, int BM>
+__device__ __forceinline__ void tile_origin(const GemmArgs &a, int64_t &m0, int &n0) {
   const int n_tiles = a.N / BN;
   const int64_t m_tiles = (a.M + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_tiles * m_tiles;
@@ -145,109 +101,18 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
   const int64_t first_m = group * GM;
   const int64_t gsize = (m_tiles - first_m) < GM ? (m_tiles - first_m) : GM;
   const int64_t in_group = t - group * GM * n_tiles;
-  const int64_t tm_idx = first_m + in_group % gsize;
-  const int tn_idx = (int)(in_group / gsize);
-  const int64_t m0 = tm_idx * BM;
-  const int n0 = tn_idx * BN;
+  m0 = (first_m + in_group % gsize) * BM;
+  n0 = (int)(in_group / gsize) * BN;
+}
 
-  const int64_t Kb = (int64_t)a.K * (BF16 ? 2 : 1);
-  const uint8_t *gA = (const uint8_t *)a.A;
-  const uint8_t *gB = (const uint8_t *)a.B;
-  const int nk = (int)(Kb / KB);
-
-  // staging registers (named scalars, not arrays: they stay in VGPRs across iterations)
-  static_assert(CH_B <= 4 && CH_A <= 4, "at most 4 staged chunks per thread and operand");
-  uint4 rb0, rb1, rb2, rb3, ra0, ra1, ra2, ra3;
-#define H3K_GLOAD(kt_)                                                                       \
-  {                                                                                          \
-    const int64_t kof = (int64_t)(kt_) * KB;                                                 \
-    static_for<CH_B>([&](auto I) {                                                           \
-      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
-      pick<I>(rb0, rb1, rb2, rb3) = *(const uint4 *)(gB + (int64_t)(n0 + row) * Kb + kof + col * 16);              \
-    });                                                                                      \
-    static_for<CH_A>([&](auto I) {                                                           \
-      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
-      /* rows past M read row M-1: they only feed output rows that are never stored */       \
-      const int64_t m = (m0 + row) < a.M ? (m0 + row) : (a.M - 1);                           \
-      pick<I>(ra0, ra1, ra2, ra3) = *(const uint4 *)(gA + m * Kb + kof + col * 16);                                \
-    });                                                                                      \
-  }
-#define H3K_LSTORE(buf_)                                                                     \
-  {                                                                                          \
-    static_for<CH_B>([&](auto I) {                                                           \
-      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
-      *(uint4 *)(sB + ((buf_) * BN + row) * KBP + col * 16) = pick<I>(rb0, rb1, rb2, rb3);                         \
-    });                                                                                      \
-    static_for<CH_A>([&](auto I) {                                                           \
-      const int c = tid + I * NT, row = c / CPR, col = c % CPR;                              \
-      *(uint4 *)(sA + ((buf_) * BM + row) * KBP + col * 16) = pick<I>(ra0, ra1, ra2, ra3);                         \
-    });                                                                                      \
-  }
-
-  AccT acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = AccT{0, 0, 0, 0};
-
-  const int frow = lane & 15, fk = (lane >> 4) * 16;
-  // one pipeline step: MFMAs over the KB bytes of K staged in LDS buffer cur_
-#define H3K_COMPUTE(cur_)                                                                     \
-  {                                                                                          \
-    const uint8_t *bB = sB + ((cur_) * BN + wn * TN * 16 + frow) * KBP + fk;                 \
-    const uint8_t *bA = sA + ((cur_) * BM + wm * TM * 16 + frow) * KBP + fk;                 \
-    _Pragma("unroll") for (int ks = 0; ks < KB / 64; ++ks) {                                 \
-      v4i fb[TN], fa[TM];                                                                    \
-      _Pragma("unroll") for (int i = 0; i < TN; ++i) fb[i] =                                 \
-          *(const v4i *)(bB + i * 16 * KBP + ks * 64);                                       \
-      _Pragma("unroll") for (int j = 0; j < TM; ++j) fa[j] =                                 \
-          *(const v4i *)(bA + j * 16 * KBP + ks * 64);                                       \
-      _Pragma("unroll") for (int i = 0; i < TN; ++i)                                         \
-      _Pragma("unroll") for (int j = 0; j < TM; ++j) acc[i][j] = mma<BF16>(fb[i], fa[j], acc[i][j]); \
-    }                                                                                        \
-  }
-  // Software pipeline, prefetch distance 2. Iteration kt: store the registers holding
-  // tile kt+1 (loaded one iteration earlier) into LDS buffer (kt+1)&1, issue the global
-  // loads of tile kt+2, then run the MFMAs of tile kt from buffer kt&1. The barrier that
-  // ends iteration kt-1 separates both the reads of buffer (kt+1)&1 in iteration kt-1
-  // from its rewrite here, and the rewrite of buffer kt&1 from the reads below.
-  H3K_GLOAD(0);
-  H3K_LSTORE(0);
-  H3K_GLOAD(nk > 1 ? 1 : 0);  // (re-reads tile 0 when there is no tile 1; unused then)
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 < nk; ++kt) {
-    H3K_LSTORE((kt + 1) & 1);
-    H3K_GLOAD(kt + 2);
-    H3K_COMPUTE(kt & 1);
-#ifdef H3K_GEMM_SGB2
-    // issue order for the scheduler: LDS stores, global loads, then the second K step's
-    // fragment reads spread over the first K step's MFMAs
-    static_assert(KB == 128, "schedule written for two 64-byte K steps");
-    __builtin_amdgcn_sched_group_barrier(0x200, CH_A + CH_B, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, CH_A + CH_B, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, TN + TM, 0);
-    static_for<TN + TM>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(0x008, TN * TM * 2 - 2 * (TN + TM), 0);
-#endif
-    __syncthreads();
-  }
-  if (kt + 1 < nk) {
-    H3K_LSTORE((kt + 1) & 1);
-    H3K_COMPUTE(kt & 1);
-    __syncthreads();
-    ++kt;
-  }
-  H3K_COMPUTE(kt & 1);
-
-  // ---- epilogue. acc[i][j][r] = C[m][n] with m = token (lane & 15 within tile j),
-  // n = channel (4 * (lane >> 4) + r within tile i).
+// Epilogue of one wave's TN x TM block of 16x16 accumulator tiles. acc[i][j][r] = C[m][n]
+// with m = token m_base + 16 j + (lane & 15) and n = channel n_base + 16 i + 4 (lane >> 4) + r.
+template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename AccT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
+                                              int n_base, int64_t m_base, int lane) {
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
-    const int n = n0 + wn * TN * 16 + i * 16 + (lane >> 4) * 4;
+    const int n = n_base + i * 16 + (lane >> 4) * 4;
     float sw[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (!BF16 && EPI != EPI_RAW_I32) {
       float4 t4 = *(const float4 *)(a.sw + n);
@@ -255,7 +120,7 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int64_t m = m0 + wm * TM * 16 + j * 16 + (lane & 15);
+      const int64_t m = m_base + j * 16 + (lane & 15);
       if (m >= a.M) continue;
       if constexpr (EPI == EPI_RAW_I32) {
         if constexpr (!BF16) {
@@ -307,14 +172,146 @@ __global__ __launch_bounds__(WN *WM * 64) void gemm_kernel(const GemmArgs a) {
   }
 }
 
-#undef H3K_GLOAD
-#undef H3K_LSTORE
-#undef H3K_COMPUTE
+// ------------------------------------------------------------------ ping-pong kernel
+// 256 x 256 work-group tile, 8 waves in two groups of four. Waves w and w + 4 run on the
+// same SIMD, so group g = w / 4 puts one wave of each group on every SIMD. The groups are
+// offset by one barrier: while the waves of one group issue the matrix-core work of a K
+// step from registers, the waves of the other group load the next step's fragments from
+// LDS and issue global -> LDS copies, so each SIMD always has one wave feeding its matrix
+// core. Group g owns weight rows [128 g, 128 g + 128) of the tile, wave w % 4 owns tokens
+// [64 (w % 4), 64 (w % 4) + 64): 8 x 4 accumulator tiles of 16 x 16 per wave.
+//
+// A K step is 64 bytes (one MFMA K step); LDS holds two stages of two steps each. A stage
+// is 128 bytes of K for the 256 weight rows then the 256 token rows, stored row-major with
+// 128-byte rows; the 16-byte chunk c of row r sits at position c ^ (r % 8). A global -> LDS
+// copy instruction fills 8 rows (1 KB, lane l writes offset 16 l): lane l fetches row l / 8,
+// chunk (l % 8) ^ (l / 8 % 8), so eight consecutive lanes read one full 128-byte line. The
+// MFMA fragment of lane l (row l % 16, chunk 4 h + l / 16 for the stage's step h) is read
+// from position (4 h + l / 16) ^ (l % 8); the XOR spreads a fragment read over the banks.
+constexpr int PP_SB = 128;                    // bytes of K per stage (two MFMA K steps)
+constexpr int PP_STAGE = (256 + 256) * PP_SB;  // LDS bytes of one stage
 
-template <int BN, int BM, int WN, int WM, bool BF16, int EPI, bool OUTF32, bool RESF32>
-static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
-  auto kern = gemm_kernel<BN, BM, WN, WM, BF16, EPI, OUTF32, RESF32>;
-  constexpr size_t lds = gemm_lds_bytes<BN, BM>();
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int waitcnt_vm_lgkm0(int vm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (0 << 8);
+}
+
+// Work-group barrier without a memory fence. A fenced barrier (__syncthreads) waits for
+// every outstanding global -> LDS copy (vmcnt(0)), which would drain the copy pipeline at
+// each barrier; ordering is instead made explicit with s_waitcnt before the barrier. The
+// asm memory clobber keeps the compiler from moving memory accesses across it and the
+// scheduling barriers keep the matrix-core work inside its phase.
+#define H3K_PP_SYNC()                                   \
+  {                                                     \
+    __builtin_amdgcn_sched_barrier(0);                  \
+    asm volatile("s_barrier" ::: "memory");             \
+    __builtin_amdgcn_sched_barrier(0);                  \
+  }
+
+template <bool BF16, int EPI, bool OUTF32, bool RESF32>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
+  constexpr int TN = 8, TM = 4;
+  using AccT = typename std::conditional<BF16, v4f, v4i>::type;
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, wq = wave & 3;
+
+  int64_t m0;
+  int n0;
+  tile_origin<256, 256>(a, m0, n0);
+  const int64_t Kb = (int64_t)a.K * (BF16 ? 2 : 1);
+  const int ns = (int)(Kb / PP_SB);  // stages
+
+  // global -> LDS copies: wave w copies the 8-row groups w, w + 8, w + 16, w + 24 of the
+  // weight tile and of the token tile in every stage. Token rows past M read row M - 1:
+  // they only feed accumulator rows that are never stored.
+  const int cr = lane >> 3, cc = (lane & 7) ^ cr;
+  const uint8_t *gB = (const uint8_t *)a.B + (int64_t)(n0 + wave * 8 + cr) * Kb + cc * 16;
+  const uint8_t *gA[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t m = m0 + (wave + 8 * q) * 8 + cr;
+    gA[q] = (const uint8_t *)a.A + (m < a.M ? m : a.M - 1) * Kb + cc * 16;
+  }
+  const int64_t gB_q = 64 * Kb;  // 8 row groups further down the weight tile
+#define H3K_PP_COPY(s_)                                                                     \
+  {                                                                                         \
+    const int64_t ko = (int64_t)(s_) * PP_SB;                                               \
+    uint8_t *dst = smem + ((s_) & 1) * PP_STAGE + wave * 1024;                              \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                           \
+      __builtin_amdgcn_global_load_lds(gB + q * gB_q + ko,                                  \
+          (__attribute__((address_space(3))) void *)(dst + q * 8192), 16, 0, 0);            \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                           \
+      __builtin_amdgcn_global_load_lds(gA[q] + ko,                                          \
+          (__attribute__((address_space(3))) void *)(dst + 32768 + q * 8192), 16, 0, 0);    \
+  }
+
+  AccT acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = AccT{0, 0, 0, 0};
+
+  // fragments of one step: weight rows 128 grp + 16 i, token rows 64 wq + 16 j
+  v4i fb[TN], fa[TM];
+  const int frag_off = (lane & 15) * PP_SB + (((lane >> 4) ^ (lane & 7)) * 16);
+#define H3K_PP_READ(s_, h_)                                                                 \
+  {                                                                                         \
+    const uint8_t *src = smem + ((s_) & 1) * PP_STAGE + (frag_off ^ ((h_) * 64));           \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i) fb[i] =                                  \
+        *(const v4i *)(src + (grp * TN + i) * 16 * PP_SB);                                  \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j) fa[j] =                                  \
+        *(const v4i *)(src + 32768 + (wq * TM + j) * 16 * PP_SB);                           \
+  }
+#define H3K_PP_MFMA()                                                                       \
+  {                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < TN; ++i)                                          \
+    _Pragma("unroll") for (int j = 0; j < TM; ++j) acc[i][j] = mma<BF16>(fb[i], fa[j], acc[i][j]); \
+  }
+
+  // Step k = 2 s + h reads stage s (buffer s % 2). Barrier instances are counted after the
+  // prologue's: instance 2k + 1 ends group 0's memory phase of step k and group 1's compute
+  // phase of step k - 1; instance 2k + 2 ends group 0's compute phase of step k and group
+  // 1's memory phase of step k.
+  //  - The copies of stage s + 1 are issued in the memory phase of step 2 s: buffer (s + 1) % 2
+  //    last held stage s - 1, whose last reader (group 1, step 2 s - 1) passed instance 4 s.
+  //  - Each wave waits for its own copies at the end of its memory phase of step 2 s + 1, at
+  //    the latest instance 4 s + 4, before which nobody reads stage s + 1.
+  H3K_PP_COPY(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  H3K_PP_SYNC();
+  if (grp) H3K_PP_SYNC();
+
+  for (int st = 0; st < ns; ++st) {
+    if (st + 1 < ns) H3K_PP_COPY(st + 1);
+    H3K_PP_READ(st, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    H3K_PP_SYNC();
+    H3K_PP_MFMA();
+    H3K_PP_SYNC();
+    H3K_PP_READ(st, 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    H3K_PP_SYNC();
+    H3K_PP_MFMA();
+    // Group 1's last compute phase needs no closing barrier (no LDS access follows), which
+    // leaves both groups with the same barrier count; group 0 closes its last compute phase
+    // at the instance that ends group 1's last memory phase, then runs its epilogue while
+    // group 1 computes.
+    if (st + 1 < ns || grp == 0) H3K_PP_SYNC();
+  }
+
+  gemm_epilogue<TN, TM, BF16, EPI, OUTF32, RESF32>(a, acc, n0 + grp * TN * 16,
+                                                 m0 + wq * TM * 16, lane);
+}
+#undef H3K_PP_COPY
+#undef H3K_PP_READ
+#undef H3K_PP_MFMA
+
+template <bool BF16, int EPI, bool OUTF32, bool RESF32>
+static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
+  auto kern = gemm_pp_kernel<BF16, EPI, OUTF32, RESF32>;
+  constexpr size_t lds = (size_t)2 * PP_STAGE;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)kern,
@@ -322,15 +319,14 @@ static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t m_tiles = (a.M + BM - 1) / BM;
-  const int64_t nwg = m_tiles * (a.N / BN);
-  kern<<<dim3((unsigned)nwg), dim3(WN * WM * 64), lds, s>>>(a);
+  const int64_t nwg = ((a.M + 255) / 256) * (a.N / 256);
+  kern<<<dim3((unsigned)nwg), dim3(512), lds, s>>>(a);
   return hipGetLastError();
 }
 
 template <bool BF16, int EPI, bool OUTF32, bool RESF32>
 static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
-  return run_gemm<H3K_GEMM_BN, H3K_GEMM_BM, H3K_GEMM_WN, H3K_GEMM_WM, BF16, EPI, OUTF32, RESF32>(a, s);
+  return run_gemm_pp<BF16, EPI, OUTF32, RESF32>(a, s);
 }
 
 // instantiated type combinations:
@@ -365,8 +361,7 @@ static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) 
 hipError_t launch_gemm(EpiKind kind, const GemmArgs &a, hipStream_t s) {
   if (kind == EPI_RAW_I32) {
     if (a.bf16_ops || a.out_f32) return hipErrorInvalidValue;
-    return run_gemm<H3K_GEMM_BN, H3K_GEMM_BM, H3K_GEMM_WN, H3K_GEMM_WM, false, EPI_RAW_I32, false,
-                    false>(a, s);
+    return gemm_tiles<false, EPI_RAW_I32, false, false>(a, s);
   }
   return gemm_dispatch(kind, a, s);
 }

@@ -30,7 +30,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # kernel kind -> (source file, substring of the mangled kernel name, extra selector)
 KINDS = {
     "attention": ("k_attn.hip", "attn_bf16_kernel"),
-    "gemm": ("k_gemm.hip", "gemm_kernel"),
+    "gemm": ("k_gemm.hip", "gemm_pp_kernel"),
     "rows": ("k_rows.hip", "row_kernel"),
     "adaln": ("k_rows.hip", "adaln_kernel"),
 }
