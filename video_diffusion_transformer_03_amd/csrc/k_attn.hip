@@ -19,6 +19,19 @@
 
 namespace h3k {
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] + [15:14], expcnt [6:4], lgkmcnt [11:8])
+constexpr int waitcnt_vm_lgkm0(int vm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (0 << 8);
+}
+// Work-group barrier without a memory fence, so global -> LDS copies stay in flight across
+// it (a fenced barrier waits for all of them); callers order memory with s_waitcnt first.
+#define H3K_PP_SYNC()                                   \
+  {                                                     \
+    __builtin_amdgcn_sched_barrier(0);                  \
+    asm volatile("s_barrier" ::: "memory");             \
+    __builtin_amdgcn_sched_barrier(0);                  \
+  }
+
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
 #ifndef H3K_ATTN_OCC
@@ -274,6 +287,419 @@ __global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------- bf16, Dh = 128
+// Software-pipelined kernel: 8 waves x 32 queries per work-group. Iteration j overlaps,
+// inside each wave, the matrix-core products of one tile with the softmax arithmetic of
+// another (a wave's own VALU work issues between its MFMAs; work of a second wave on the
+// same SIMD overlaps far less):
+//   phase 1: S(j+1) = K(j+1) Q^T        with  P(j) = exp2(S(j) - m), row sums
+//   phase 2: O += V(j) P(j)^T           with  row maximum of S(j+1), rescale decision
+// The O / l rescale a new maximum calls for is applied at the start of the next iteration,
+// after phase 2 has added the tile scaled by the old maximum.
+//
+// K and V^T tiles reach LDS through direct global -> LDS copies into four resident
+// stages; stage u holds K tile u and V^T tile u - 1 (what iteration u - 1 reads), and
+// iteration j issues the copies of stage j + 4. LDS layouts (16-byte chunks, XOR swizzles keep fragment reads free of bank
+// conflicts; every copy instruction fills 1 KB and reads whole 128-byte lines):
+//   K   64 rows x 256 B: row R holds key kof(R) of the tile (the kperm order above), chunk
+//       c at position c ^ (R % 16)
+//   V^T 128 rows (head dims) x 128 B (64 keys): chunk c at position c ^ (R % 8)
+namespace v2 {
+constexpr int NW = 8, BQ = NW * 32, BK = 64, DH = 128;
+constexpr int NB = 4, DIST = 4;            // resident stages; iteration j copies stage j + DIST
+constexpr int K_BYTES = BK * DH * 2;       // 16 KB
+constexpr int STAGE = 2 * K_BYTES;         // K then V^T
+constexpr size_t LDS = (size_t)NB * STAGE;
+constexpr int COPIES = 4;                  // copy instructions per wave and stage
+
+__device__ __forceinline__ int kof(int R) {  // key (within the tile) held by K row R
+  const int i = R & 15;
+  return (R & ~31) + 8 * (i >> 2) + 4 * ((R >> 4) & 1) + (i & 3);
+}
+
+// S^T = K Q^T for one K tile: lane holds keys (t4/2)*32 + 8g + 4(t4%2) + r, query c16
+__device__ __forceinline__ void s_tile(v4f (&s)[4][2], const v8bf (&qf)[2][4],
+                                       const uint8_t *kb, int koff) {
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4) s[t4][0] = s[t4][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const v8bf kf = *(const v8bf *)(kb + t4 * 4096 + (koff ^ (kk * 64)));
+      s[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], s[t4][0], 0, 0, 0);
+      s[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], s[t4][1], 0, 0, 0);
+    }
+  }
+}
+
+// P = exp2(S sl2 - m) rounded to bf16 (the P^T operand, keys 8g .. 8g+7 of each 32-key
+// step), l += sum of the rounded P
+__device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
+                                         const float (&m)[2], float (&l)[2], float sl2) {
+  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float mneg = -m[qt];
+    float acc = l[qt];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks][qt][r], sl2, mneg));
+        p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks + 1][qt][r], sl2, mneg));
+      }
+      uint4 u;
+      u.x = pack_bf2(p[0], p[1]);
+      u.y = pack_bf2(p[2], p[3]);
+      u.z = pack_bf2(p[4], p[5]);
+      u.w = pack_bf2(p[6], p[7]);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.x), ones, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.y), ones, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.z), ones, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.w), ones, acc, false);
+      pb[ks][qt] = __builtin_bit_cast(v8bf, u);
+    }
+    l[qt] = acc;
+  }
+}
+
+// O^T += V^T P^T for one V^T tile
+__device__ __forceinline__ void pv_tile(v4f (&o)[8][2], const v8bf (&pb)[2][2],
+                                        const uint8_t *vb, int voff) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const v8bf vf = *(const v8bf *)(vb + dt * 2048 + (voff ^ (ks * 64)));
+      o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ks][0], o[dt][0], 0, 0, 0);
+      o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ks][1], o[dt][1], 0, 0, 0);
+    }
+  }
+}
+
+// Row maxima of a score tile in the exp2 domain (with MASK, keys >= kmax of the tile are
+// set to -inf first); grow = some row exceeds the running maximum m by more than 2^8.
+template <bool MASK>
+__device__ __forceinline__ bool max_vals(v4f (&s)[4][2], const float (&m)[2], float (&mnew)[2],
+                                         float sl2, int g, int kmax) {
+  if (MASK && kmax < BK) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = (t4 >> 1) * 32 + 8 * g + 4 * (t4 & 1) + r;
+        if (key >= kmax) s[t4][0][r] = s[t4][1][r] = -INFINITY;
+      }
+  }
+  bool grow = false;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float mx = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), s[0][qt][2]);
+    mx = fmaxf(fmaxf(mx, s[0][qt][3]), s[1][qt][0]);
+    mx = fmaxf(fmaxf(mx, s[1][qt][1]), s[1][qt][2]);
+    mx = fmaxf(fmaxf(mx, s[1][qt][3]), s[2][qt][0]);
+    mx = fmaxf(fmaxf(mx, s[2][qt][1]), s[2][qt][2]);
+    mx = fmaxf(fmaxf(mx, s[2][qt][3]), s[3][qt][0]);
+    mx = fmaxf(fmaxf(mx, s[3][qt][1]), s[3][qt][2]);
+    mx = fmaxf(mx, s[3][qt][3]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mnew[qt] = mx * sl2;
+    grow |= mnew[qt] > m[qt] + kRescaleLog2;
+  }
+  return grow;
+}
+
+// Lazy rescale decision: the running maximum m moves only when a row's maximum exceeds it
+// by more than 2^8 (P then stays <= 256). Returns whether any row of the wave moved
+// (alpha then holds the factors for O and l).
+__device__ __forceinline__ bool rescale_decision(bool grow, const float (&mnew)[2],
+                                                 float (&m)[2], float (&alpha)[2]) {
+  if (!(__builtin_amdgcn_read_exec() & __ballot(grow))) return false;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float mref = mnew[qt] > m[qt] + kRescaleLog2 ? mnew[qt] : m[qt];
+    alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mref);
+    m[qt] = mref;
+  }
+  return true;
+}
+
+#ifndef H3K_ATTN_PD
+#define H3K_ATTN_PD 3
+#endif
+constexpr int PD = H3K_ATTN_PD;  // LDS fragment reads issued this many MFMA pairs ahead
+
+// Phase 1 of an iteration, interleaved by hand in 16 steps (a scheduling barrier ends each
+// step): step i reads K fragment i + PD, issues the two MFMAs of fragment i (S^T tile t4 =
+// i % 4, head-dim step kk = i / 4, both query tiles) into nxt, and does one sixteenth of the
+// softmax of cur: two exp2, one bf16 pair packed into pb, one dot2 into the row sum.
+__device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4][2],
+                                            v8bf (&pb)[2][2], const v8bf (&qf)[2][4],
+                                            const uint8_t *kb, int koff, const float (&m)[2],
+                                            float (&l)[2], float sl2) {
+  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+  v8bf kf[PD + 1];
+  static_for<PD>([&](auto I) {
+    kf[I] = *(const v8bf *)(kb + (I % 4) * 4096 + (koff ^ ((I / 4) * 64)));
+  });
+  const float mneg[2] = {-m[0], -m[1]};
+  float lacc[2] = {l[0], l[1]};
+  uint32_t u[4];
+  static_for<16>([&](auto I) {
+    constexpr int i = I;
+    if constexpr (i + PD < 16)
+      kf[(i + PD) % (PD + 1)] =
+          *(const v8bf *)(kb + ((i + PD) % 4) * 4096 + (koff ^ (((i + PD) / 4) * 64)));
+    constexpr int t4 = i % 4, kk = i / 4;
+    const v8bf k = kf[i % (PD + 1)];
+    const v4f z = {0.f, 0.f, 0.f, 0.f};
+    nxt[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[0][kk], kk ? nxt[t4][0] : z, 0, 0, 0);
+    nxt[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[1][kk], kk ? nxt[t4][1] : z, 0, 0, 0);
+    // softmax slice: chunk c = i / 4 is (query tile qt, 32-key step ks), part i % 4 a pair
+    constexpr int c = i / 4, part = i % 4, qt = c >> 1, ks = c & 1;
+    constexpr int tt = 2 * ks + (part >> 1), r0 = (part & 1) * 2;
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0], sl2, mneg[qt]));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0 + 1], sl2, mneg[qt]));
+    u[part] = pack_bf2(p0, p1);
+    lacc[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u[part]), ones, lacc[qt], false);
+    if constexpr (part == 3) pb[ks][qt] = __builtin_bit_cast(v8bf, make_uint4(u[0], u[1], u[2], u[3]));
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  l[0] = lacc[0];
+  l[1] = lacc[1];
+}
+
+// Phase 2, same shape: step i reads V^T fragment i + PD, issues the two MFMAs of fragment i
+// (head-dim tile dt = i % 8, key step ks = i / 8) into o, and advances the row maximum of
+// nxt (query tile i / 8, two scores per step; the cross-lane part ends each half).
+__device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2][2],
+                                             const v4f (&nxt)[4][2], const uint8_t *vb, int voff,
+                                             const float (&m)[2], float (&mnew)[2], float sl2) {
+  v8bf vf[PD + 1];
+  static_for<PD>([&](auto I) {
+    vf[I] = *(const v8bf *)(vb + (I % 8) * 2048 + (voff ^ ((I / 8) * 64)));
+  });
+  float mx = 0.f;
+  bool grow = false;
+  static_for<16>([&](auto I) {
+    constexpr int i = I;
+    if constexpr (i + PD < 16)
+      vf[(i + PD) % (PD + 1)] =
+          *(const v8bf *)(vb + ((i + PD) % 8) * 2048 + (voff ^ (((i + PD) / 8) * 64)));
+    constexpr int dt = i % 8, ks = i / 8;
+    const v8bf v = vf[i % (PD + 1)];
+    o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][0], o[dt][0], 0, 0, 0);
+    o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][1], o[dt][1], 0, 0, 0);
+    constexpr int qt = i / 8, st = i % 8;  // scores 2 st, 2 st + 1 of query tile qt
+    const float a0 = nxt[st >> 1][qt][(st & 1) * 2], a1 = nxt[st >> 1][qt][(st & 1) * 2 + 1];
+    if constexpr (st == 0)
+      mx = fmaxf(a0, a1);
+    else
+      mx = fmaxf(fmaxf(mx, a0), a1);
+    if constexpr (st == 7) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mnew[qt] = mx * sl2;
+      grow |= mnew[qt] > m[qt] + kRescaleLog2;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return grow;
+}
+
+// keys >= kmax of a score tile -> -inf (last key tile)
+__device__ __forceinline__ void mask_tile(v4f (&s)[4][2], int g, int kmax) {
+  if (kmax < BK) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = (t4 >> 1) * 32 + 8 * g + 4 * (t4 & 1) + r;
+        if (key >= kmax) s[t4][0][r] = s[t4][1][r] = -INFINITY;
+      }
+  }
+}
+
+__device__ __forceinline__ void rescale(v4f (&o)[8][2], float (&l)[2], const float (&alpha)[2]) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    l[qt] *= alpha[qt];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt][qt] *= alpha[qt];
+  }
+}
+}  // namespace v2
+
+template <bool OF32>
+__global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict__ Q,
+                                                      const uint16_t *__restrict__ K,
+                                                      const uint16_t *__restrict__ Vt,
+                                                      void *__restrict__ Ov, int H, int64_t L,
+                                                      float sl2) {
+  using namespace v2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int head = blockIdx.y;
+  const int64_t q0 = (int64_t)blockIdx.x * BQ + wave * 32;
+  const uint16_t *Qh = Q + (int64_t)head * L * DH;
+  const uint16_t *Kh = K + (int64_t)head * L * DH;
+  const uint16_t *Vh = Vt + (int64_t)head * DH * L;
+  const uint32_t Lu = (uint32_t)L;
+  const int nkt = (int)((L + BK - 1) / BK);
+
+  // Q^T operand: query q0 + qt*16 + c16 (rows past L read row L-1, never stored)
+  v8bf qf[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int64_t qi = (q0 + qt * 16 + c16) < L ? (q0 + qt * 16 + c16) : (L - 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[qt][kk] = __builtin_bit_cast(v8bf, ld16(Qh + qi * DH + kk * 32 + g * 8));
+  }
+
+  // copy lanes: K instructions wave and wave + 8 (rows 4i .. 4i+3), V^T instructions wave
+  // and wave + 8 (rows 8i .. 8i+7). Keys past L read key L-1 (K) or the last valid 8-key
+  // chunk (V^T; L % 8 == 0); their scores are masked, so p = 0 meets finite values.
+  int kkey[2], kcol[2], vrow[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int Rk = 4 * (wave + 8 * q) + (lane >> 4);
+    kkey[q] = kof(Rk);
+    kcol[q] = ((lane & 15) ^ (Rk & 15)) * 8;
+    vrow[q] = 8 * (wave + 8 * q) + (lane >> 3);
+  }
+  const int vcol = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+// Buffer (MUBUF) copies rather than global_load_lds: for the latter the compiler assumes a
+// pending copy may also count against lgkmcnt and waits for every outstanding LDS read at
+// each fragment use, which would undo the read-ahead of the phases below. Byte offsets
+// within a head stay below 256 L < 2^32.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, (int)0xffffffffu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, (int)0xffffffffu, 0x00020000);
+#define H3K_V2_COPY(u_)                                                                        \
+  {                                                                                            \
+    const int u = (u_);                                                                        \
+    uint8_t *dst = smem + (u % NB) * STAGE;                                                    \
+    const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;                               \
+    const uint32_t vt0 = (uint32_t)(u >= 1 ? u - 1 : 0) * BK;                                  \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                            \
+      const uint32_t key = min(kt0 + (uint32_t)kkey[q], Lu - 1u);                              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,                                            \
+          (__attribute__((address_space(3))) void *)(dst + (wave + 8 * q) * 1024), 16,         \
+          (key * DH + kcol[q]) * 2, 0, 0, 0);                                                  \
+    }                                                                                          \
+    const uint32_t col = min(vt0 + (uint32_t)vcol, Lu - 8u);                                   \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                              \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs,                                            \
+          (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * q) * 1024),   \
+          16, ((uint32_t)vrow[q] * Lu + col) * 2, 0, 0, 0);                                    \
+  }
+  // fragment offsets inside a stage: K row t4*16 + c16, chunk 4kk + g; V^T row dt*16 + c16,
+  // chunk 4ks + g (the kk / ks part is applied as an XOR of kk*64 / ks*64)
+  const int koff = c16 * 256 + ((g ^ c16) * 16);
+  const int voff = K_BYTES + c16 * 128 + ((g ^ (c16 & 7)) * 16);
+
+  v4f o[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i][0] = o[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f};
+  v4f sa[4][2], sb[4][2];
+  v8bf pb[2][2];
+
+  // prologue: stages 0 .. DIST-1 in flight (past nkt they repeat valid tiles into buffers
+  // no later copy targets); S(0) from stage 0, its maximum; then stage 1 for iteration 0
+  static_for<DIST>([&](auto J) { H3K_V2_COPY(J); });
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 1)));
+  H3K_PP_SYNC();
+  s_tile(sa, qf, smem, koff);
+  float mnew[2];
+  bool pend = max_vals<true>(sa, m, mnew, sl2, g, (int)min((int64_t)BK, L));
+  pend = rescale_decision(pend, mnew, m, alpha);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));
+  H3K_PP_SYNC();
+
+  // iteration j reads stage j + 1. Its copies of stage j + DIST go to the buffer of stage
+  // j + DIST - NB <= j, last read in iteration j - 1 (or the prologue); the wave's copy of
+  // stage j + 2 is complete at the barrier ending iteration j (DIST - 2 younger stages may
+  // still be in flight).
+#define H3K_V2_ITER(CUR, NXT, j_, MASK)                                                        \
+  {                                                                                            \
+    const int jj = (j_);                                                                       \
+    if (jj + DIST <= nkt) H3K_V2_COPY(jj + DIST);                                              \
+    const uint8_t *sb_ = smem + ((jj + 1) % NB) * STAGE;                                       \
+    if (pend) rescale(o, l, alpha);                                                            \
+    phase_s_exp(NXT, CUR, pb, qf, sb_, koff, m, l, sl2);                                       \
+    if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
+    const bool grow_ = phase_pv_max(o, pb, NXT, sb_, voff, m, mnew, sl2);                      \
+    pend = rescale_decision(grow_, mnew, m, alpha);                                            \
+    if (jj + DIST <= nkt)                                                                      \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
+    else                                                                                       \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                         \
+    H3K_PP_SYNC();                                                                             \
+  }
+#define H3K_V2_LAST(CUR)                                                                       \
+  {                                                                                            \
+    const uint8_t *sb_ = smem + (nkt % NB) * STAGE;                                            \
+    if (pend) rescale(o, l, alpha);                                                            \
+    exp_tile(CUR, pb, m, l, sl2);                                                              \
+    pv_tile(o, pb, sb_, voff);                                                                 \
+  }
+  // nkt - 1 iterations in pairs (the score tiles swap roles); only the last iteration, whose
+  // S tile is the last key tile, can need the key mask. An odd count runs one iteration
+  // first (masked variant; the mask is a no-op unless it is also the last) and moves its S
+  // tile back into sa, so every path ends with the current tile in sa.
+  const int nit = nkt - 1;
+  int j = 0;
+  if (nit & 1) {
+    H3K_V2_ITER(sa, sb, 0, true);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) sa[t4][0] = sb[t4][0], sa[t4][1] = sb[t4][1];
+    j = 1;
+  }
+  for (; j + 2 < nit; j += 2) {
+    H3K_V2_ITER(sa, sb, j, false);
+    H3K_V2_ITER(sb, sa, j + 1, false);
+  }
+  if (j < nit) {
+    H3K_V2_ITER(sa, sb, j, false);
+    H3K_V2_ITER(sb, sa, j + 1, true);
+  }
+  H3K_V2_LAST(sa);
+#undef H3K_V2_ITER
+#undef H3K_V2_LAST
+#undef H3K_V2_COPY
+
+  const int64_t ldo = (int64_t)H * DH;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float lt = l[qt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = 1.0f / lt;
+    const int64_t qi = q0 + qt * 16 + c16;
+    if (qi < L) {
+      const int64_t obase = qi * ldo + (int64_t)head * DH + g * 4;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4f v = o[dt][qt];
+        if constexpr (OF32) {
+          *(float4 *)((float *)Ov + obase + dt * 16) =
+              make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        } else {
+          *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
+              make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- fp32
 // Debug path: fp32 everywhere, plain FMA arithmetic. 64 queries per work-group, four
 // threads per query, each owning DH/4 head dims; 32-key tiles of K and V^T in LDS.
@@ -344,9 +770,32 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
   }
 }
 
+template <bool OF32>
+static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o, int H,
+                          int64_t L, float sl2, hipStream_t s) {
+  auto kern = attn_v2_kernel<OF32>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)v2::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid((unsigned)((L + v2::BQ - 1) / v2::BQ), (unsigned)H);
+  kern<<<grid, 512, v2::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
+                                  (const uint16_t *)vt, o, H, L, sl2);
+  return hipGetLastError();
+}
+
+#ifndef H3K_ATTN_V2
+#define H3K_ATTN_V2 1
+#endif
+
 template <int DH, bool OF32>
 static hipError_t attn_mfma(const void *q, const void *k, const void *vt, void *o, int H,
                             int64_t L, float sl2, hipStream_t s) {
+  if constexpr (DH == 128 && H3K_ATTN_V2)
+    if (L < (1 << 24)) return attn_v2<OF32>(q, k, vt, o, H, L, sl2, s);
   using C = AttnCfg<DH>;
   auto kern = attn_bf16_kernel<DH, OF32>;
   static bool attr_set = false;
