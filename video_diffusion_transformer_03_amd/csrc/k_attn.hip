@@ -34,6 +34,22 @@ constexpr int waitcnt_vm_lgkm0(int vm) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
+// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of the wave) with
+// gfx950 row swaps in registers; a shuffle (__shfl_xor) would go through LDS
+// (ds_bpermute) and wait for every outstanding LDS read.
+__device__ __forceinline__ float rows_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 #ifndef H3K_ATTN_OCC
 #define H3K_ATTN_OCC 2  // waves per SIMD the register budget is sized for
 #endif
@@ -120,8 +136,7 @@ __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH 
     mx = fmaxf(fmaxf(mx, s[2][qt][3]), s[3][qt][0]);
     mx = fmaxf(fmaxf(mx, s[3][qt][1]), s[3][qt][2]);
     mx = fmaxf(mx, s[3][qt][3]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);
     const float mnew = mx * sl2;
     const bool grow = mnew > st.m[qt] + kRescaleLog2;
     if (__builtin_amdgcn_read_exec() & __ballot(grow)) {
@@ -266,8 +281,7 @@ __global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     float l = st.l[qt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l = rows_sum(l);
     const float inv = 1.0f / l;
     const int64_t qi = q0 + qt * 16 + c16;
     if (qi < L) {
@@ -404,8 +418,7 @@ __device__ __forceinline__ bool max_vals(v4f (&s)[4][2], const float (&m)[2], fl
     mx = fmaxf(fmaxf(mx, s[2][qt][3]), s[3][qt][0]);
     mx = fmaxf(fmaxf(mx, s[3][qt][1]), s[3][qt][2]);
     mx = fmaxf(mx, s[3][qt][3]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);
     mnew[qt] = mx * sl2;
     grow |= mnew[qt] > m[qt] + kRescaleLog2;
   }
@@ -427,6 +440,9 @@ __device__ __forceinline__ bool rescale_decision(bool grow, const float (&mnew)[
   return true;
 }
 
+#ifndef H3K_ATTN_DMA
+#define H3K_ATTN_DMA 1  // K/V tiles by global -> LDS copies (1) or through registers (0)
+#endif
 #ifndef H3K_ATTN_PD
 #define H3K_ATTN_PD 3
 #endif
@@ -500,8 +516,7 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2]
     else
       mx = fmaxf(fmaxf(mx, a0), a1);
     if constexpr (st == 7) {
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = rows_max(mx);
       mnew[qt] = mx * sl2;
       grow |= mnew[qt] > m[qt] + kRescaleLog2;
     }
@@ -599,6 +614,28 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
           (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * q) * 1024),   \
           16, ((uint32_t)vrow[q] * Lu + col) * 2, 0, 0, 0);                                    \
   }
+  // register-staged alternative: global loads into four 16-byte registers, then ds_write
+  // to the same LDS positions the copies fill
+  uint4 rk0, rk1, rv0, rv1;
+#define H3K_V2_GLOAD(u_)                                                                       \
+  {                                                                                            \
+    const int u = (u_);                                                                        \
+    const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;                               \
+    const uint32_t vt0 = (uint32_t)(u >= 1 ? u - 1 : 0) * BK;                                  \
+    rk0 = ld16(Kh + min(kt0 + (uint32_t)kkey[0], Lu - 1u) * DH + kcol[0]);                     \
+    rk1 = ld16(Kh + min(kt0 + (uint32_t)kkey[1], Lu - 1u) * DH + kcol[1]);                     \
+    const uint32_t col = min(vt0 + (uint32_t)vcol, Lu - 8u);                                   \
+    rv0 = ld16(Vh + (uint32_t)vrow[0] * Lu + col);                                             \
+    rv1 = ld16(Vh + (uint32_t)vrow[1] * Lu + col);                                             \
+  }
+#define H3K_V2_LSTORE(u_)                                                                      \
+  {                                                                                            \
+    uint8_t *dst = smem + ((u_) % NB) * STAGE + wave * 1024 + lane * 16;                       \
+    *(uint4 *)dst = rk0;                                                                       \
+    *(uint4 *)(dst + 8 * 1024) = rk1;                                                          \
+    *(uint4 *)(dst + K_BYTES) = rv0;                                                           \
+    *(uint4 *)(dst + K_BYTES + 8 * 1024) = rv1;                                                \
+  }
   // fragment offsets inside a stage: K row t4*16 + c16, chunk 4kk + g; V^T row dt*16 + c16,
   // chunk 4ks + g (the kk / ks part is applied as an XOR of kk*64 / ks*64)
   const int koff = c16 * 256 + ((g ^ c16) * 16);
@@ -613,15 +650,27 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 
   // prologue: stages 0 .. DIST-1 in flight (past nkt they repeat valid tiles into buffers
   // no later copy targets); S(0) from stage 0, its maximum; then stage 1 for iteration 0
+#if H3K_ATTN_DMA
   static_for<DIST>([&](auto J) { H3K_V2_COPY(J); });
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 1)));
+#else
+  // register staging: stages 0 and 1 in LDS, stage 2 in registers
+  H3K_V2_GLOAD(0);
+  H3K_V2_LSTORE(0);
+  H3K_V2_GLOAD(1);
+  H3K_V2_LSTORE(1);
+  H3K_V2_GLOAD(2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+#endif
   H3K_PP_SYNC();
   s_tile(sa, qf, smem, koff);
   float mnew[2];
   bool pend = max_vals<true>(sa, m, mnew, sl2, g, (int)min((int64_t)BK, L));
   pend = rescale_decision(pend, mnew, m, alpha);
+#if H3K_ATTN_DMA
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));
   H3K_PP_SYNC();
+#endif
 
   // iteration j reads stage j + 1. Its copies of stage j + DIST go to the buffer of stage
   // j + DIST - NB <= j, last read in iteration j - 1 (or the prologue); the wave's copy of
@@ -630,14 +679,18 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #define H3K_V2_ITER(CUR, NXT, j_, MASK)                                                        \
   {                                                                                            \
     const int jj = (j_);                                                                       \
-    if (jj + DIST <= nkt) H3K_V2_COPY(jj + DIST);                                              \
+    if (H3K_ATTN_DMA && jj + DIST <= nkt) H3K_V2_COPY(jj + DIST);                              \
+    if (!H3K_ATTN_DMA && jj + 2 <= nkt) H3K_V2_LSTORE(jj + 2);                                 \
+    if (!H3K_ATTN_DMA && jj + 3 <= nkt) H3K_V2_GLOAD(jj + 3);                                  \
     const uint8_t *sb_ = smem + ((jj + 1) % NB) * STAGE;                                       \
     if (pend) rescale(o, l, alpha);                                                            \
     phase_s_exp(NXT, CUR, pb, qf, sb_, koff, m, l, sl2);                                       \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
     const bool grow_ = phase_pv_max(o, pb, NXT, sb_, voff, m, mnew, sl2);                      \
     pend = rescale_decision(grow_, mnew, m, alpha);                                            \
-    if (jj + DIST <= nkt)                                                                      \
+    if (!H3K_ATTN_DMA)                                                                         \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));                                        \
+    else if (jj + DIST <= nkt)                                                                 \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
     else                                                                                       \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                         \
@@ -674,13 +727,14 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #undef H3K_V2_ITER
 #undef H3K_V2_LAST
 #undef H3K_V2_COPY
+#undef H3K_V2_GLOAD
+#undef H3K_V2_LSTORE
 
   const int64_t ldo = (int64_t)H * DH;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     float lt = l[qt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    lt = rows_sum(lt);
     const float inv = 1.0f / lt;
     const int64_t qi = q0 + qt * 16 + c16;
     if (qi < L) {
