@@ -222,7 +222,7 @@ def measured_traffic(path, workload, kernel):
         return None
     if tr.get("workload") != workload:
         return None
-    key = {"attention": "attn_bf16_kernel"}.get(kernel)
+    key = {"attention": "attn_v2_kernel"}.get(kernel)
     if key is None:
         return None
     import hashlib

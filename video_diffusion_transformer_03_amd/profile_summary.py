@@ -13,6 +13,12 @@ Reads the CSV files rocprofv3 writes (`--output-format csv`):
 Writes `profiles/kernels_<workload>.txt` (durations, HBM bytes per launch) and
 `profiles/traffic.json` (per-kernel HBM bytes per launch, with a hash of the kernel sources
 so a later change to a kernel marks its numbers stale).
+
+With --sq DIR (a `--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY
+SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE` run of the same command)
+it also writes `profiles/sq_<workload>.txt`: per kernel the fraction of SIMD cycles the matrix
+cores were busy, the fraction of wave time spent waiting, LDS bank-conflict cycles per LDS
+instruction and LDS-active cycles per CU cycle.
 """
 from __future__ import annotations
 
@@ -29,7 +35,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # kernel kind -> (source file, substring of the mangled kernel name, extra selector)
 KINDS = {
-    "attention": ("k_attn.hip", "attn_bf16_kernel"),
+    "attention": ("k_attn.hip", "attn_v2_kernel"),
     "gemm": ("k_gemm.hip", "gemm_pp_kernel"),
     "rows": ("k_rows.hip", "row_kernel"),
     "adaln": ("k_rows.hip", "adaln_kernel"),
@@ -56,10 +62,22 @@ def _one(pattern: str) -> str:
     return hits[0]
 
 
-def kernel_stats(d: str):
+def kernel_stats(d: str, steps: int, warmup: int):
+    """{kernel: (calls, mean ns over the timed dispatches, total ns)} from the per-dispatch
+    trace. The profiled command runs `warmup` untimed steps first; a kernel launched n times
+    in all is averaged over its last n * steps / (steps + warmup) dispatches, the ones of the
+    timed steps (kernels launched once outside the steps are averaged over all)."""
+    per = defaultdict(list)
+    for r in csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))):
+        per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]),
+                                      int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     out = {}
-    for r in csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))):
-        out[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]), float(r["TotalDurationNs"]))
+    for name, v in per.items():
+        v.sort()
+        n = len(v)
+        timed = n * steps // (steps + warmup) if n % (steps + warmup) == 0 else n
+        durs = [t for _, t in v[n - timed:]]
+        out[name] = (n, sum(durs) / len(durs), float(sum(t for _, t in v)))
     return out
 
 
@@ -89,11 +107,14 @@ def main():
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--workload", required=True)
     ap.add_argument("--steps", type=int, required=True, help="timed steps of the profiled run")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed steps before them")
     ap.add_argument("--cmd", required=True, help="the command lines that produced the inputs")
     ap.add_argument("--out", default="profiles")
+    ap.add_argument("--sq", default=None, help="directory of the SQ counter run (optional)")
+    ap.add_argument("--sq-cmd", default="", help="the command line of the SQ counter run")
     a = ap.parse_args()
 
-    stats = kernel_stats(a.ktrace)
+    stats = kernel_stats(a.ktrace, a.steps, a.warmup)
     fetch = counter_by_kernel(a.fetch, "FETCH_SIZE")
     write = counter_by_kernel(a.write, "WRITE_SIZE")
     ff = copy_factor(a.copy_fetch, "FETCH_SIZE", a.copy_bytes)
@@ -102,6 +123,7 @@ def main():
     lines = [f"# Kernel durations and HBM traffic per launch, workload {a.workload}", "",
              "Commands:", *[f"    {c}" for c in a.cmd.split(" ;; ")], "",
              f"Copy calibration (plain 1 GiB device copy): FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {fw:.3f}", "",
+             f"Durations: mean over the dispatches of the {a.steps} timed steps ({a.warmup} warm-up steps excluded).", "",
              f"{'kernel':58s} {'calls':>6s} {'avg us':>10s} {'read MB':>9s} {'write MB':>9s}"]
     traffic = {"workload": a.workload, "copy_factor": {"fetch": ff, "write": fw},
                "sources": {f: source_hash(f) for f, _ in KINDS.values()}, "kernels": {}}
@@ -124,6 +146,37 @@ def main():
     os.makedirs(a.out, exist_ok=True)
     open(os.path.join(a.out, f"kernels_{a.workload}.txt"), "w").write("\n".join(lines) + "\n")
     json.dump(traffic, open(os.path.join(a.out, "traffic.json"), "w"), indent=1)
+    print("\n".join(lines))
+    if a.sq:
+        sq_summary(a)
+
+
+def sq_summary(a):
+    """MFMA-busy and LDS figures per kernel from one SQ counter run (means over dispatches).
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so cycles per XCD = value / 8; the machine
+    has 256 CUs, 1024 SIMDs; SQ_WAVE_CYCLES and SQ_WAIT_ANY count quad-cycles."""
+    acc = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(_one(os.path.join(a.sq, "**", "*counter_collection.csv")))):
+        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# Matrix-core and LDS activity per launch, workload {a.workload}", "",
+             "Command:", f"    {a.sq_cmd}", "",
+             f"{'kernel':58s} {'MFMA busy':>10s} {'wait/wave':>10s} {'LDS confl/inst':>15s} {'LDS active':>11s}"]
+    rows = []
+    for name, cs in acc.items():
+        if "h3k::" not in name:
+            continue
+        d = {c: sum(v) / len(v) for c, v in cs.items()}
+        cyc = d.get("GRBM_GUI_ACTIVE", 0) / 8
+        if cyc <= 0:
+            continue
+        mfma = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (cyc * 1024)
+        wait = d.get("SQ_WAIT_ANY", 0) / max(d.get("SQ_WAVE_CYCLES", 1), 1)
+        confl = d.get("SQ_LDS_BANK_CONFLICT", 0) / max(d.get("SQ_INSTS_LDS", 1), 1)
+        ldsa = d.get("SQ_LDS_IDX_ACTIVE", 0) / (cyc * 256)
+        rows.append((cyc, name, mfma, wait, confl, ldsa))
+    for cyc, name, mfma, wait, confl, ldsa in sorted(rows, reverse=True):
+        lines.append(f"{short_name(name)[:58]:58s} {mfma:10.3f} {wait:10.3f} {confl:15.3f} {ldsa:11.3f}")
+    open(os.path.join(a.out, f"sq_{a.workload}.txt"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
