@@ -249,8 +249,15 @@ def _time_steps(torch, fn, steps, warmup):
 
 
 def extras(S, h3k, torch):
-    """The 50-block stack at L=16384 (ms per denoising step, with and without horizontal
-    token pairing in blocks [10, 40)) and one block at L=65536 (tokens/s)."""
+    """Measurements beside the headline line:
+      - the 50-block stack at L=16384: ms per denoising step without and with horizontal
+        token pairing in blocks [10, 40), and a sweep of pairing ranges with the relative
+        L2 distance of the stack output from the unpaired stack's;
+      - the precision series at L=16384 (BF16 GEMMs, int8 MLP, int8 MLP + QKV, W8A8);
+      - block time against sequence length (L = 4096 .. 65536) with a least-squares fit
+        t = a L + b L^2, and one block at L=65536 with its attention fraction."""
+    import dataclasses
+
     out = {}
     wl = S.WORKLOADS["stack50_l16384"]
     blocks = []
@@ -261,32 +268,85 @@ def extras(S, h3k, torch):
     x = S.activations(wl, device="cuda")
     c = S.conditioning(wl, device="cuda")
     dims = h3k.dims_of(wl)
-    res = {}
-    for tr in [(0, 0), wl.tr_range]:
+    res, sweep, ref = {}, {}, None
+    for tr in [(0, 0), wl.tr_range, (5, 45), (15, 35), (20, 30), (0, 50)]:
         ws = h3k.alloc_workspace(h3k.stack_workspace_bytes(dims, wl.L, *tr))
         y = torch.empty_like(x)
         t = _time_steps(torch, lambda: h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y), 2, 1)
-        res["token_reduction" if tr[1] > tr[0] else "full"] = round(t * 1e3, 2)
+        if tr == (0, 0):
+            ref = y.float().clone()
+            res["full"] = round(t * 1e3, 2)
+        else:
+            yf = y.float()
+            dist = float((yf - ref).norm() / ref.norm())
+            if tr == tuple(wl.tr_range):
+                res["token_reduction"] = round(t * 1e3, 2)
+            sweep[f"[{tr[0]},{tr[1]})"] = {"ms": round(t * 1e3, 2), "rel_l2_vs_full": round(dist, 5)}
         del ws, y
     out["stack50_l16384_ms_per_denoise_step"] = res
-    del blocks
+    out["stack50_token_reduction_sweep"] = sweep
+    del blocks, ref
     torch.cuda.empty_cache()
-    wl = S.WORKLOADS["block_l65536"]
-    bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"))
+
+    # precision series (one block, L=16384)
+    wl = S.WORKLOADS["block_l16384"]
+    bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"), keep_bf16=True)
     x = S.activations(wl, device="cuda")
     c = S.conditioning(wl, device="cuda")
     dims = h3k.dims_of(wl)
-    ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, wl.L, 0))
-    y = torch.empty_like(x)
-    h3k.profile_enable(True)
-    t = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, 0, ws, y), 3, 1)
-    prof = h3k.profile_read()
-    h3k.profile_enable(False)
-    n, tot = prof["attention"]
-    attn_ms = tot / n
-    out["block_l65536"] = {"ms_per_step": round(t * 1e3, 3), "tokens_per_s": round(wl.L / t, 1),
-                           "attention_ms": round(attn_ms, 3),
-                           "attention_bf16_frac": round(4.0 * wl.L * wl.L * wl.d / (attn_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+    series = {}
+    for name, flags in [("bf16", h3k.F_BF16_GEMM), ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT),
+                        ("int8_mlp_qkv", h3k.F_BF16_OUT), ("w8a8", 0)]:
+        ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, wl.L, flags))
+        y = torch.empty_like(x)
+        t = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, y), 5, 2)
+        series[name] = round(t * 1e3, 3)
+        del ws, y
+    out["precision_series_l16384_ms"] = series
+    del bw
+    torch.cuda.empty_cache()
+
+    # sequence-length scaling (one W8A8 block)
+    base = S.WORKLOADS["block_l16384"]
+    grids = {4096: (4, 32, 32), 8192: (4, 32, 64), 16384: (4, 64, 64), 32768: (8, 64, 64),
+             65536: (16, 64, 64)}
+    scaling, l65536 = {}, None
+    for L, grid in grids.items():
+        wl = dataclasses.replace(base, name=f"block_l{L}", grid=grid)
+        bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"))
+        x = S.activations(wl, device="cuda")
+        c = S.conditioning(wl, device="cuda")
+        dims = h3k.dims_of(wl)
+        ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, L, 0))
+        y = torch.empty_like(x)
+        h3k.profile_enable(True)
+        t = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, 0, ws, y), 3, 1)
+        prof = h3k.profile_read()
+        h3k.profile_enable(False)
+        n, tot = prof["attention"]
+        attn_ms = tot / n
+        frac = 4.0 * L * L * wl.d / (attn_ms * 1e-3) / 1e12 / PEAK["bf16"]
+        scaling[str(L)] = {"ms": round(t * 1e3, 3), "attention_ms": round(attn_ms, 3),
+                           "attention_bf16_frac": round(frac, 4)}
+        if L == 65536:
+            l65536 = {"ms_per_step": round(t * 1e3, 3), "tokens_per_s": round(L / t, 1),
+                      "attention_ms": round(attn_ms, 3), "attention_bf16_frac": round(frac, 4)}
+        del bw, x, ws, y
+        torch.cuda.empty_cache()
+    Ls = [float(k) for k in scaling]
+    ts = [scaling[k]["ms"] for k in scaling]
+    # least squares for t = a L + b L^2 (normal equations of the two-column design)
+    s11 = sum(v * v for v in Ls)
+    s12 = sum(v ** 3 for v in Ls)
+    s22 = sum(v ** 4 for v in Ls)
+    r1 = sum(v * t for v, t in zip(Ls, ts))
+    r2 = sum(v * v * t for v, t in zip(Ls, ts))
+    det = s11 * s22 - s12 * s12
+    a = (r1 * s22 - r2 * s12) / det
+    b = (s11 * r2 - s12 * r1) / det
+    out["sequence_scaling_ms"] = {"points": scaling, "fit": {"a_ms_per_token": a, "b_ms_per_token2": b,
+                                  "quadratic_share_at_16384": round(b * 16384 ** 2 / (a * 16384 + b * 16384 ** 2), 4)}}
+    out["block_l65536"] = l65536
     return out
 
 

@@ -71,8 +71,15 @@ enum {
                             bf16 weights wb_* (the pages' BF16 baseline)              */
   H3K_F_FP32_DEBUG = 2u, /* fp32 activations end to end (x_in/x_out fp32), same int8
                             GEMMs, fp32 attention without matrix cores               */
-  H3K_F_SYNC = 4u        /* synchronise the stream and check for errors after every
+  H3K_F_SYNC = 4u,       /* synchronise the stream and check for errors after every
                             launch (debugging)                                        */
+  /* Per-projection precision, for the pages' precision series (BF16 -> int8 MLP -> int8
+   * MLP and QKV; "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
+   * "Int8 양자화"): each flag runs that projection as a bf16 x bf16 GEMM on wb_*, without
+   * its activation quantiser. H3K_F_BF16_GEMM is all three. */
+  H3K_F_BF16_QKV = 8u,   /* QKV projection                                            */
+  H3K_F_BF16_OUT = 16u,  /* attention output projection                               */
+  H3K_F_BF16_MLP = 32u   /* MLP up and down projections                               */
 };
 
 /* element types */
@@ -101,7 +108,8 @@ typedef struct {
   const float *s_up;       /* fp32 [F]      */
   const int8_t *w_down;    /* int8 [d, F]   */
   const float *s_down;     /* fp32 [d]      */
-  const uint16_t *wb_qkv;  /* bf16 originals, read only under H3K_F_BF16_GEMM; else NULL */
+  const uint16_t *wb_qkv;  /* bf16 originals, read only for projections a bf16 flag
+                              selects (may be NULL otherwise)                         */
   const uint16_t *wb_o;
   const uint16_t *wb_up;
   const uint16_t *wb_down;
@@ -118,10 +126,11 @@ typedef struct {
   size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied                */
   size_t vt;                    /* T [H, Dh, L] head-major, transposed                  */
   size_t o;                     /* [L, d] attention output, head e in columns e*Dh ..;
-                                   fp32, or bf16 under H3K_F_BF16_GEMM                  */
+                                   fp32, or bf16 when the output projection is bf16      */
   size_t x1;                    /* fp32 [L, d] residual stream after the attention half */
-  size_t g;                     /* [L, F] GELU output; fp32, or bf16 under H3K_F_BF16_GEMM */
-  size_t h, h2;                 /* bf16 [L, d] modulated activations (H3K_F_BF16_GEMM) */
+  size_t g;                     /* [L, F] GELU output; fp32, or bf16 when the MLP is bf16 */
+  size_t h, h2;                 /* bf16 [L, d] modulated activations feeding a bf16 QKV /
+                                   MLP projection (0 when unused)                       */
   size_t total;                 /* bytes needed (= h3k_workspace_bytes)                */
 } h3k_ws_layout;
 

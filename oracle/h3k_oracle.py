@@ -214,27 +214,52 @@ def quantize_block_weights(wb: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     return out
 
 
-def _linear(h, w, name: str, variant: str) -> np.ndarray:
-    if variant == "w8a8":
+# Projections computed in W8A8 for each variant; the others use the dense weights with no
+# activation quantisation. The two middle variants are the steps of the pages' precision
+# series (page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
+# "Int8 양자화": int8 MLP first, then int8 QKV on top of it).
+INT8_PROJECTIONS = {
+    "w8a8": ("_qkv", "_o", "_up", "_down"),
+    "int8_mlp_qkv": ("_qkv", "_up", "_down"),
+    "int8_mlp": ("_up", "_down"),
+    "bf16gemm": (),
+}
+
+
+def _linear(h, w, name: str, variant: str, dense_inputs: str = "fp64") -> np.ndarray:
+    """One projection. A dense (bf16) projection multiplies by the dense weights; with
+    dense_inputs="bf16" its activation operand is first rounded to bfloat16, since a bf16
+    GEMM takes bf16 operands (BF16 TensorOps projections: page "h3-metal: Apple Silicon을
+    위한 네이티브 MiniMax-H3 추론", section "Metal 4 및 TensorOps")."""
+    if variant not in INT8_PROJECTIONS:
+        raise ValueError(variant)
+    if name in INT8_PROJECTIONS[variant]:
         return w8a8_linear(h, w["q" + name], w["s" + name])
-    if variant == "bf16gemm":
-        return h @ w["w" + name].T
-    raise ValueError(variant)
+    if dense_inputs == "bf16":
+        h = round_bf16(h)
+    elif dense_inputs != "fp64":
+        raise ValueError(dense_inputs)
+    return h @ w["w" + name].T
 
 
 def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
                   variant: str = "w8a8", rows: Optional[Sequence[int]] = None,
                   w_scale: float = 1.0, w_offset: float = 0.0,
                   eps: float = LN_EPS, theta: float = ROPE_THETA,
-                  attn_inputs: str = "fp64", return_parts: bool = False):
+                  attn_inputs: str = "fp64", dense_inputs: str = "fp64",
+                  return_parts: bool = False):
     """One DiT block forward. x [L, d] (fp64 view of the input values), cond [d_cond];
-    w holds w_ada and, per projection, int8 codes q_* with fp32 scales s_* (variant
-    "w8a8") or the dense matrices w_* (variant "bf16gemm": no activation quantisation).
+    w holds w_ada and, per projection, int8 codes q_* with fp32 scales s_* and/or the
+    dense matrices w_*. variant selects the projections computed in W8A8 (see
+    INT8_PROJECTIONS): "w8a8" all, "int8_mlp_qkv" all but the output projection,
+    "int8_mlp" the MLP only, "bf16gemm" none (dense, no activation quantisation).
 
     attn_inputs: "fp64" keeps Q, K, V exact; "bf16" rounds them to bfloat16 (after RoPE)
     before attention, as on the path whose QKV projection hands the attention bf16
     tensors (page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
     "Metal 4 및 TensorOps": BF16 QKV projection routed into head-major attention inputs).
+    dense_inputs: "fp64" multiplies dense projections by the exact activations; "bf16"
+    rounds each dense projection's activation operand to bfloat16 first (see _linear).
 
     rows: token rows whose output is wanted (all if None). Q, K and V are formed for
     every token (attention needs them); everything after attention is per token and is
@@ -244,7 +269,7 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     assert d == n_heads * head_dim and L == grid[0] * grid[1] * grid[2]
     mod = split_modulation(adaln_modulation(w["w_ada"], cond), d)
     h = modulate(layer_norm(x, eps), mod["shift1"], mod["scale1"])
-    y = _linear(h, w, "_qkv", variant)
+    y = _linear(h, w, "_qkv", variant, dense_inputs)
     q = y[:, 0:d].reshape(L, n_heads, head_dim)
     k = y[:, d:2 * d].reshape(L, n_heads, head_dim)
     v = y[:, 2 * d:3 * d].reshape(L, n_heads, head_dim)
@@ -258,10 +283,10 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     sel = np.arange(L) if rows is None else np.asarray(rows)
     o = attention(q, k, v, sel).reshape(len(sel), d)
     xs = x[sel]
-    x1 = xs + mod["gate1"] * _linear(o, w, "_o", variant)
+    x1 = xs + mod["gate1"] * _linear(o, w, "_o", variant, dense_inputs)
     h2 = modulate(layer_norm(x1, eps), mod["shift2"], mod["scale2"])
-    g = gelu(_linear(h2, w, "_up", variant))
-    x2 = x1 + mod["gate2"] * _linear(g, w, "_down", variant)
+    g = gelu(_linear(h2, w, "_up", variant, dense_inputs))
+    x2 = x1 + mod["gate2"] * _linear(g, w, "_down", variant, dense_inputs)
     if return_parts:
         return x2, {"m": np.concatenate([mod[k] for k in mod]), "h": h, "q": q, "k": k,
                     "v": v, "o": o, "x1": x1, "h2": h2, "g": g, "rows": sel}

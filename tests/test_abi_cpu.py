@@ -62,6 +62,34 @@ def test_workspace_monotone_and_layout():
     assert h3k.stack_workspace_bytes(dm, 4096, 1, 3) > h3k.workspace_bytes(dm, 4096, 0)
 
 
+@pytest.mark.parametrize("flags", [h3k.F_BF16_QKV, h3k.F_BF16_OUT, h3k.F_BF16_MLP,
+                                   h3k.F_BF16_QKV | h3k.F_BF16_OUT, h3k.F_BF16_GEMM])
+def test_workspace_mixed_precision(flags):
+    # each projection's buffers follow its own precision: a bf16 projection has no int8
+    # codes, and its input is a bf16 tensor (h, O or h2/g) instead of an fp32 one
+    L, d, F = 512, 256, 1024
+    dm = tiny_dims()
+    lay = h3k.workspace_layout(dm, L, flags)
+    bq = bool(flags & (h3k.F_BF16_QKV | h3k.F_BF16_GEMM))
+    bo = bool(flags & (h3k.F_BF16_OUT | h3k.F_BF16_GEMM))
+    bm = bool(flags & (h3k.F_BF16_MLP | h3k.F_BF16_GEMM))
+    assert (lay["qa"] == 0) == bq and (lay["h"] != 0) == bq
+    assert (lay["qo"] == 0) == bo
+    assert (lay["qa2"] == 0) == bm and (lay["qg"] == 0) == bm and (lay["h2"] != 0) == bm
+    spans = [(lay["q"], 2 * L * d), (lay["k"], 2 * L * d), (lay["vt"], 2 * L * d),
+             (lay["o"], (2 if bo else 4) * L * d), (lay["x1"], 4 * L * d),
+             (lay["g"], (2 if bm else 4) * L * F)]
+    for name, n in (("qa", L * d), ("qo", L * d), ("qa2", L * d), ("qg", L * F),
+                    ("h", 2 * L * d), ("h2", 2 * L * d)):
+        if lay[name]:
+            spans.append((lay[name], n))
+    spans.sort()
+    for (o1, n1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 + n1 <= o2
+    assert spans[-1][0] + spans[-1][1] <= lay["total"]
+    assert lay["total"] == h3k.workspace_bytes(dm, L, flags)
+
+
 def _block(dm, L, flags=0, x=FAKE, out=FAKE, cond=FAKE, ws=FAKE, ws_bytes=1 << 40, w=None):
     if w is None:
         w = h3k.BlockWeightsC(*([FAKE] * 9 + [None] * 4))
@@ -80,6 +108,10 @@ def _block(dm, L, flags=0, x=FAKE, out=FAKE, cond=FAKE, ws=FAKE, ws_bytes=1 << 4
     (dict(ws_bytes=1024), h3k.ENOSPC),
     (dict(flags=h3k.F_BF16_GEMM), h3k.EINVAL),                  # dense weights missing
     (dict(flags=h3k.F_BF16_GEMM | h3k.F_FP32_DEBUG), h3k.EUNSUPPORTED),
+    (dict(flags=h3k.F_BF16_QKV), h3k.EINVAL),                   # dense QKV weights missing
+    (dict(flags=h3k.F_BF16_OUT), h3k.EINVAL),                   # dense out-proj weights missing
+    (dict(flags=h3k.F_BF16_MLP), h3k.EINVAL),                   # dense MLP weights missing
+    (dict(flags=h3k.F_BF16_MLP | h3k.F_FP32_DEBUG), h3k.EUNSUPPORTED),
     (dict(flags=64), h3k.EINVAL),
 ])
 def test_block_validation(case, code):

@@ -24,8 +24,14 @@ def _wl(name, **kw):
     return dataclasses.replace(S.WORKLOADS[name], **kw)
 
 
+BF16_ANY = h3k.F_BF16_GEMM | h3k.F_BF16_QKV | h3k.F_BF16_OUT | h3k.F_BF16_MLP
+# the precision series: oracle variant -> flags that select the bf16 projections
+SERIES = [("w8a8", 0), ("int8_mlp_qkv", h3k.F_BF16_OUT),
+          ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT), ("bf16gemm", h3k.F_BF16_GEMM)]
+
+
 def run_gpu(wl, flags=0, zero_gates=False, gen_device="cpu"):
-    bw, dense = gpu_block(wl, 0, keep_bf16=bool(flags & h3k.F_BF16_GEMM), gen_device=gen_device)
+    bw, dense = gpu_block(wl, 0, keep_bf16=bool(flags & BF16_ANY), gen_device=gen_device)
     if zero_gates:
         d = wl.d
         bw.w_ada[2 * d:3 * d] = 0
@@ -43,18 +49,23 @@ def run_gpu(wl, flags=0, zero_gates=False, gen_device="cpu"):
 
 def oracle_full(wl, r, variant="w8a8", rows=None, attn_inputs=None):
     """The oracle block on the run's inputs. On the bf16 path the attention consumes bf16
-    Q, K, V, so the oracle rounds them there (attn_inputs="bf16"); the fp32 debug path is
-    compared with the all-fp64 oracle."""
+    Q, K, V and every bf16 projection bf16 activations, so the oracle rounds them there
+    (attn_inputs = dense_inputs = "bf16"); the fp32 debug path is compared with the
+    all-fp64 oracle."""
     if attn_inputs is None:
         attn_inputs = "fp64" if r["flags"] & h3k.F_FP32_DEBUG else "bf16"
-    w = oracle_weights(r["bw"], r["dense"] if variant == "bf16gemm" else None)
+    w = oracle_weights(r["bw"], r["dense"] if variant != "w8a8" else None)
     return O.block_forward(np64(r["x"]), np64(r["c"]), w, n_heads=wl.n_heads, head_dim=wl.head_dim,
-                           grid=wl.grid, variant=variant, rows=rows, attn_inputs=attn_inputs)
+                           grid=wl.grid, variant=variant, rows=rows, attn_inputs=attn_inputs,
+                           dense_inputs=attn_inputs)
 
 
 # ----------------------------------------------------------------------------- tiny, full oracle
 @pytest.mark.parametrize("variant,flags,tol", [("w8a8", 0, 2e-2), ("w8a8", h3k.F_FP32_DEBUG, 1e-3),
-                                               ("bf16gemm", h3k.F_BF16_GEMM, 2e-2)])
+                                               ("bf16gemm", h3k.F_BF16_GEMM, 2e-2),
+                                               ("int8_mlp_qkv", h3k.F_BF16_OUT, 2e-2),
+                                               ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT, 2e-2),
+                                               ("bf16gemm", h3k.F_BF16_QKV | h3k.F_BF16_OUT | h3k.F_BF16_MLP, 2e-2)])
 def test_block_tiny(variant, flags, tol):
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl, flags)
@@ -75,7 +86,8 @@ def test_block_ragged(grid, H, Dh):
         assert err <= tol, (grid, flags, err)
 
 
-@pytest.mark.parametrize("flags", [0, h3k.F_FP32_DEBUG, h3k.F_BF16_GEMM])
+@pytest.mark.parametrize("flags", [0, h3k.F_FP32_DEBUG, h3k.F_BF16_GEMM, h3k.F_BF16_OUT,
+                                   h3k.F_BF16_QKV | h3k.F_BF16_OUT])
 def test_block_zero_gates_identity(flags):
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl, flags, zero_gates=True)
@@ -111,7 +123,7 @@ def _sample_rows(L, n, seed):
     return np.unique(np.concatenate([[0, L - 1], rows]))
 
 
-@pytest.mark.parametrize("variant,flags", [("w8a8", 0), ("bf16gemm", h3k.F_BF16_GEMM)])
+@pytest.mark.parametrize("variant,flags", SERIES)
 def test_block_l4096(variant, flags):
     wl = S.WORKLOADS["block_l4096"]
     r = run_gpu(wl, flags, gen_device="cuda")

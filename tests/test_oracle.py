@@ -206,8 +206,9 @@ def test_gelu_textbook():
 
 
 # ----------------------------------------------------------------------------- block (brute force)
-def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0):
-    """Independent scalar-loop implementation of the block on tiny shapes."""
+def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_dense=False):
+    """Independent scalar-loop implementation of the block on tiny shapes. round_dense:
+    dense projections take bf16-rounded activations (torch's RNE conversion)."""
     L, d = len(x), len(x[0])
     F = len(w["w_up"])
     m = [math.fsum(w["w_ada"][i][j] * c[j] for j in range(len(c))) for i in range(6 * d)]
@@ -233,13 +234,18 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0):
             codes.append(max(-127, min(127, int(r))))
         return codes, float(np.float32(a) / np.float32(127))
 
+    int8 = {"w8a8": {"_qkv", "_o", "_up", "_down"}, "int8_mlp_qkv": {"_qkv", "_up", "_down"},
+            "int8_mlp": {"_up", "_down"}, "bf16gemm": set()}[variant]
+
     def lin(row, name):
-        if variant == "w8a8":
+        if name in int8:
             codes, s = quant(row)
             Wq, Ws = w["q" + name], w["s" + name]
             return [sum(codes[k] * int(Wq[n][k]) for k in range(len(row))) * s * float(Ws[n])
                     for n in range(len(Wq))]
         Wd = w["w" + name]
+        if round_dense:
+            row = torch.tensor(row, dtype=torch.float64).to(torch.bfloat16).double().tolist()
         return [math.fsum(row[k] * Wd[n][k] for k in range(len(row))) for n in range(len(Wd))]
 
     T, Hg, Wg = grid
@@ -291,7 +297,7 @@ def _tiny_weights(d, F, dc, seed):
     return O.quantize_block_weights(wb)
 
 
-@pytest.mark.parametrize("variant", ["w8a8", "bf16gemm"])
+@pytest.mark.parametrize("variant", ["w8a8", "int8_mlp_qkv", "int8_mlp", "bf16gemm"])
 def test_block_bruteforce_tiny(variant):
     d, H, Dh, F, dc, grid = 12, 2, 6, 24, 5, (2, 2, 2)
     w = _tiny_weights(d, F, dc, 7)
@@ -311,6 +317,23 @@ def test_block_bruteforce_tiny(variant):
     # row subsets are the same rows of the full output
     sub = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant, rows=[5, 1])
     assert np.array_equal(sub, got[[5, 1]])
+
+
+@pytest.mark.parametrize("variant", ["int8_mlp", "bf16gemm"])
+def test_block_bruteforce_dense_bf16_inputs(variant):
+    d, H, Dh, F, dc, grid = 12, 2, 6, 24, 5, (2, 2, 2)
+    w = _tiny_weights(d, F, dc, 11)
+    r = np.random.default_rng(12)
+    x = _bf16(r.standard_normal((8, d)))
+    c = r.standard_normal(dc)
+    got = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
+                          dense_inputs="bf16")
+    ref = _bf_block(x.tolist(), c.tolist(), {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()},
+                    H, Dh, grid, variant, round_dense=True)
+    assert np.allclose(got, ref, rtol=1e-9, atol=1e-9)
+    # rounding the operands changes the result (the option is not a no-op)
+    plain = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant)
+    assert not np.allclose(got, plain, rtol=1e-9, atol=1e-9)
 
 
 def test_block_zero_gates_identity():

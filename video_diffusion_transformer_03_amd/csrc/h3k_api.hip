@@ -111,10 +111,20 @@ int check_dims(const char *fn, const h3k_dims *dm, int64_t L) {
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// which projections run as bf16 GEMMs
+struct Prec {
+  bool qkv, out, mlp;
+  explicit Prec(uint32_t f)
+      : qkv(f & (H3K_F_BF16_GEMM | H3K_F_BF16_QKV)),
+        out(f & (H3K_F_BF16_GEMM | H3K_F_BF16_OUT)),
+        mlp(f & (H3K_F_BF16_GEMM | H3K_F_BF16_MLP)) {}
+  bool any() const { return qkv || out || mlp; }
+};
+
 void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
   const size_t d = dm->d, F = dm->d_ff, H = dm->n_heads, Dh = dm->head_dim;
   const size_t T = (flags & H3K_F_FP32_DEBUG) ? 4 : 2;
-  const bool bf = (flags & H3K_F_BF16_GEMM) != 0;
+  const Prec p(flags);
   const size_t Lz = (size_t)L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -128,19 +138,19 @@ void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
   w->s_o = take(Lz * 4);
   w->s_a2 = take(Lz * 4);
   w->s_g = take(Lz * 4);
-  w->qa = bf ? 0 : take(Lz * d);
-  w->qo = bf ? 0 : take(Lz * d);
-  w->qa2 = bf ? 0 : take(Lz * d);
-  w->qg = bf ? 0 : take(Lz * F);
+  w->qa = p.qkv ? 0 : take(Lz * d);
+  w->qo = p.out ? 0 : take(Lz * d);
+  w->qa2 = p.mlp ? 0 : take(Lz * d);
+  w->qg = p.mlp ? 0 : take(Lz * F);
   w->q = take(H * Lz * Dh * T);
   w->k = take(H * Lz * Dh * T);
   w->vt = take(H * Lz * Dh * T);
-  // O, x1 and g feed quantisers (or the next GEMM): fp32 except on the dense bf16 path
-  w->o = take(Lz * d * (bf ? 2 : 4));
+  // O, x1 and g feed quantisers (fp32) or a bf16 GEMM (bf16)
+  w->o = take(Lz * d * (p.out ? 2 : 4));
   w->x1 = take(Lz * d * 4);
-  w->g = take(Lz * F * (bf ? 2 : 4));
-  w->h = bf ? take(Lz * d * 2) : 0;
-  w->h2 = bf ? take(Lz * d * 2) : 0;
+  w->g = take(Lz * F * (p.mlp ? 2 : 4));
+  w->h = p.qkv ? take(Lz * d * 2) : 0;
+  w->h2 = p.mlp ? take(Lz * d * 2) : 0;
   w->total = off;
 }
 
@@ -152,16 +162,23 @@ P *at(void *ws, size_t off) {
 int check_weights(const char *fn, const h3k_block_weights *w, uint32_t flags) {
   if (!w) return fail(H3K_EINVAL, "%s: weights is NULL", fn);
   H3K_CHECK_PTR(w->w_ada);
-  if (flags & H3K_F_BF16_GEMM) {
+  const Prec p(flags);
+  if (p.qkv) {
     H3K_CHECK_PTR(w->wb_qkv);
-    H3K_CHECK_PTR(w->wb_o);
-    H3K_CHECK_PTR(w->wb_up);
-    H3K_CHECK_PTR(w->wb_down);
   } else {
     H3K_CHECK_PTR(w->w_qkv);
     H3K_CHECK_PTR(w->s_qkv);
+  }
+  if (p.out) {
+    H3K_CHECK_PTR(w->wb_o);
+  } else {
     H3K_CHECK_PTR(w->w_o);
     H3K_CHECK_PTR(w->s_o);
+  }
+  if (p.mlp) {
+    H3K_CHECK_PTR(w->wb_up);
+    H3K_CHECK_PTR(w->wb_down);
+  } else {
     H3K_CHECK_PTR(w->w_up);
     H3K_CHECK_PTR(w->s_up);
     H3K_CHECK_PTR(w->w_down);
@@ -171,10 +188,11 @@ int check_weights(const char *fn, const h3k_block_weights *w, uint32_t flags) {
 }
 
 int check_flags(const char *fn, uint32_t flags) {
-  if (flags & ~(uint32_t)(H3K_F_BF16_GEMM | H3K_F_FP32_DEBUG | H3K_F_SYNC))
+  if (flags & ~(uint32_t)(H3K_F_BF16_GEMM | H3K_F_FP32_DEBUG | H3K_F_SYNC | H3K_F_BF16_QKV |
+                          H3K_F_BF16_OUT | H3K_F_BF16_MLP))
     return fail(H3K_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
-  if ((flags & H3K_F_BF16_GEMM) && (flags & H3K_F_FP32_DEBUG))
-    return fail(H3K_EUNSUPPORTED, "%s: H3K_F_BF16_GEMM with H3K_F_FP32_DEBUG is unsupported", fn);
+  if (Prec(flags).any() && (flags & H3K_F_FP32_DEBUG))
+    return fail(H3K_EUNSUPPORTED, "%s: bf16 projections with H3K_F_FP32_DEBUG are unsupported", fn);
   return H3K_OK;
 }
 
@@ -186,7 +204,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   const int64_t L = (int64_t)T * Hg * Wg;
   const int d = dm->d, F = dm->d_ff, H = dm->n_heads, Dh = dm->head_dim;
   const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
-  const bool bf = (flags & H3K_F_BF16_GEMM) != 0;
+  const Prec p(flags);
   h3k_ws_layout lay;
   plan(dm, L, flags, &lay);
   float *m = at<float>(ws, lay.m);
@@ -208,8 +226,8 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // LN + modulate (+ quant)
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
-    hipError_t e = bf ? launch_rows(1, x_in, false, shift1, scale1, L, d, dm->ln_eps, nullptr, nullptr,
-                                    at<uint16_t>(ws, lay.h), s)
+    hipError_t e = p.qkv ? launch_rows(1, x_in, false, shift1, scale1, L, d, dm->ln_eps, nullptr, nullptr,
+                                       at<uint16_t>(ws, lay.h), s)
                       : launch_rows(0, x_in, f32, shift1, scale1, L, d, dm->ln_eps,
                                     at<int8_t>(ws, lay.qa), at<float>(ws, lay.s_a), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant"))) return rc;
@@ -217,12 +235,12 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // QKV + RoPE + head-major scatter
   GemmArgs ga{};
   ga.M = L;
-  ga.bf16_ops = bf;
   ga.out_f32 = f32;
   {
     GemmArgs a = ga;
-    a.A = bf ? (const void *)at<uint16_t>(ws, lay.h) : (const void *)at<int8_t>(ws, lay.qa);
-    a.B = bf ? (const void *)w->wb_qkv : (const void *)w->w_qkv;
+    a.bf16_ops = p.qkv;
+    a.A = p.qkv ? (const void *)at<uint16_t>(ws, lay.h) : (const void *)at<int8_t>(ws, lay.qa);
+    a.B = p.qkv ? (const void *)w->wb_qkv : (const void *)w->w_qkv;
     a.N = 3 * d;
     a.K = d;
     a.sa = at<float>(ws, lay.s_a);
@@ -242,11 +260,11 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
-                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !bf, s);
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !p.out, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
   // quantise O
-  if (!bf) {
+  if (!p.out) {
     Launch l(H3K_K_ROWQUANT_O, s, flags);
     if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), true, nullptr, nullptr, L, d, 0.f,
                                  at<int8_t>(ws, lay.qo), at<float>(ws, lay.s_o), nullptr, s),
@@ -257,8 +275,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   float *x1 = at<float>(ws, lay.x1);
   {
     GemmArgs a = ga;
-    a.A = bf ? (const void *)at<uint16_t>(ws, lay.o) : (const void *)at<int8_t>(ws, lay.qo);
-    a.B = bf ? (const void *)w->wb_o : (const void *)w->w_o;
+    a.bf16_ops = p.out;
+    a.A = p.out ? (const void *)at<uint16_t>(ws, lay.o) : (const void *)at<int8_t>(ws, lay.qo);
+    a.B = p.out ? (const void *)w->wb_o : (const void *)w->w_o;
     a.N = d;
     a.K = d;
     a.sa = at<float>(ws, lay.s_o);
@@ -274,8 +293,8 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // LN + modulate (+ quant) of x1
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
-    hipError_t e = bf ? launch_rows(1, x1, true, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
-                                    at<uint16_t>(ws, lay.h2), s)
+    hipError_t e = p.mlp ? launch_rows(1, x1, true, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
+                                       at<uint16_t>(ws, lay.h2), s)
                       : launch_rows(0, x1, true, shift2, scale2, L, d, dm->ln_eps,
                                     at<int8_t>(ws, lay.qa2), at<float>(ws, lay.s_a2), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant_2"))) return rc;
@@ -283,19 +302,20 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // MLP up + GELU
   {
     GemmArgs a = ga;
-    a.A = bf ? (const void *)at<uint16_t>(ws, lay.h2) : (const void *)at<int8_t>(ws, lay.qa2);
-    a.B = bf ? (const void *)w->wb_up : (const void *)w->w_up;
+    a.bf16_ops = p.mlp;
+    a.A = p.mlp ? (const void *)at<uint16_t>(ws, lay.h2) : (const void *)at<int8_t>(ws, lay.qa2);
+    a.B = p.mlp ? (const void *)w->wb_up : (const void *)w->w_up;
     a.N = F;
     a.K = d;
     a.sa = at<float>(ws, lay.s_a2);
     a.sw = w->s_up;
     a.out = at<void>(ws, lay.g);
-    a.out_f32 = !bf;
+    a.out_f32 = !p.mlp;
     Launch l(H3K_K_GEMM_UP, s, flags);
     if ((rc = l.done(launch_gemm(EPI_GELU, a, s), fn, "gemm_up"))) return rc;
   }
   // quantise g
-  if (!bf) {
+  if (!p.mlp) {
     Launch l(H3K_K_ROWQUANT_G, s, flags);
     if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), true, nullptr, nullptr, L, F, 0.f,
                                  at<int8_t>(ws, lay.qg), at<float>(ws, lay.s_g), nullptr, s),
@@ -305,8 +325,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // MLP down + gated residual: x_out = x1 + gate2 * y
   {
     GemmArgs a = ga;
-    a.A = bf ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
-    a.B = bf ? (const void *)w->wb_down : (const void *)w->w_down;
+    a.bf16_ops = p.mlp;
+    a.A = p.mlp ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
+    a.B = p.mlp ? (const void *)w->wb_down : (const void *)w->w_down;
     a.N = d;
     a.K = F;
     a.sa = at<float>(ws, lay.s_g);

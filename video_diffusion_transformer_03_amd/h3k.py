@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libh3k.so")
 
 OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 F_BF16_GEMM, F_FP32_DEBUG, F_SYNC = 1, 2, 4
+# per-projection bf16 GEMMs (the precision series); F_BF16_GEMM is all three
+F_BF16_QKV, F_BF16_OUT, F_BF16_MLP = 8, 16, 32
 DT_F32, DT_BF16 = 0, 1
 KERNELS = ["adaln", "rope_table", "ln_quant", "gemm_qkv", "attention", "rowquant_o",
            "gemm_o", "gemm_up", "rowquant_g", "gemm_down", "token_pair", "token_unpair"]
