@@ -251,8 +251,9 @@ def _time_steps(torch, fn, steps, warmup):
 def extras(S, h3k, torch):
     """Measurements beside the headline line:
       - the 50-block stack at L=16384: ms per denoising step without and with horizontal
-        token pairing in blocks [10, 40), and a sweep of pairing ranges with the relative
-        L2 distance of the stack output from the unpaired stack's;
+        token pairing in blocks [10, 40), eager and replayed as a recorded HIP graph, and a
+        sweep of pairing ranges with the relative L2 distance of the stack output from the
+        unpaired stack's;
       - the precision series at L=16384 (BF16 GEMMs, int8 MLP, int8 MLP + QKV, W8A8);
       - block time against sequence length (L = 4096 .. 65536) with a least-squares fit
         t = a L + b L^2, and one block at L=65536 with its attention fraction."""
@@ -273,6 +274,11 @@ def extras(S, h3k, torch):
         ws = h3k.alloc_workspace(h3k.stack_workspace_bytes(dims, wl.L, *tr))
         y = torch.empty_like(x)
         t = _time_steps(torch, lambda: h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y), 2, 1)
+        if tr in ((0, 0), tuple(wl.tr_range)):
+            g = h3k.stack_graph(x, c, blocks, dims, tr[0], tr[1], 0, ws, y)
+            tg = _time_steps(torch, g.launch, 2, 1)
+            res["graph_" + ("token_reduction" if tr[1] > tr[0] else "full")] = round(tg * 1e3, 2)
+            del g
         if tr == (0, 0):
             ref = y.float().clone()
             res["full"] = round(t * 1e3, 2)

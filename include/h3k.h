@@ -192,6 +192,32 @@ int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
                       const h3k_dims *dm, int64_t L, int32_t tr_begin, int32_t tr_end,
                       uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- the stack step as a HIP graph ---- */
+
+/* A recorded h3k_stack_forward call: its kernels with these exact arguments (pointers,
+ * sizes, flags) as one HIP graph, so that a denoising loop launches a whole 50-block step
+ * with one call (launch amortisation; "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3
+ * 추론" and "MiniMax-H3在Apple Silicon上的兩種推理實現工程取舍", section 性能上限, describe
+ * the reference's pre-encoded two-part command buffers). */
+typedef struct h3k_graph_s h3k_graph;
+
+/* Records the call on `stream` (a created stream: capture is not possible on the null
+ * stream) without running it. Arguments and errors as h3k_stack_forward; H3K_F_SYNC is
+ * rejected (H3K_EINVAL). Every launch of the graph reads the buffers as they are then, so
+ * the caller updates x_in / cond in place between launches and keeps every buffer alive
+ * while the graph exists. On success *graph_out owns a graph (free with
+ * h3k_graph_destroy); on error it is NULL. */
+int h3k_stack_graph_create(const void *x_in, void *x_out, const float *cond,
+                           const h3k_block_weights *blocks, int32_t n_blocks,
+                           const h3k_dims *dm, int64_t L, int32_t tr_begin, int32_t tr_end,
+                           uint32_t flags, void *ws, size_t ws_bytes, void *stream,
+                           h3k_graph **graph_out);
+/* Enqueues the recorded step on `stream` (any stream). Launches on one workspace must not
+ * overlap. */
+int h3k_graph_launch(h3k_graph *graph, void *stream);
+/* Frees the graph (NULL is ignored). */
+void h3k_graph_destroy(h3k_graph *graph);
+
 /* ---- single steps of the block (the same kernels the block call launches) ---- */
 
 /* m[i] = sum_j w_ada[i, j] * cond[j], fp32 accumulation. w_ada bf16 [n_out, d_cond],

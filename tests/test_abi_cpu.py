@@ -156,3 +156,21 @@ def test_component_validation():
     assert lib.h3k_token_pair(FAKE, FAKE, FAKE, h3k.DT_BF16, 2, 2, 3, 8, None) == h3k.EINVAL
     assert lib.h3k_token_unpair(FAKE, FAKE, FAKE, h3k.DT_BF16, 2, 2, 4, 12, None) == h3k.EUNSUPPORTED
     assert lib.h3k_profile_read(99, C.byref(C.c_int64()), C.byref(C.c_double())) == h3k.EINVAL
+
+
+def test_stack_graph_validation():
+    """Graph creation refuses, before any HIP call, a NULL output handle, the null stream
+    (capture needs a created stream) and H3K_F_SYNC (a host sync cannot be recorded)."""
+    lib = h3k.lib()
+    dm = tiny_dims()
+    arr = (h3k.BlockWeightsC * 2)(*[h3k.BlockWeightsC(*([FAKE] * 9 + [None] * 4)) for _ in range(2)])
+    h = C.c_void_p(FAKE)
+    args = (FAKE, FAKE, FAKE, arr, 2, C.byref(dm), 512, 0, 0)
+    assert lib.h3k_stack_graph_create(*args, 0, FAKE, 1 << 40, FAKE, None) == h3k.EINVAL
+    assert lib.h3k_stack_graph_create(*args, 0, FAKE, 1 << 40, None, C.byref(h)) == h3k.EINVAL
+    assert h.value is None and "null stream" in h3k.last_error()
+    h = C.c_void_p(FAKE)
+    assert lib.h3k_stack_graph_create(*args, h3k.F_SYNC, FAKE, 1 << 40, FAKE, C.byref(h)) == h3k.EINVAL
+    assert h.value is None and "H3K_F_SYNC" in h3k.last_error()
+    assert lib.h3k_graph_launch(None, None) == h3k.EINVAL
+    lib.h3k_graph_destroy(None)  # NULL is ignored

@@ -60,6 +60,32 @@ def test_stack_zero_gates_identity():
         assert torch.equal(out, x), tr
 
 
+@pytest.mark.parametrize("tr", [(0, 0), (1, 2), (0, 2), (0, 3)])
+def test_stack_graph_replays_tiny(tr):
+    """A recorded stack step equals the eager call bit for bit on every replay, with other
+    eager work between replays, and picks up new input contents."""
+    wl = dataclasses.replace(S.WORKLOADS["tiny"], n_blocks=3)
+    blocks = _blocks(wl, 3)
+    x = S.activations(wl).cuda()
+    c = S.conditioning(wl).cuda()
+    dims = h3k.dims_of(wl)
+    eager = h3k.stack_forward(x, c, blocks, dims, *tr)
+    xg = x.clone()
+    g = h3k.stack_graph(xg, c, blocks, dims, *tr)
+    for rep in range(3):
+        other = h3k.stack_forward(x.flip(0).contiguous(), c, blocks, dims, *tr)  # eager work between
+        out = g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        assert torch.isfinite(other.float()).all()
+    x2 = (x.float() * 0.5).to(x.dtype)
+    xg.copy_(x2)
+    out = g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(out, h3k.stack_forward(x2, c, blocks, dims, *tr))
+    del g
+
+
 def _compose(wl, x, c, blocks, tr, on_block=None):
     """The stack composed from single-block calls (the same kernels, one call each)."""
     T, Hg, Wg = wl.grid
@@ -123,3 +149,11 @@ def test_stack50_l16384_token_reduction():
     comp = _compose(wl, x, c, blocks, tr, on_block)
     assert sorted(seen) == sorted(sampled)
     assert torch.equal(comp, out)
+
+    # the same step recorded as a graph: two replays, bitwise equal to the eager call
+    g = h3k.stack_graph(x, c, blocks, dims, *tr)
+    for _ in range(2):
+        got = g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(got, out)
+    del g

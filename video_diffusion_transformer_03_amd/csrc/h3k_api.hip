@@ -506,7 +506,7 @@ int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
     if (tr && b == tr_begin) {
       // x_out holds the full-resolution state x_pre until the unpair
       if (src != x_out) {
-        hipError_t e = hipMemcpyAsync(x_out, src, (size_t)L * dm->d * esz, hipMemcpyDeviceToDevice, s);
+        hipError_t e = launch_copy16(x_out, src, (int64_t)L * dm->d * (int64_t)esz / 16, s);
         if (e != hipSuccess) return fail(H3K_EHIP, "%s: copy failed: %s", fn, hipGetErrorString(e));
         src = x_out;
       }
@@ -528,6 +528,65 @@ int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
     }
   }
   return H3K_OK;
+}
+
+struct h3k_graph_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+int h3k_stack_graph_create(const void *x_in, void *x_out, const float *cond,
+                           const h3k_block_weights *blocks, int32_t n_blocks, const h3k_dims *dm,
+                           int64_t L, int32_t tr_begin, int32_t tr_end, uint32_t flags, void *ws,
+                           size_t ws_bytes, void *stream, h3k_graph **graph_out) {
+  const char *fn = "h3k_stack_graph_create";
+  if (!graph_out) return fail(H3K_EINVAL, "%s: graph_out is NULL", fn);
+  *graph_out = nullptr;
+  if (!stream) return fail(H3K_EINVAL, "%s: capture needs a created stream, not the null stream", fn);
+  if (flags & H3K_F_SYNC) return fail(H3K_EINVAL, "%s: H3K_F_SYNC synchronises the stream; not capturable", fn);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: begin capture: %s", fn, hipGetErrorString(e));
+  const bool prof = g_prof_on;
+  g_prof_on = false;  // no event nodes in the graph
+  int rc = h3k_stack_forward(x_in, x_out, cond, blocks, n_blocks, dm, L, tr_begin, tr_end, flags,
+                             ws, ws_bytes, stream);
+  g_prof_on = prof;
+  std::string err = rc ? g_err : std::string();
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(s, &graph);
+  if (rc) {
+    if (graph) hipGraphDestroy(graph);
+    g_err = std::string(fn) + ": " + err;
+    return rc;
+  }
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: end capture: %s", fn, hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    hipGraphDestroy(graph);
+    return fail(H3K_EHIP, "%s: instantiate: %s", fn, hipGetErrorString(e));
+  }
+  h3k_graph *g = new h3k_graph;
+  g->graph = graph;
+  g->exec = exec;
+  *graph_out = g;
+  return H3K_OK;
+}
+
+int h3k_graph_launch(h3k_graph *graph, void *stream) {
+  const char *fn = "h3k_graph_launch";
+  if (!graph) return fail(H3K_EINVAL, "%s: graph is NULL", fn);
+  hipError_t e = hipGraphLaunch(graph->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+void h3k_graph_destroy(h3k_graph *graph) {
+  if (!graph) return;
+  if (graph->exec) hipGraphExecDestroy(graph->exec);
+  if (graph->graph) hipGraphDestroy(graph->graph);
+  delete graph;
 }
 
 int h3k_adaln_modulation(const uint16_t *w_ada, const float *cond, float *m, int64_t n_out,

@@ -79,6 +79,8 @@ hipError_t launch_token_pair(const void *x, void *xr, void *xr2, bool f32, int T
                              int Wg, int d, hipStream_t s);
 hipError_t launch_token_unpair(void *x, const void *xo, const void *xi, bool f32, int T,
                                int Hg, int Wg, int d, hipStream_t s);
+// dst = src, n16 16-byte chunks (both 16-byte aligned)
+hipError_t launch_copy16(void *dst, const void *src, int64_t n16, hipStream_t s);
 
 // GEMM: out = epilogue(A[M,K] . B[N,K]^T). A = activations (tokens), B = weights.
 enum EpiKind { EPI_RAW_I32 = 0, EPI_QKV = 1, EPI_GELU = 2, EPI_RESID = 3 };

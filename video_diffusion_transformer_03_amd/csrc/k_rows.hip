@@ -404,4 +404,19 @@ hipError_t launch_token_unpair(void *x, const void *xo, const void *xi, bool f32
   return hipGetLastError();
 }
 
+// device-to-device copy of n16 16-byte chunks (a kernel, so that a captured stack graph
+// holds kernel nodes only)
+__global__ __launch_bounds__(256) void copy16_kernel(uint4 *__restrict__ dst,
+                                                     const uint4 *__restrict__ src, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy16(void *dst, const void *src, int64_t n16, hipStream_t s) {
+  const int64_t blocks = (n16 + 255) / 256;
+  dim3 grid((unsigned)(blocks < 8192 ? blocks : 8192));
+  copy16_kernel<<<grid, 256, 0, s>>>((uint4 *)dst, (const uint4 *)src, n16);
+  return hipGetLastError();
+}
+
 }  // namespace h3k

@@ -81,6 +81,11 @@ def lib() -> C.CDLL:
             "h3k_token_pair": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, i32, vp]),
             "h3k_token_unpair": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, i32, vp]),
             "h3k_last_error": (C.c_char_p, []),
+            "h3k_stack_graph_create": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), i32,
+                                                 C.POINTER(Dims), i64, i32, i32, u32, vp, sz, vp,
+                                                 C.POINTER(vp)]),
+            "h3k_graph_launch": (C.c_int, [vp, vp]),
+            "h3k_graph_destroy": (None, [vp]),
             "h3k_profile_enable": (C.c_int, [C.c_int]),
             "h3k_profile_read": (C.c_int, [C.c_int, C.POINTER(i64), C.POINTER(C.c_double)]),
         }
@@ -273,6 +278,47 @@ def stack_forward(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWei
                                    C.byref(dims), L, tr_begin, tr_end, flags, _dev(ws, "ws"),
                                    ws.numel(), _stream(stream)))
     return out
+
+
+class StackGraph:
+    """A recorded h3k_stack_forward call (h3k_stack_graph_create). launch() replays it on
+    a stream; it reads x and cond as they are at launch time and writes out. Holds the
+    tensors it was recorded with, so they stay alive while the graph exists."""
+
+    def __init__(self, x, cond, blocks, dims, tr_begin, tr_end, flags, ws, out, capture_stream):
+        self._keep = (x, cond, list(blocks), ws, out)
+        self.out = out
+        arr = (BlockWeightsC * len(blocks))(*[b.c_struct() for b in blocks])
+        h = C.c_void_p()
+        _check(lib().h3k_stack_graph_create(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), arr,
+                                            len(blocks), C.byref(dims), x.shape[0], tr_begin, tr_end,
+                                            flags, _dev(ws, "ws"), ws.numel(),
+                                            C.c_void_p(capture_stream.cuda_stream), C.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None) -> torch.Tensor:
+        _check(lib().h3k_graph_launch(self._h, _stream(stream)))
+        return self.out
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().h3k_graph_destroy(h)
+            self._h = None
+
+
+def stack_graph(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWeights], dims: Dims,
+                tr_begin: int = 0, tr_end: int = 0, flags: int = 0,
+                ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> StackGraph:
+    """Record a stack step (captured on a side stream created here; nothing runs)."""
+    L = x.shape[0]
+    if ws is None:
+        ws = alloc_workspace(stack_workspace_bytes(dims, L, tr_begin, tr_end, flags), x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    side = torch.cuda.Stream(device=x.device)
+    torch.cuda.current_stream(x.device).synchronize()
+    return StackGraph(x, cond, blocks, dims, tr_begin, tr_end, flags, ws, out, side)
 
 
 def adaln_modulation(w_ada: torch.Tensor, cond: torch.Tensor, stream=None) -> torch.Tensor:
