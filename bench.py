@@ -291,6 +291,23 @@ def extras(S, h3k, torch):
         del ws, y
     out["stack50_l16384_ms_per_denoise_step"] = res
     out["stack50_token_reduction_sweep"] = sweep
+    # whole denoising loops (h3k_denoise) with the pages' speed/quality controls: the
+    # aggressive pass count, and the default column of their table (20 passes, reuse 2,
+    # core reuse 4, 45 blocks, token pairing on)
+    loops = {}
+    for name, kw in [("steps4", dict(steps=4, reuse=1, core_reuse=1, layers=50, tr=(0, 0))),
+                     ("steps20_reuse2_core4_layers45_tr", dict(steps=20, reuse=2, core_reuse=4,
+                                                               layers=45, tr=(10, 40)))]:
+        ws = h3k.alloc_workspace(h3k.denoise_workspace_bytes(dims, wl.L, *kw["tr"]))
+        xs = x.clone()
+        run = lambda: h3k.denoise(xs, c, blocks, dims, kw["steps"], kw["reuse"], kw["core_reuse"],  # noqa: E731
+                                  kw["layers"], kw["tr"][0], kw["tr"][1], 0, ws)
+        t = _time_steps(torch, run, 1, 1)
+        loops[name] = {"s": round(t, 3), "stack_evaluations": len([
+            f for f, k in enumerate(k for k in range(kw["steps"]) if k % kw["reuse"] == 0 or k == kw["steps"] - 1)
+            if f % kw["core_reuse"] == 0 or k == kw["steps"] - 1])}
+        del ws, xs
+    out["denoise_l16384"] = loops
     del blocks, ref
     torch.cuda.empty_cache()
 

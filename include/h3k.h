@@ -192,6 +192,34 @@ int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
                       const h3k_dims *dm, int64_t L, int32_t tr_begin, int32_t tr_end,
                       uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- a denoising loop around the stack ---- */
+
+/* Workspace bytes for h3k_denoise (the stack's, plus the stack output y in the activation
+ * type and fp32 velocity v and core residual r, each [L, d]). */
+size_t h3k_denoise_workspace_bytes(const h3k_dims *dm, int64_t L, int32_t tr_begin,
+                                   int32_t tr_end, uint32_t flags);
+
+/* `steps` Euler steps of a flow-matching sampler on t_k = 1 - k / steps, k = 0 .. steps, with
+ * the speed/quality controls of "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론",
+ * section "속도 및 품질 트레이드오프" (the pages give the controls, not their formulas; this is
+ * the plainest reading, and the stack output stands in for the velocity because the
+ * patch embedding and output head are not part of the block stack):
+ *   - the stack is the first `layers` blocks (active DiT blocks), token pairing on
+ *     [tr_begin, tr_end) of them;
+ *   - whole-denoiser reuse: the velocity is evaluated afresh at steps k with k % reuse == 0
+ *     and at the last step, and reused in between (20 steps: 11 evaluations for reuse 2, 8
+ *     for reuse 3);
+ *   - core residual reuse: of those evaluations, every core_reuse-th and the last run the
+ *     stack (y = stack(x), cached residual r = y - x, v = y); the others use v = x + r;
+ *   - update x <- x + (t_{k+1} - t_k) v, stored in the activation type.
+ * x: [L, d] noise in, result out (bf16, or fp32 under H3K_F_FP32_DEBUG); other arguments as
+ * h3k_stack_forward. Errors: H3K_EINVAL for steps, reuse or core_reuse < 1, layers outside
+ * [1, n_blocks] or a pairing range outside [0, layers]; the stack's errors otherwise. */
+int h3k_denoise(void *x, const float *cond, const h3k_block_weights *blocks, int32_t n_blocks,
+                const h3k_dims *dm, int64_t L, int32_t steps, int32_t reuse, int32_t core_reuse,
+                int32_t layers, int32_t tr_begin, int32_t tr_end, uint32_t flags, void *ws,
+                size_t ws_bytes, void *stream);
+
 /* ---- the stack step as a HIP graph ---- */
 
 /* A recorded h3k_stack_forward call: its kernels with these exact arguments (pointers,

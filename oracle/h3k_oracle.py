@@ -339,3 +339,44 @@ def stack_forward(x, cond, blocks, *, n_heads: int, head_dim: int, grid,
         if tr_on and b == tr_end - 1:
             x = token_unpair(x_pre, x, xr_in, grid)
     return x
+
+
+# --------------------------------------------------------------------------- denoising loop
+def fresh_steps(steps: int, reuse: int) -> list:
+    """Steps k at which the whole denoiser is evaluated afresh: k % reuse == 0 and the last
+    step (page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
+    "속도 및 품질 트레이드오프": reuse cuts 20 passes to 11 or 8 fresh evaluations)."""
+    return [k for k in range(steps) if k % reuse == 0 or k == steps - 1]
+
+
+def denoise(x, core, *, steps: int, reuse: int = 1, core_reuse: int = 1,
+            store_bf16: bool = False) -> np.ndarray:
+    """Euler steps of a flow-matching sampler on t_k = 1 - k / steps (same page and section
+    give the controls --steps, --reuse, --core-reuse; the formulas are the plainest reading):
+    at fresh steps (fresh_steps) every core_reuse-th evaluation and the last one run the
+    core, y = core(x), caching r = y - x and setting v = y; the other fresh steps set
+    v = x + r; other steps keep v. Then x <- x + (t_{k+1} - t_k) v. core: callable on
+    [L, d] arrays (the stack of the active blocks). store_bf16 rounds y and each new x to
+    bfloat16, as the path that stores activations in bf16 does."""
+    x = np.asarray(x, np.float64).copy()
+    dt = -1.0 / steps
+    fresh = set(fresh_steps(steps, reuse))
+    v = r = None
+    f = 0
+    for k in range(steps):
+        last = k == steps - 1
+        if k in fresh:
+            if f % core_reuse == 0 or last:
+                y = core(x)
+                if store_bf16:
+                    y = round_bf16(y)
+                r = y - x
+                v = y
+            else:
+                v = x + r
+            f += 1
+        x = x + dt * v
+        if store_bf16:
+            x = round_bf16(x)
+    return x
+

@@ -174,3 +174,20 @@ def test_stack_graph_validation():
     assert h.value is None and "H3K_F_SYNC" in h3k.last_error()
     assert lib.h3k_graph_launch(None, None) == h3k.EINVAL
     lib.h3k_graph_destroy(None)  # NULL is ignored
+
+
+
+def test_denoise_validation():
+    lib = h3k.lib()
+    dm = tiny_dims()
+    arr = (h3k.BlockWeightsC * 2)(*[h3k.BlockWeightsC(*([FAKE] * 9 + [None] * 4)) for _ in range(2)])
+    base = dict(steps=4, reuse=1, core_reuse=1, layers=2, tb=0, te=0)
+    for bad in [dict(steps=0), dict(reuse=0), dict(core_reuse=0), dict(layers=0), dict(layers=3),
+                dict(tb=1, te=3), dict(tb=2, te=1)]:
+        a = dict(base, **bad)
+        rc = lib.h3k_denoise(FAKE, FAKE, arr, 2, C.byref(dm), 512, a["steps"], a["reuse"], a["core_reuse"],
+                             a["layers"], a["tb"], a["te"], 0, FAKE, 1 << 40, None)
+        assert rc == h3k.EINVAL, bad
+    rc = lib.h3k_denoise(FAKE, FAKE, arr, 2, C.byref(dm), 512, 4, 1, 1, 2, 0, 0, 0, FAKE, 1024, None)
+    assert rc == h3k.ENOSPC
+    assert h3k.denoise_workspace_bytes(dm, 512) > h3k.stack_workspace_bytes(dm, 512, 0, 0)

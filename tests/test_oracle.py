@@ -385,3 +385,39 @@ def test_stack_composition_and_identity():
         w["w_ada"][2 * d:3 * d] = 0.0
         w["w_ada"][5 * d:6 * d] = 0.0
     assert np.array_equal(O.stack_forward(x, c, blocks, tr_begin=1, tr_end=3, **kw), x)
+
+
+# ----------------------------------------------------------------------------- denoising loop
+def test_fresh_steps_match_pages():
+    # page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "속도 및 품질
+    # 트레이드오프": reuse 2 and 3 cut 20 denoising passes to 11 and 8 fresh DiT evaluations
+    assert len(O.fresh_steps(20, 1)) == 20
+    assert len(O.fresh_steps(20, 2)) == 11
+    assert len(O.fresh_steps(20, 3)) == 8
+    assert O.fresh_steps(4, 2) == [0, 2, 3]
+
+
+def test_denoise_linear_core_closed_forms():
+    """With a linear core y = a x the Euler sampler has products of (1 + c dt a) factors."""
+    a = 0.7
+    x0 = np.array([[1.0, -2.0, 0.5]])
+    core = lambda x: a * x  # noqa: E731
+    # no reuse: x_N = x_0 (1 + dt a)^N
+    N = 6
+    got = O.denoise(x0, core, steps=N)
+    assert np.allclose(got, x0 * (1 - a / N) ** N, rtol=1e-14, atol=0)
+    # whole reuse 2, 4 steps: fresh at k = 0, 2, 3 -> x_4 = x_0 (1 + 2 dt a)(1 + dt a)^2
+    dt = -1 / 4
+    got = O.denoise(x0, core, steps=4, reuse=2)
+    assert np.allclose(got, x0 * (1 + 2 * dt * a) * (1 + dt * a) ** 2, rtol=1e-14, atol=0)
+    # core reuse 2, 3 steps: k=0 runs the core (r = (a-1) x_0), k=1 uses v = x_1 + r,
+    # k=2 (last) runs the core again
+    dt = -1 / 3
+    x1 = x0 * (1 + dt * a)
+    x2 = x1 + dt * (x1 + (a - 1) * x0)
+    x3 = x2 * (1 + dt * a)
+    got = O.denoise(x0, core, steps=3, core_reuse=2)
+    assert np.allclose(got, x3, rtol=1e-14, atol=0)
+    # store_bf16 rounds every state: the result is exactly representable in bf16
+    got = O.denoise(x0, core, steps=3, store_bf16=True)
+    assert np.array_equal(got, O.round_bf16(got))

@@ -157,3 +157,33 @@ def test_stack50_l16384_token_reduction():
         torch.cuda.synchronize()
         assert torch.equal(got, out)
     del g
+
+
+
+@pytest.mark.parametrize("steps,reuse,core_reuse,layers,tr,flags", [
+    (4, 1, 1, 2, (0, 0), 0),
+    (5, 2, 2, 2, (1, 2), 0),
+    (4, 1, 3, 1, (0, 1), 0),
+    (3, 2, 1, 2, (0, 0), h3k.F_FP32_DEBUG),
+])
+def test_denoise_tiny(steps, reuse, core_reuse, layers, tr, flags):
+    """The denoising loop against the oracle's sampler around the oracle stack of the first
+    `layers` blocks (bf16 path: y and x stored in bf16 on both sides)."""
+    wl = dataclasses.replace(S.WORKLOADS["tiny"], n_blocks=2)
+    blocks = _blocks(wl, 2)
+    xdt = torch.float32 if flags else torch.bfloat16
+    x = S.activations(wl).cuda().to(xdt)
+    c = S.conditioning(wl).cuda()
+    x0 = np64(x)
+    got = h3k.denoise(x.clone(), c, blocks, h3k.dims_of(wl), steps, reuse, core_reuse, layers,
+                      tr[0], tr[1], flags)
+    torch.cuda.synchronize()
+    ow = [oracle_weights(b) for b in blocks[:layers]]
+    core = lambda xs: O.stack_forward(xs, np64(c), ow, n_heads=wl.n_heads, head_dim=wl.head_dim,  # noqa: E731
+                                      grid=wl.grid, tr_begin=tr[0], tr_end=tr[1],
+                                      attn_inputs="fp64" if flags else "bf16")
+    ref = O.denoise(x0, core, steps=steps, reuse=reuse, core_reuse=core_reuse, store_bf16=not flags)
+    err = rel_l2(np64(got), ref)
+    print(f"denoise steps={steps} reuse={reuse} core_reuse={core_reuse} layers={layers} tr={tr} "
+          f"flags={flags}: rel-L2 {err:.3e}")
+    assert err <= (1e-3 if flags else 2e-2)

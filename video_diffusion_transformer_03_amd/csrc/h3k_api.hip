@@ -530,6 +530,63 @@ int h3k_stack_forward(const void *x_in, void *x_out, const float *cond,
   return H3K_OK;
 }
 
+size_t h3k_denoise_workspace_bytes(const h3k_dims *dm, int64_t L, int32_t tr_begin,
+                                   int32_t tr_end, uint32_t flags) {
+  const size_t b = h3k_stack_workspace_bytes(dm, L, tr_begin, tr_end, flags);
+  if (!b) return 0;
+  const size_t T = (flags & H3K_F_FP32_DEBUG) ? 4 : 2;
+  const size_t n = (size_t)L * dm->d;
+  return b + up256(n * T) + 2 * up256(n * 4);
+}
+
+int h3k_denoise(void *x, const float *cond, const h3k_block_weights *blocks, int32_t n_blocks,
+                const h3k_dims *dm, int64_t L, int32_t steps, int32_t reuse, int32_t core_reuse,
+                int32_t layers, int32_t tr_begin, int32_t tr_end, uint32_t flags, void *ws,
+                size_t ws_bytes, void *stream) {
+  const char *fn = "h3k_denoise";
+  int rc;
+  if ((rc = check_flags(fn, flags))) return rc;
+  if ((rc = check_dims(fn, dm, L))) return rc;
+  H3K_CHECK_PTR(x);
+  H3K_CHECK_PTR(ws);
+  if (steps < 1 || reuse < 1 || core_reuse < 1)
+    return fail(H3K_EINVAL, "%s: steps, reuse and core_reuse must be >= 1", fn);
+  if (layers < 1 || layers > n_blocks)
+    return fail(H3K_EINVAL, "%s: need 1 <= layers <= n_blocks", fn);
+  if (tr_begin < 0 || tr_end < tr_begin || tr_end > layers)
+    return fail(H3K_EINVAL, "%s: need 0 <= tr_begin <= tr_end <= layers", fn);
+  const size_t need = h3k_denoise_workspace_bytes(dm, L, tr_begin, tr_end, flags);
+  if (ws_bytes < need) return fail(H3K_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
+  const size_t sw = h3k_stack_workspace_bytes(dm, L, tr_begin, tr_end, flags);
+  const int64_t n = L * dm->d;
+  uint8_t *y = (uint8_t *)ws + sw;
+  float *v = (float *)(y + up256((size_t)n * (f32 ? 4 : 2)));
+  float *r = (float *)((uint8_t *)v + up256((size_t)n * 4));
+  const float dt = -1.0f / (float)steps;
+  int fresh = 0;
+  for (int k = 0; k < steps; ++k) {
+    const bool last = k == steps - 1;
+    if (k % reuse == 0 || last) {
+      hipError_t e;
+      if (fresh % core_reuse == 0 || last) {
+        if ((rc = h3k_stack_forward(x, y, cond, blocks, layers, dm, L, tr_begin, tr_end, flags, ws,
+                                    sw, stream)))
+          return rc;
+        e = launch_sampler(SAMPLER_FRESH, x, y, v, r, dt, n, f32, s);
+      } else {
+        e = launch_sampler(SAMPLER_REUSED, x, nullptr, v, r, dt, n, f32, s);
+      }
+      if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+      ++fresh;
+    }
+    hipError_t e = launch_sampler(SAMPLER_EULER, x, nullptr, v, r, dt, n, f32, s);
+    if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  }
+  return H3K_OK;
+}
+
 struct h3k_graph_s {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;

@@ -79,6 +79,10 @@ hipError_t launch_token_pair(const void *x, void *xr, void *xr2, bool f32, int T
                              int Wg, int d, hipStream_t s);
 hipError_t launch_token_unpair(void *x, const void *xo, const void *xi, bool f32, int T,
                                int Hg, int Wg, int d, hipStream_t s);
+// denoising-loop element steps (see k_rows.hip); n % 8 == 0
+enum SamplerMode { SAMPLER_FRESH = 0, SAMPLER_REUSED = 1, SAMPLER_EULER = 2 };
+hipError_t launch_sampler(int mode, void *x, const void *y, float *v, float *r, float dt,
+                          int64_t n, bool f32, hipStream_t s);
 // dst = src, n16 16-byte chunks (both 16-byte aligned)
 hipError_t launch_copy16(void *dst, const void *src, int64_t n16, hipStream_t s);
 

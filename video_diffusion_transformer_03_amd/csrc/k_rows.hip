@@ -419,4 +419,55 @@ hipError_t launch_copy16(void *dst, const void *src, int64_t n16, hipStream_t s)
   return hipGetLastError();
 }
 
+// Denoising-loop element steps, one thread per 8 elements of [L, d]; x and y (the stack
+// output) in the activation type T, v (velocity) and r (cached core residual) fp32:
+//   SAMPLER_FRESH    r = y - x, v = y
+//   SAMPLER_REUSED   v = x + r
+//   SAMPLER_EULER    x = x + dt * v (rounded to T)
+template <typename T>
+__global__ __launch_bounds__(256) void sampler_kernel(int mode, T *__restrict__ x,
+                                                      const T *__restrict__ y, float *__restrict__ v,
+                                                      float *__restrict__ r, float dt, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t o = i * 8;
+  float xs[8];
+  load8(x + o, xs);
+  if (mode == SAMPLER_FRESH) {
+    float ys[8];
+    load8(y + o, ys);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      r[o + t] = ys[t] - xs[t];
+      v[o + t] = ys[t];
+    }
+  } else if (mode == SAMPLER_REUSED) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[o + t] = xs[t] + r[o + t];
+  } else {
+    float out[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) out[t] = xs[t] + dt * v[o + t];
+    if constexpr (sizeof(T) == 2) {
+      *(uint4 *)(x + o) = make_uint4(pack_bf2(out[0], out[1]), pack_bf2(out[2], out[3]),
+                                     pack_bf2(out[4], out[5]), pack_bf2(out[6], out[7]));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) x[o + t] = out[t];
+    }
+  }
+}
+
+hipError_t launch_sampler(int mode, void *x, const void *y, float *v, float *r, float dt,
+                          int64_t n, bool f32, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  dim3 grid((unsigned)((n8 + 255) / 256));
+  if (f32)
+    sampler_kernel<float><<<grid, 256, 0, s>>>(mode, (float *)x, (const float *)y, v, r, dt, n8);
+  else
+    sampler_kernel<uint16_t><<<grid, 256, 0, s>>>(mode, (uint16_t *)x, (const uint16_t *)y, v, r,
+                                                  dt, n8);
+  return hipGetLastError();
+}
+
 }  // namespace h3k

@@ -81,6 +81,9 @@ def lib() -> C.CDLL:
             "h3k_token_pair": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, i32, vp]),
             "h3k_token_unpair": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, i32, vp]),
             "h3k_last_error": (C.c_char_p, []),
+            "h3k_denoise_workspace_bytes": (sz, [C.POINTER(Dims), i64, i32, i32, u32]),
+            "h3k_denoise": (C.c_int, [vp, vp, C.POINTER(BlockWeightsC), i32, C.POINTER(Dims), i64,
+                                      i32, i32, i32, i32, i32, i32, u32, vp, sz, vp]),
             "h3k_stack_graph_create": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), i32,
                                                  C.POINTER(Dims), i64, i32, i32, u32, vp, sz, vp,
                                                  C.POINTER(vp)]),
@@ -278,6 +281,26 @@ def stack_forward(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWei
                                    C.byref(dims), L, tr_begin, tr_end, flags, _dev(ws, "ws"),
                                    ws.numel(), _stream(stream)))
     return out
+
+
+def denoise_workspace_bytes(dims: Dims, L: int, tr_begin: int = 0, tr_end: int = 0, flags: int = 0) -> int:
+    return lib().h3k_denoise_workspace_bytes(C.byref(dims), L, tr_begin, tr_end, flags)
+
+
+def denoise(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWeights], dims: Dims,
+            steps: int, reuse: int = 1, core_reuse: int = 1, layers: Optional[int] = None,
+            tr_begin: int = 0, tr_end: int = 0, flags: int = 0,
+            ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h3k_denoise: `steps` Euler steps on x in place (x: [L, d] noise in, result out)."""
+    L = x.shape[0]
+    layers = len(blocks) if layers is None else layers
+    if ws is None:
+        ws = alloc_workspace(denoise_workspace_bytes(dims, L, tr_begin, tr_end, flags), x.device)
+    arr = (BlockWeightsC * len(blocks))(*[b.c_struct() for b in blocks])
+    _check(lib().h3k_denoise(_dev(x, "x"), _dev(cond, "cond"), arr, len(blocks), C.byref(dims), L,
+                             steps, reuse, core_reuse, layers, tr_begin, tr_end, flags,
+                             _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    return x
 
 
 class StackGraph:
