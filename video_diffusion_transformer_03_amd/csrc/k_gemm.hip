@@ -55,25 +55,40 @@ __device__ __forceinline__ void store1(void *base, int64_t idx, float y) {
     ((uint16_t *)base)[idx] = f2bf(y);
 }
 
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+// erf without branches: Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26, erf(x) = 1 - (a1 t + ... + a5 t^5) e^(-x^2), t = 1 / (1 + p x) for x >= 0, odd in
+// x; absolute error <= 1.5e-7 (about one fp32 ulp of 1), with the hardware reciprocal and
+// exp2 adding about an ulp each.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
 }
 
-// rotation (cos, sin) of pair i of head_dim for token l
-__device__ __forceinline__ float2 rope_cs(const float2 *tbl, const RopeGeom &g, int i,
-                                          int64_t l) {
+// exact (erf) GELU, x * Phi(x)
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f));
+}
+
+// Table offsets of token l's three axes: pair i of head_dim turns by tbl[ofs.x + i] (i < Pt),
+// tbl[ofs.y + i] (Pt <= i < Pt + Ph) or tbl[ofs.z + i] (the rest); the pair-index bases are
+// folded into the offsets.
+__device__ __forceinline__ int3 rope_offsets(const RopeGeom &g, int64_t l) {
   const int hw = g.Hg * g.Wg;
   const int t = (int)(l / hw);
   const int rem = (int)(l - (int64_t)t * hw);
   const int h = rem / g.Wg;
   const int w = rem - h * g.Wg;
-  int e;
-  if (i < g.Pt)
-    e = t * g.Pt + i;
-  else if (i < g.Pt + g.Ph)
-    e = g.base_h + h * g.Ph + (i - g.Pt);
-  else
-    e = g.base_w + w * g.Pw + (i - g.Pt - g.Ph);
+  return make_int3(t * g.Pt, g.base_h + h * g.Ph - g.Pt, g.base_w + w * g.Pw - g.Pt - g.Ph);
+}
+__device__ __forceinline__ float2 rope_cs(const float2 *tbl, const RopeGeom &g, int i, int3 ofs) {
+  const int e = i < g.Pt ? ofs.x + i : (i < g.Pt + g.Ph ? ofs.y + i : ofs.z + i);
   return tbl[e];
 }
 
@@ -110,6 +125,14 @@ __device__ __forceinline__ void tile_origin(const GemmArgs &a, int64_t &m0, int 
 template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
                                               int n_base, int64_t m_base, int lane) {
+  int3 rofs[TM];  // RoPE table offsets of the lane's token in each 16-row tile (QKV only)
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int64_t m = m_base + j * 16 + (lane & 15);
+      rofs[j] = rope_offsets(a.rg, m < a.M ? m : a.M - 1);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
     const int n = n_base + i * 16 + (lane >> 4) * 4;
@@ -145,7 +168,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
           if (sec < 2) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const float2 cs = rope_cs(a.rope, a.rg, dh / 2 + p, m);
+              const float2 cs = rope_cs(a.rope, a.rg, dh / 2 + p, rofs[j]);
               const float u0 = y[2 * p], u1 = y[2 * p + 1];
               y[2 * p] = u0 * cs.x - u1 * cs.y;
               y[2 * p + 1] = u0 * cs.y + u1 * cs.x;
@@ -214,7 +237,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
   using AccT = typename std::conditional<BF16, v4f, v4i>::type;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index made visibly uniform so that branches on the group are scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, wq = wave & 3;
 
   int64_t m0;
@@ -225,26 +249,34 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
 
   // global -> LDS copies: wave w copies the 8-row groups w, w + 8, w + 16, w + 24 of the
   // weight tile and of the token tile in every stage. Token rows past M read row M - 1:
-  // they only feed accumulator rows that are never stored.
+  // they only feed accumulator rows that are never stored. The copies are buffer loads
+  // (MUBUF) from resources based at the tile's first row, so 32-bit offsets suffice and
+  // they count only in vmcnt.
   const int cr = lane >> 3, cc = (lane & 7) ^ cr;
-  const uint8_t *gB = (const uint8_t *)a.B + (int64_t)(n0 + wave * 8 + cr) * Kb + cc * 16;
-  const uint8_t *gA[4];
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const uint8_t *)a.B + (int64_t)n0 * Kb), (short)0, (int)0xffffffffu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((const uint8_t *)a.A + m0 * Kb), (short)0, (int)0xffffffffu, 0x00020000);
+  const uint32_t oB = (uint32_t)((wave * 8 + cr) * Kb + cc * 16);
+  uint32_t oA[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t m = m0 + (wave + 8 * q) * 8 + cr;
-    gA[q] = (const uint8_t *)a.A + (m < a.M ? m : a.M - 1) * Kb + cc * 16;
+    oA[q] = (uint32_t)(((m < a.M ? m : a.M - 1) - m0) * Kb + cc * 16);
   }
-  const int64_t gB_q = 64 * Kb;  // 8 row groups further down the weight tile
+  const uint32_t oB_q = (uint32_t)(64 * Kb);  // 8 row groups further down the weight tile
 #define H3K_PP_COPY(s_)                                                                     \
   {                                                                                         \
-    const int64_t ko = (int64_t)(s_) * PP_SB;                                               \
+    const uint32_t ko = (uint32_t)(s_) * PP_SB;                                             \
     uint8_t *dst = smem + ((s_) & 1) * PP_STAGE + wave * 1024;                              \
     _Pragma("unroll") for (int q = 0; q < 4; ++q)                                           \
-      __builtin_amdgcn_global_load_lds(gB + q * gB_q + ko,                                  \
-          (__attribute__((address_space(3))) void *)(dst + q * 8192), 16, 0, 0);            \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs,                                         \
+          (__attribute__((address_space(3))) void *)(dst + q * 8192), 16,                   \
+          oB + q * oB_q + ko, 0, 0, 0);                                                     \
     _Pragma("unroll") for (int q = 0; q < 4; ++q)                                           \
-      __builtin_amdgcn_global_load_lds(gA[q] + ko,                                          \
-          (__attribute__((address_space(3))) void *)(dst + 32768 + q * 8192), 16, 0, 0);    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars,                                         \
+          (__attribute__((address_space(3))) void *)(dst + 32768 + q * 8192), 16,           \
+          oA[q] + ko, 0, 0, 0);                                                             \
   }
 
   AccT acc[TN][TM];
@@ -294,10 +326,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     H3K_PP_SYNC();
     H3K_PP_MFMA();
-    // Group 1's last compute phase needs no closing barrier (no LDS access follows), which
-    // leaves both groups with the same barrier count; group 0 closes its last compute phase
-    // at the instance that ends group 1's last memory phase, then runs its epilogue while
-    // group 1 computes.
     if (st + 1 < ns || grp == 0) H3K_PP_SYNC();
   }
 
