@@ -34,21 +34,6 @@ constexpr int waitcnt_vm_lgkm0(int vm) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
-// max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of the wave) with
-// gfx950 row swaps in registers; a shuffle (__shfl_xor) would go through LDS
-// (ds_bpermute) and wait for every outstanding LDS read.
-__device__ __forceinline__ float rows_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
 
 #ifndef H3K_ATTN_OCC
 #define H3K_ATTN_OCC 2  // waves per SIMD the register budget is sized for

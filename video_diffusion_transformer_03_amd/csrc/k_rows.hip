@@ -141,6 +141,26 @@ __device__ __forceinline__ void load8(const float *p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+// streaming variants for inputs read exactly once (nontemporal: no cache allocation)
+__device__ __forceinline__ void load8_nt(const uint16_t *p, float v[8]) {
+  const v4u u = __builtin_nontemporal_load((const v4u *)p);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[2 * t] = __uint_as_float(u[t] << 16);
+    v[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_nt(const float *p, float v[8]) {
+  const v4f a = __builtin_nontemporal_load((const v4f *)p);
+  const v4f b = __builtin_nontemporal_load((const v4f *)(p + 4));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[t] = a[t];
+    v[4 + t] = b[t];
+  }
+}
+
 template <int WPR>
 __device__ __forceinline__ float group_reduce(float v, bool is_max, float *red) {
   v = is_max ? wave_max(v) : wave_sum(v);
@@ -183,7 +203,10 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
   for (int i = 0; i < MAXV; ++i) {
     int c = tid + i * NT;
     if (active && c < nvec) {
-      load8(xr + (int64_t)c * 8, v[i]);
+      if constexpr (MODE == RM_Q)  // O and g are read once
+        load8_nt(xr + (int64_t)c * 8, v[i]);
+      else
+        load8(xr + (int64_t)c * 8, v[i]);
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) v[i][t] = 0.f;
