@@ -120,79 +120,142 @@ __device__ __forceinline__ void tile_origin(const GemmArgs &a, int64_t &m0, int 
   n0 = (int)(in_group / gsize) * BN;
 }
 
+// Per-column-block operands of the epilogue (one 16-channel block i of a wave's tile),
+// loaded ahead of use so that the global-memory latency of one block overlaps the
+// arithmetic and stores of the blocks before it. Fields an epilogue does not use are never
+// touched and take no registers.
+template <int TM, bool RESF32>
+struct EpiChunk {
+  float sw[4];                  // weight scales of the lane's 4 channels
+  float g[4];                   // gate (RESID)
+  uint32_t r[TM][RESF32 ? 4 : 2];  // residual bits, fp32 or packed bf16 (RESID)
+  float2 cs[TM][2];             // RoPE (cos, sin) of the lane's two channel pairs (QKV)
+};
+
 // Epilogue of one wave's TN x TM block of 16x16 accumulator tiles. acc[i][j][r] = C[m][n]
 // with m = token m_base + 16 j + (lane & 15) and n = channel n_base + 16 i + 4 (lane >> 4) + r.
+// Loads use token rows clamped to M - 1; only the stores test m < M. Every element is read
+// and written by the same lane, so an output that aliases the residual stays correct.
 template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
                                               int n_base, int64_t m_base, int lane) {
+  constexpr int PF = 2;  // column blocks loaded ahead
+  int64_t mrow[TM];
+  bool mval[TM];
+  float sa[TM];
   int3 rofs[TM];  // RoPE table offsets of the lane's token in each 16-row tile (QKV only)
-  if constexpr (EPI == EPI_QKV) {
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int64_t m = m_base + j * 16 + (lane & 15);
-      rofs[j] = rope_offsets(a.rg, m < a.M ? m : a.M - 1);
-    }
+  for (int j = 0; j < TM; ++j) {
+    const int64_t m = m_base + j * 16 + (lane & 15);
+    mval[j] = m < a.M;
+    mrow[j] = mval[j] ? m : a.M - 1;
+    sa[j] = 1.f;
+    if constexpr (!BF16 && EPI != EPI_RAW_I32) sa[j] = a.sa[mrow[j]];
+    if constexpr (EPI == EPI_QKV) rofs[j] = rope_offsets(a.rg, mrow[j]);
   }
-#pragma unroll
-  for (int i = 0; i < TN; ++i) {
+
+  auto load_chunk = [&](EpiChunk<TM, RESF32> &c, int i) {
     const int n = n_base + i * 16 + (lane >> 4) * 4;
-    float sw[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (!BF16 && EPI != EPI_RAW_I32) {
-      float4 t4 = *(const float4 *)(a.sw + n);
-      sw[0] = t4.x; sw[1] = t4.y; sw[2] = t4.z; sw[3] = t4.w;
+      const float4 t4 = *(const float4 *)(a.sw + n);
+      c.sw[0] = t4.x; c.sw[1] = t4.y; c.sw[2] = t4.z; c.sw[3] = t4.w;
     }
+    if constexpr (EPI == EPI_RESID) {
+      const float4 g4 = *(const float4 *)(a.gate + n);
+      c.g[0] = g4.x; c.g[1] = g4.y; c.g[2] = g4.z; c.g[3] = g4.w;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        if constexpr (RESF32) {
+          const uint4 u = *(const uint4 *)((const float *)a.res + mrow[j] * a.N + n);
+          c.r[j][0] = u.x; c.r[j][1] = u.y; c.r[j][2] = u.z; c.r[j][3] = u.w;
+        } else {
+          const uint2 u = *(const uint2 *)((const uint16_t *)a.res + mrow[j] * a.N + n);
+          c.r[j][0] = u.x; c.r[j][1] = u.y;
+        }
+      }
+    }
+    if constexpr (EPI == EPI_QKV) {
+      const int sec = n / a.d;
+      const int dh = (n - sec * a.d) % a.Dh;
+      if (sec < 2) {
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) c.cs[j][p] = rope_cs(a.rope, a.rg, dh / 2 + p, rofs[j]);
+      }
+    }
+  };
+
+  auto store_chunk = [&](const EpiChunk<TM, RESF32> &c, int i) {
+    const int n = n_base + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int64_t m = m_base + j * 16 + (lane & 15);
-      if (m >= a.M) continue;
+      const int64_t m = mrow[j];
       if constexpr (EPI == EPI_RAW_I32) {
         if constexpr (!BF16) {
-          v4i v = acc[i][j];
-          *(int4 *)(a.c32 + m * a.N + n) = make_int4(v[0], v[1], v[2], v[3]);
+          const v4i v = acc[i][j];
+          if (mval[j]) *(int4 *)(a.c32 + m * a.N + n) = make_int4(v[0], v[1], v[2], v[3]);
         }
       } else {
         float y[4];
-        if constexpr (BF16) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = acc[i][j][r];
-        } else {
-          const float sa = a.sa[m];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = ((float)acc[i][j][r] * sa) * sw[r];
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (BF16)
+            y[r] = acc[i][j][r];
+          else
+            y[r] = ((float)acc[i][j][r] * sa[j]) * c.sw[r];
         }
         if constexpr (EPI == EPI_QKV) {
           const int sec = n / a.d;
-          const int c = n - sec * a.d;
-          const int head = c / a.Dh;
-          const int dh = c - head * a.Dh;
+          const int cc = n - sec * a.d;
+          const int head = cc / a.Dh;
+          const int dh = cc - head * a.Dh;
           if (sec < 2) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const float2 cs = rope_cs(a.rope, a.rg, dh / 2 + p, rofs[j]);
+              const float2 cs = c.cs[j][p];
               const float u0 = y[2 * p], u1 = y[2 * p + 1];
               y[2 * p] = u0 * cs.x - u1 * cs.y;
               y[2 * p + 1] = u0 * cs.y + u1 * cs.x;
             }
-            store4<OUTF32>(sec == 0 ? a.q : a.k, ((int64_t)head * a.M + m) * a.Dh + dh, y[0],
-                           y[1], y[2], y[3]);
-          } else {
+            if (mval[j])
+              store4<OUTF32>(sec == 0 ? a.q : a.k, ((int64_t)head * a.M + m) * a.Dh + dh, y[0],
+                             y[1], y[2], y[3]);
+          } else if (mval[j]) {
             const int64_t base = ((int64_t)head * a.Dh + dh) * a.M + m;
 #pragma unroll
             for (int r = 0; r < 4; ++r) store1<OUTF32>(a.vt, base + (int64_t)r * a.M, y[r]);
           }
         } else if constexpr (EPI == EPI_GELU) {
-          store4<OUTF32>(a.out, m * a.N + n, gelu_erf(y[0]), gelu_erf(y[1]), gelu_erf(y[2]),
-                         gelu_erf(y[3]));
+          if (mval[j])
+            store4<OUTF32>(a.out, m * a.N + n, gelu_erf(y[0]), gelu_erf(y[1]), gelu_erf(y[2]),
+                           gelu_erf(y[3]));
         } else if constexpr (EPI == EPI_RESID) {
           float r4[4];
-          load4<RESF32>(a.res, m * a.N + n, r4);
-          const float4 g4 = *(const float4 *)(a.gate + n);
-          store4<OUTF32>(a.out, m * a.N + n, r4[0] + g4.x * y[0], r4[1] + g4.y * y[1],
-                         r4[2] + g4.z * y[2], r4[3] + g4.w * y[3]);
+          if constexpr (RESF32) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) r4[r] = __uint_as_float(c.r[j][r]);
+          } else {
+            r4[0] = __uint_as_float(c.r[j][0] << 16);
+            r4[1] = __uint_as_float(c.r[j][0] & 0xffff0000u);
+            r4[2] = __uint_as_float(c.r[j][1] << 16);
+            r4[3] = __uint_as_float(c.r[j][1] & 0xffff0000u);
+          }
+          if (mval[j])
+            store4<OUTF32>(a.out, m * a.N + n, r4[0] + c.g[0] * y[0], r4[1] + c.g[1] * y[1],
+                           r4[2] + c.g[2] * y[2], r4[3] + c.g[3] * y[3]);
         }
       }
     }
-  }
+  };
+
+  EpiChunk<TM, RESF32> buf[PF + 1];
+  static_for<PF>([&](auto I) { load_chunk(buf[I], I); });
+  static_for<TN>([&](auto I) {
+    constexpr int i = I;
+    if constexpr (i + PF < TN) load_chunk(buf[(i + PF) % (PF + 1)], i + PF);
+    store_chunk(buf[i % (PF + 1)], i);
+  });
 }
 
 // ------------------------------------------------------------------ ping-pong kernel
