@@ -101,15 +101,16 @@ __device__ __forceinline__ auto mma(v4i b, v4i a, typename std::conditional<BF16
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a, c, 0, 0, 0);
 }
 
-// Work-group tile origin. The work-groups the hardware places on one XCD (bid % 8) get a
-// contiguous range of logical tiles, walked in groups of 8 M-tiles so that concurrent
-// work-groups of an XCD share weight and activation tiles in that XCD's L2.
+// Origin of tile t. The hardware places work-group b on XCD b % 8, and a persistent
+// work-group b takes tiles b, b + G, b + 2G, ... (G, the grid, a multiple of 8 or the tile
+// count), so t % 8 is the XCD. Each XCD gets a contiguous range of logical tiles, walked in
+// groups of 8 M-tiles so that concurrent work-groups of an XCD share weight and activation
+// tiles in that XCD's L2.
 template <int BN, int BM>
-__device__ __forceinline__ void tile_origin(const GemmArgs &a, int64_t &m0, int &n0) {
+__device__ __forceinline__ void tile_origin(const GemmArgs &a, int64_t t, int64_t &m0, int &n0) {
   const int n_tiles = a.N / BN;
   const int64_t m_tiles = (a.M + BM - 1) / BM;
   const int64_t nwg = (int64_t)n_tiles * m_tiles;
-  int64_t t = blockIdx.x;
   if ((nwg & 7) == 0) t = (t & 7) * (nwg >> 3) + (t >> 3);
   constexpr int GM = 8;
   const int64_t group = t / ((int64_t)GM * n_tiles);
@@ -139,7 +140,7 @@ struct EpiChunk {
 template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
                                               int n_base, int64_t m_base, int lane) {
-  constexpr int PF = 2;  // column blocks loaded ahead
+  constexpr int PF = (EPI == EPI_QKV || RESF32) ? 1 : 2;  // column blocks loaded ahead
   int64_t mrow[TM];
   bool mval[TM];
   float sa[TM];
@@ -304,9 +305,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, wq = wave & 3;
 
+  const int64_t ntiles = (int64_t)(a.N / 256) * ((a.M + 255) / 256);
+  int64_t t = blockIdx.x;
   int64_t m0;
   int n0;
-  tile_origin<256, 256>(a, m0, n0);
+  tile_origin<256, 256>(a, t, m0, n0);
   const int64_t Kb = (int64_t)a.K * (BF16 ? 2 : 1);
   const int ns = (int)(Kb / PP_SB);  // stages
 
@@ -316,38 +319,39 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
   // (MUBUF) from resources based at the tile's first row, so 32-bit offsets suffice and
   // they count only in vmcnt.
   const int cr = lane >> 3, cc = (lane & 7) ^ cr;
-  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const uint8_t *)a.B + (int64_t)n0 * Kb), (short)0, (int)0xffffffffu, 0x00020000);
-  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const uint8_t *)a.A + m0 * Kb), (short)0, (int)0xffffffffu, 0x00020000);
   const uint32_t oB = (uint32_t)((wave * 8 + cr) * Kb + cc * 16);
-  uint32_t oA[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t m = m0 + (wave + 8 * q) * 8 + cr;
-    oA[q] = (uint32_t)(((m < a.M ? m : a.M - 1) - m0) * Kb + cc * 16);
-  }
   const uint32_t oB_q = (uint32_t)(64 * Kb);  // 8 row groups further down the weight tile
-#define H3K_PP_COPY(s_)                                                                     \
+  __amdgpu_buffer_rsrc_t brs, ars;
+  uint32_t oA[4];
+  auto tile_copy_setup = [&](int64_t tm0, int tn0, __amdgpu_buffer_rsrc_t &b_rs,
+                             __amdgpu_buffer_rsrc_t &a_rs, uint32_t (&o_a)[4]) {
+    b_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const uint8_t *)a.B + (int64_t)tn0 * Kb), (short)0, (int)0xffffffffu, 0x00020000);
+    a_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const uint8_t *)a.A + tm0 * Kb), (short)0, (int)0xffffffffu, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t m = tm0 + (wave + 8 * q) * 8 + cr;
+      o_a[q] = (uint32_t)(((m < a.M ? m : a.M - 1) - tm0) * Kb + cc * 16);
+    }
+  };
+  tile_copy_setup(m0, n0, brs, ars, oA);
+#define H3K_PP_COPY_WITH(s_, b_rs, a_rs, o_a)                                               \
   {                                                                                         \
     const uint32_t ko = (uint32_t)(s_) * PP_SB;                                             \
     uint8_t *dst = smem + ((s_) & 1) * PP_STAGE + wave * 1024;                              \
     _Pragma("unroll") for (int q = 0; q < 4; ++q)                                           \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs,                                         \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs,                                        \
           (__attribute__((address_space(3))) void *)(dst + q * 8192), 16,                   \
           oB + q * oB_q + ko, 0, 0, 0);                                                     \
     _Pragma("unroll") for (int q = 0; q < 4; ++q)                                           \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars,                                         \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs,                                        \
           (__attribute__((address_space(3))) void *)(dst + 32768 + q * 8192), 16,           \
-          oA[q] + ko, 0, 0, 0);                                                             \
+          o_a[q] + ko, 0, 0, 0);                                                            \
   }
+#define H3K_PP_COPY(s_) H3K_PP_COPY_WITH(s_, brs, ars, oA)
 
   AccT acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = AccT{0, 0, 0, 0};
-
   // fragments of one step: weight rows 128 grp + 16 i, token rows 64 wq + 16 j
   v4i fb[TN], fa[TM];
   const int frag_off = (lane & 15) * PP_SB + (((lane >> 4) ^ (lane & 7)) * 16);
@@ -365,39 +369,84 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
     _Pragma("unroll") for (int j = 0; j < TM; ++j) acc[i][j] = mma<BF16>(fb[i], fa[j], acc[i][j]); \
   }
 
-  // Step k = 2 s + h reads stage s (buffer s % 2). Barrier instances are counted after the
-  // prologue's: instance 2k + 1 ends group 0's memory phase of step k and group 1's compute
-  // phase of step k - 1; instance 2k + 2 ends group 0's compute phase of step k and group
-  // 1's memory phase of step k.
+  // Step k = 2 s + h reads stage s (buffer s % 2). Barrier instances are counted from the
+  // tile's first one: instance 2k + 1 ends group 0's memory phase of step k and group 1's
+  // compute phase of step k - 1; instance 2k + 2 ends group 0's compute phase of step k and
+  // group 1's memory phase of step k.
   //  - The copies of stage s + 1 are issued in the memory phase of step 2 s: buffer (s + 1) % 2
   //    last held stage s - 1, whose last reader (group 1, step 2 s - 1) passed instance 4 s.
   //  - Each wave waits for its own copies at the end of its memory phase of step 2 s + 1, at
   //    the latest instance 4 s + 4, before which nobody reads stage s + 1.
+  //  - After instance 4 ns every read of the tile's stages is complete, so both groups copy
+  //    stage 0 of their next tile into buffer 0 before their epilogue; the epilogue's
+  //    global-memory latency then covers that copy's.
   H3K_PP_COPY(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
-  H3K_PP_SYNC();
-  if (grp) H3K_PP_SYNC();
-
-  for (int st = 0; st < ns; ++st) {
-    if (st + 1 < ns) H3K_PP_COPY(st + 1);
-    H3K_PP_READ(st, 0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-    H3K_PP_SYNC();
-    H3K_PP_MFMA();
-    H3K_PP_SYNC();
-    H3K_PP_READ(st, 1);
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] = AccT{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     H3K_PP_SYNC();
-    H3K_PP_MFMA();
-    if (st + 1 < ns || grp == 0) H3K_PP_SYNC();
-  }
+    if (grp) H3K_PP_SYNC();
 
-  gemm_epilogue<TN, TM, BF16, EPI, OUTF32, RESF32>(a, acc, n0 + grp * TN * 16,
-                                                 m0 + wq * TM * 16, lane);
+    for (int st = 0; st < ns; ++st) {
+      if (st + 1 < ns) H3K_PP_COPY(st + 1);
+      H3K_PP_READ(st, 0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+      H3K_PP_SYNC();
+      H3K_PP_MFMA();
+      H3K_PP_SYNC();
+      H3K_PP_READ(st, 1);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      H3K_PP_SYNC();
+      H3K_PP_MFMA();
+      // Group 1's last compute phase needs no closing barrier (no LDS access follows), which
+      // leaves both groups with the same barrier count; group 0 closes its last compute
+      // phase at the instance that ends group 1's last memory phase, then runs its epilogue
+      // while group 1 computes.
+      if (st + 1 < ns || grp == 0) H3K_PP_SYNC();
+    }
+
+    const int64_t tn = t + gridDim.x;
+    const bool more = tn < ntiles;
+    int64_t m0n = 0;
+    int n0n = 0;
+    if (more) {
+      tile_origin<256, 256>(a, tn, m0n, n0n);
+      tile_copy_setup(m0n, n0n, brs, ars, oA);
+      H3K_PP_COPY(0);
+    }
+    gemm_epilogue<TN, TM, BF16, EPI, OUTF32, RESF32>(a, acc, n0 + grp * TN * 16,
+                                                   m0 + wq * TM * 16, lane);
+    if (!more) break;
+    t = tn;
+    m0 = m0n;
+    n0 = n0n;
+  }
 }
 #undef H3K_PP_COPY
+#undef H3K_PP_COPY_WITH
 #undef H3K_PP_READ
 #undef H3K_PP_MFMA
+
+// compute units of the current device, queried once per device
+static hipError_t compute_units(int *n) {
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (cached[dev] == 0) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (v <= 0) return hipErrorInvalidValue;
+    cached[dev] = v;
+  }
+  *n = cached[dev];
+  return hipSuccess;
+}
 
 template <bool BF16, int EPI, bool OUTF32, bool RESF32>
 static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
@@ -410,8 +459,14 @@ static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  // persistent: one work-group per compute unit (the LDS footprint allows one), each
+  // walking tiles b, b + grid, ...
   const int64_t nwg = ((a.M + 255) / 256) * (a.N / 256);
-  kern<<<dim3((unsigned)nwg), dim3(512), lds, s>>>(a);
+  int n_cu = 0;
+  if (hipError_t e = compute_units(&n_cu); e != hipSuccess) return e;
+  const int64_t full = n_cu >= 8 ? (n_cu & ~7) : n_cu;  // keeps tile % 8 == XCD
+  const int64_t grid = nwg < full ? nwg : full;
+  kern<<<dim3((unsigned)grid), dim3(512), lds, s>>>(a);
   return hipGetLastError();
 }
 
