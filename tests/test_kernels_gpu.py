@@ -88,7 +88,10 @@ def test_row_quantize(rows, cols, dtype):
 
 # ----------------------------------------------------------------------------- int8 GEMM
 @pytest.mark.parametrize("M,N,K", [(1, 256, 128), (100, 768, 640), (1000, 512, 5120),
-                                   (4096, 1536, 1024), (333, 256, 20480)])
+                                   (4096, 1536, 1024), (333, 256, 20480),
+                                   # more tiles than compute units: work-groups walk several
+                                   # tiles, the last M-tile ragged
+                                   (4100, 4352, 256), (8200, 4096, 128)])
 def test_gemm_i8_exact(M, N, K):
     g = _gen(M * 7 + N)
     a = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int8)
