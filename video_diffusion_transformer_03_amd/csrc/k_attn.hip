@@ -35,22 +35,16 @@ constexpr int waitcnt_vm_lgkm0(int vm) {
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *(const uint4 *)p; }
 
 
-#ifndef H3K_ATTN_OCC
-#define H3K_ATTN_OCC 2  // waves per SIMD the register budget is sized for
-#endif
-#ifndef H3K_ATTN_KPAD
-#define H3K_ATTN_KPAD 16  // elements of padding per K-tile row in LDS
-#endif
-#ifndef H3K_ATTN_VPAD
-#define H3K_ATTN_VPAD 16  // elements of padding per V^T-tile row in LDS
-#endif
+constexpr int kAttnOcc = 2;   // waves per SIMD the register budget is sized for
+constexpr int kAttnKPad = 16;  // elements of padding per K-tile row in LDS
+constexpr int kAttnVPad = 16;  // elements of padding per V^T-tile row in LDS
 
 template <int DH>
 struct AttnCfg {
   static constexpr int BQ = 128;                  // queries per work-group (4 waves x 32)
   static constexpr int BK = 64;                   // keys per tile
-  static constexpr int KP = DH + H3K_ATTN_KPAD;   // K tile row pitch (elements)
-  static constexpr int VP = BK + H3K_ATTN_VPAD;   // V^T tile row pitch (elements)
+  static constexpr int KP = DH + kAttnKPad;   // K tile row pitch (elements)
+  static constexpr int VP = BK + kAttnVPad;   // V^T tile row pitch (elements)
   static constexpr int K_ELEMS = BK * KP;
   static constexpr int V_ELEMS = DH * VP;
   static constexpr size_t LDS = (size_t)2 * (K_ELEMS + V_ELEMS) * 2;
@@ -171,7 +165,7 @@ __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH 
 }
 
 template <int DH, bool OF32>
-__global__ __launch_bounds__(256, H3K_ATTN_OCC) void attn_bf16_kernel(
+__global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ Vt, void *__restrict__ Ov, int H, int64_t L, float sl2) {
   using C = AttnCfg<DH>;
@@ -425,13 +419,7 @@ __device__ __forceinline__ bool rescale_decision(bool grow, const float (&mnew)[
   return true;
 }
 
-#ifndef H3K_ATTN_DMA
-#define H3K_ATTN_DMA 1  // K/V tiles by global -> LDS copies (1) or through registers (0)
-#endif
-#ifndef H3K_ATTN_PD
-#define H3K_ATTN_PD 3
-#endif
-constexpr int PD = H3K_ATTN_PD;  // LDS fragment reads issued this many MFMA pairs ahead
+constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
 
 // Phase 1 of an iteration, interleaved by hand in 16 steps (a scheduling barrier ends each
 // step): step i reads K fragment i + PD, issues the two MFMAs of fragment i (S^T tile t4 =
@@ -576,7 +564,7 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 // Buffer (MUBUF) copies rather than global_load_lds: for the latter the compiler assumes a
 // pending copy may also count against lgkmcnt and waits for every outstanding LDS read at
 // each fragment use, which would undo the read-ahead of the phases below. Byte offsets
-// within a head stay below 256 L < 2^32.
+// within a head are at most 256 L - 16, below 2^32 for L <= 2^24 (the entry points' limit).
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -599,28 +587,6 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
           (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * q) * 1024),   \
           16, ((uint32_t)vrow[q] * Lu + col) * 2, 0, 0, 0);                                    \
   }
-  // register-staged alternative: global loads into four 16-byte registers, then ds_write
-  // to the same LDS positions the copies fill
-  uint4 rk0, rk1, rv0, rv1;
-#define H3K_V2_GLOAD(u_)                                                                       \
-  {                                                                                            \
-    const int u = (u_);                                                                        \
-    const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;                               \
-    const uint32_t vt0 = (uint32_t)(u >= 1 ? u - 1 : 0) * BK;                                  \
-    rk0 = ld16(Kh + min(kt0 + (uint32_t)kkey[0], Lu - 1u) * DH + kcol[0]);                     \
-    rk1 = ld16(Kh + min(kt0 + (uint32_t)kkey[1], Lu - 1u) * DH + kcol[1]);                     \
-    const uint32_t col = min(vt0 + (uint32_t)vcol, Lu - 8u);                                   \
-    rv0 = ld16(Vh + (uint32_t)vrow[0] * Lu + col);                                             \
-    rv1 = ld16(Vh + (uint32_t)vrow[1] * Lu + col);                                             \
-  }
-#define H3K_V2_LSTORE(u_)                                                                      \
-  {                                                                                            \
-    uint8_t *dst = smem + ((u_) % NB) * STAGE + wave * 1024 + lane * 16;                       \
-    *(uint4 *)dst = rk0;                                                                       \
-    *(uint4 *)(dst + 8 * 1024) = rk1;                                                          \
-    *(uint4 *)(dst + K_BYTES) = rv0;                                                           \
-    *(uint4 *)(dst + K_BYTES + 8 * 1024) = rv1;                                                \
-  }
   // fragment offsets inside a stage: K row t4*16 + c16, chunk 4kk + g; V^T row dt*16 + c16,
   // chunk 4ks + g (the kk / ks part is applied as an XOR of kk*64 / ks*64)
   const int koff = c16 * 256 + ((g ^ c16) * 16);
@@ -635,27 +601,15 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 
   // prologue: stages 0 .. DIST-1 in flight (past nkt they repeat valid tiles into buffers
   // no later copy targets); S(0) from stage 0, its maximum; then stage 1 for iteration 0
-#if H3K_ATTN_DMA
   static_for<DIST>([&](auto J) { H3K_V2_COPY(J); });
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 1)));
-#else
-  // register staging: stages 0 and 1 in LDS, stage 2 in registers
-  H3K_V2_GLOAD(0);
-  H3K_V2_LSTORE(0);
-  H3K_V2_GLOAD(1);
-  H3K_V2_LSTORE(1);
-  H3K_V2_GLOAD(2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-#endif
   H3K_PP_SYNC();
   s_tile(sa, qf, smem, koff);
   float mnew[2];
   bool pend = max_vals<true>(sa, m, mnew, sl2, g, (int)min((int64_t)BK, L));
   pend = rescale_decision(pend, mnew, m, alpha);
-#if H3K_ATTN_DMA
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));
   H3K_PP_SYNC();
-#endif
 
   // iteration j reads stage j + 1. Its copies of stage j + DIST go to the buffer of stage
   // j + DIST - NB <= j, last read in iteration j - 1 (or the prologue); the wave's copy of
@@ -664,18 +618,14 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #define H3K_V2_ITER(CUR, NXT, j_, MASK)                                                        \
   {                                                                                            \
     const int jj = (j_);                                                                       \
-    if (H3K_ATTN_DMA && jj + DIST <= nkt) H3K_V2_COPY(jj + DIST);                              \
-    if (!H3K_ATTN_DMA && jj + 2 <= nkt) H3K_V2_LSTORE(jj + 2);                                 \
-    if (!H3K_ATTN_DMA && jj + 3 <= nkt) H3K_V2_GLOAD(jj + 3);                                  \
+    if (jj + DIST <= nkt) H3K_V2_COPY(jj + DIST);                                             \
     const uint8_t *sb_ = smem + ((jj + 1) % NB) * STAGE;                                       \
     if (pend) rescale(o, l, alpha);                                                            \
     phase_s_exp(NXT, CUR, pb, qf, sb_, koff, m, l, sl2);                                       \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
     const bool grow_ = phase_pv_max(o, pb, NXT, sb_, voff, m, mnew, sl2);                      \
     pend = rescale_decision(grow_, mnew, m, alpha);                                            \
-    if (!H3K_ATTN_DMA)                                                                         \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));                                        \
-    else if (jj + DIST <= nkt)                                                                 \
+    if (jj + DIST <= nkt)                                                                      \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
     else                                                                                       \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                         \
@@ -712,8 +662,6 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #undef H3K_V2_ITER
 #undef H3K_V2_LAST
 #undef H3K_V2_COPY
-#undef H3K_V2_GLOAD
-#undef H3K_V2_LSTORE
 
   const int64_t ldo = (int64_t)H * DH;
 #pragma unroll
@@ -826,28 +774,26 @@ static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o,
   return hipGetLastError();
 }
 
-#ifndef H3K_ATTN_V2
-#define H3K_ATTN_V2 1
-#endif
-
 template <int DH, bool OF32>
 static hipError_t attn_mfma(const void *q, const void *k, const void *vt, void *o, int H,
                             int64_t L, float sl2, hipStream_t s) {
-  if constexpr (DH == 128 && H3K_ATTN_V2)
-    if (L < (1 << 24)) return attn_v2<OF32>(q, k, vt, o, H, L, sl2, s);
-  using C = AttnCfg<DH>;
-  auto kern = attn_bf16_kernel<DH, OF32>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  if constexpr (DH == 128) {
+    return attn_v2<OF32>(q, k, vt, o, H, L, sl2, s);
+  } else {
+    using C = AttnCfg<DH>;
+    auto kern = attn_bf16_kernel<DH, OF32>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    dim3 grid((unsigned)((L + C::BQ - 1) / C::BQ), (unsigned)H);
+    kern<<<grid, 256, C::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
+                                   (const uint16_t *)vt, o, H, L, sl2);
+    return hipGetLastError();
   }
-  dim3 grid((unsigned)((L + C::BQ - 1) / C::BQ), (unsigned)H);
-  kern<<<grid, 256, C::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
-                                 (const uint16_t *)vt, o, H, L, sl2);
-  return hipGetLastError();
 }
 
 template <int DH>
