@@ -291,7 +291,9 @@ enum {
   H3K_K_TOKEN_PAIR, H3K_K_TOKEN_UNPAIR, H3K_K_COUNT
 };
 /* While enabled, every kernel the block and stack calls launch is bracketed by two HIP
- * events recorded on the call's stream. Enabling clears earlier records. */
+ * events recorded on the call's stream. Enabling clears earlier records. The records are
+ * process-wide and not synchronised: enable, run and read from one thread, with no other
+ * thread calling the library meanwhile. */
 int h3k_profile_enable(int on);
 /* Waits for the recorded events and returns, for kernel kind `kind`, the number of
  * launches recorded and their summed duration in milliseconds. */

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -139,6 +140,21 @@ struct GemmArgs {
   const float *gate;
 };
 hipError_t launch_gemm(EpiKind kind, const GemmArgs &a, hipStream_t s);
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per device
+// (the attribute is per device); `done` holds one bit per device id (< 64).
+inline hipError_t ensure_dynamic_lds(const void *kern, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  const uint64_t bit = (uint64_t)1 << dev;
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  done.fetch_or(bit, std::memory_order_acq_rel);
+  return hipSuccess;
+}
 
 // attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. in_f32: fp32 inputs (plain
 // FMA kernel, fp32 output); otherwise bf16 inputs on the matrix cores with a bf16 or

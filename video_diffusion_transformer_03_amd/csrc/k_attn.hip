@@ -761,13 +761,10 @@ template <bool OF32>
 static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o, int H,
                           int64_t L, float sl2, hipStream_t s) {
   auto kern = attn_v2_kernel<OF32>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)v2::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)v2::LDS, lds_set);
+      e != hipSuccess)
+    return e;
   dim3 grid((unsigned)((L + v2::BQ - 1) / v2::BQ), (unsigned)H);
   kern<<<grid, 512, v2::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
                                   (const uint16_t *)vt, o, H, L, sl2);
@@ -782,13 +779,10 @@ static hipError_t attn_mfma(const void *q, const void *k, const void *vt, void *
   } else {
     using C = AttnCfg<DH>;
     auto kern = attn_bf16_kernel<DH, OF32>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)C::LDS, lds_set);
+        e != hipSuccess)
+      return e;
     dim3 grid((unsigned)((L + C::BQ - 1) / C::BQ), (unsigned)H);
     kern<<<grid, 256, C::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
                                    (const uint16_t *)vt, o, H, L, sl2);

@@ -432,19 +432,19 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
 
 // compute units of the current device, queried once per device
 static hipError_t compute_units(int *n) {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // zero-initialised (static storage)
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cached[dev] == 0) {
-    int v = 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (v <= 0) return hipErrorInvalidValue;
-    cached[dev] = v;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  *n = cached[dev];
+  *n = v;
   return hipSuccess;
 }
 
@@ -452,13 +452,10 @@ template <bool BF16, int EPI, bool OUTF32, bool RESF32>
 static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
   auto kern = gemm_pp_kernel<BF16, EPI, OUTF32, RESF32>;
   constexpr size_t lds = (size_t)2 * PP_STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)lds, lds_set);
+      e != hipSuccess)
+    return e;
   // persistent: one work-group per compute unit (the LDS footprint allows one), each
   // walking tiles b, b + grid, ...
   const int64_t nwg = ((a.M + 255) / 256) * (a.N / 256);
