@@ -187,6 +187,35 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
     }
   };
 
+  // fp32 outputs: column blocks are stored in pairs (i - 1, i), each store instruction
+  // writing 8 rows x 128 contiguous bytes (full lines) after a row_ror:8 exchange
+  float hold[TM][4];
+  auto emit = [&](int i, int j, float (&v)[4]) {
+    if constexpr (OUTF32 && (EPI == EPI_GELU || EPI == EPI_RESID)) {
+      if ((i & 1) == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hold[j][r] = v[r];
+        return;
+      }
+      const bool lo = (lane & 15) < 8;
+      float X[4], Y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = dpp_mov<0x128>(hold[j][r]);
+        const float br = dpp_mov<0x128>(v[r]);
+        X[r] = lo ? hold[j][r] : br;
+        Y[r] = lo ? ar : v[r];
+      }
+      const int nn = n_base + (i - 1) * 16 + (lane >> 4) * 4 + (lo ? 0 : 16);
+      const int64_t rx = m_base + j * 16 + (lane & 7);
+      if (rx < a.M) store4<true>(a.out, rx * a.N + nn, X[0], X[1], X[2], X[3]);
+      if (rx + 8 < a.M) store4<true>(a.out, (rx + 8) * a.N + nn, Y[0], Y[1], Y[2], Y[3]);
+    } else {
+      const int n = n_base + i * 16 + (lane >> 4) * 4;
+      if (mval[j]) store4<OUTF32>(a.out, mrow[j] * a.N + n, v[0], v[1], v[2], v[3]);
+    }
+  };
+
   auto store_chunk = [&](const EpiChunk<TM, RESF32> &c, int i) {
     const int n = n_base + i * 16 + (lane >> 4) * 4;
 #pragma unroll
@@ -228,9 +257,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
             for (int r = 0; r < 4; ++r) store1<OUTF32>(a.vt, base + (int64_t)r * a.M, y[r]);
           }
         } else if constexpr (EPI == EPI_GELU) {
-          if (mval[j])
-            store4<OUTF32>(a.out, m * a.N + n, gelu_erf(y[0]), gelu_erf(y[1]), gelu_erf(y[2]),
-                           gelu_erf(y[3]));
+          float v[4] = {gelu_erf(y[0]), gelu_erf(y[1]), gelu_erf(y[2]), gelu_erf(y[3])};
+          emit(i, j, v);
         } else if constexpr (EPI == EPI_RESID) {
           float r4[4];
           if constexpr (RESF32) {
@@ -242,9 +270,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
             r4[2] = __uint_as_float(c.r[j][1] << 16);
             r4[3] = __uint_as_float(c.r[j][1] & 0xffff0000u);
           }
-          if (mval[j])
-            store4<OUTF32>(a.out, m * a.N + n, r4[0] + c.g[0] * y[0], r4[1] + c.g[1] * y[1],
-                           r4[2] + c.g[2] * y[2], r4[3] + c.g[3] * y[3]);
+          float v[4] = {r4[0] + c.g[0] * y[0], r4[1] + c.g[1] * y[1], r4[2] + c.g[2] * y[2],
+                        r4[3] + c.g[3] * y[3]};
+          emit(i, j, v);
         }
       }
     }
