@@ -133,14 +133,76 @@ struct EpiChunk {
   float2 cs[TM][2];             // RoPE (cos, sin) of the lane's two channel pairs (QKV)
 };
 
+// LDS staging of bf16 epilogue outputs: 64 rows of 128 bytes per wave at this pitch
+constexpr int kStagePitch = 144;
+constexpr int kStageBytes = 64 * kStagePitch;
+
 // Epilogue of one wave's TN x TM block of 16x16 accumulator tiles. acc[i][j][r] = C[m][n]
 // with m = token m_base + 16 j + (lane & 15) and n = channel n_base + 16 i + 4 (lane >> 4) + r.
-// Loads use token rows clamped to M - 1; only the stores test m < M. Every element is read
-// and written by the same lane, so an output that aliases the residual stays correct.
+// Loads use token rows clamped to M - 1; only the stores test m < M.
+//
+// bf16 outputs go through `stage`, 8 KB of LDS private to the wave, 64 channels (four
+// column blocks) at a time: the values are written there in the output's row order and read
+// back 16 bytes per lane, so that every store instruction writes whole 128-byte lines (a
+// token's 64 channels of Q, K or a row-major output; 64 tokens of one V^T row). Written
+// directly, a 16-channel block gives a lane 8 bytes of a row (32 bytes per row per
+// instruction), and V^T 2 bytes. The staged V^T path needs M % 8 == 0 (the block's token
+// counts are). A staged 64-channel slice is stored after all its residual loads have
+// completed and only the wave touches it, so an output aliasing the residual stays correct.
 template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
-                                              int n_base, int64_t m_base, int lane) {
+                                              int n_base, int64_t m_base, int lane,
+                                              uint8_t *stage) {
   constexpr int PF = (EPI == EPI_QKV || RESF32) ? 1 : 2;  // column blocks loaded ahead
+  constexpr bool STAGED = !OUTF32 && EPI != EPI_RAW_I32;
+  // QKV: the wave's 128 channels lie in one section (d % 128 == 0); V^T is stored transposed
+  const int sec = EPI == EPI_QKV ? n_base / a.d : 0;
+  const bool vsec = EPI == EPI_QKV && sec == 2;
+  // stage layout: 64 rows of 128 bytes at a 144-byte pitch (the padding spreads a column
+  // of the row-major writes over the banks); rows are tokens (row-major outputs) or
+  // channels (V^T). Every address is a per-lane base plus a constant.
+  auto stage_put8 = [&](int row, int col2, uint2 v) {  // 8 bytes at byte column col2
+    *(uint2 *)(stage + row * kStagePitch + col2) = v;
+  };
+  auto stage_put2 = [&](int row, int col2, uint16_t v) {
+    *(uint16_t *)(stage + row * kStagePitch + col2) = v;
+  };
+  // write back the staged 64 channels starting at channel n_pass
+  auto stage_flush = [&](int n_pass) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = k * 8 + (lane >> 3), u = lane & 7;
+      const uint4 v = *(const uint4 *)(stage + row * kStagePitch + u * 16);
+      if constexpr (EPI == EPI_QKV) {
+        const int c = n_pass - sec * a.d;  // channel within the section, 64-aligned
+        const int head = c / a.Dh, dh0 = c - head * a.Dh;
+        if (vsec) {
+          const int64_t m = m_base + u * 8;
+          if (m < a.M)
+            *(uint4 *)((uint16_t *)a.vt + ((int64_t)head * a.Dh + dh0 + row) * a.M + m) = v;
+        } else {
+          const int64_t m = m_base + row;
+          if (m < a.M)
+            *(uint4 *)((uint16_t *)(sec == 0 ? a.q : a.k) + ((int64_t)head * a.M + m) * a.Dh +
+                       dh0 + u * 8) = v;
+        }
+      } else {
+        const int64_t m = m_base + row;
+        if (m < a.M) *(uint4 *)((uint16_t *)a.out + m * a.N + n_pass + u * 8) = v;
+      }
+    }
+  };
+  // bf16 values of column block i, token tile j (channels 4 (lane >> 4) .. + 3 of the block)
+  auto stage_vals = [&](int i, int j, const float (&v)[4]) {
+    const int t = j * 16 + (lane & 15);           // token within the wave's 64
+    const int cb = (i & 3) * 16 + (lane >> 4) * 4;  // channel within the 64 being staged
+    if (vsec) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) stage_put2(cb + r, t * 2, f2bf(v[r]));
+    } else {
+      stage_put8(t, cb * 2, make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])));
+    }
+  };
   int64_t mrow[TM];
   bool mval[TM];
   float sa[TM];
@@ -211,8 +273,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
       if (rx < a.M) store4<true>(a.out, rx * a.N + nn, X[0], X[1], X[2], X[3]);
       if (rx + 8 < a.M) store4<true>(a.out, (rx + 8) * a.N + nn, Y[0], Y[1], Y[2], Y[3]);
     } else {
-      const int n = n_base + i * 16 + (lane >> 4) * 4;
-      if (mval[j]) store4<OUTF32>(a.out, mrow[j] * a.N + n, v[0], v[1], v[2], v[3]);
+      stage_vals(i, j, v);
     }
   };
 
@@ -236,7 +297,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
             y[r] = ((float)acc[i][j][r] * sa[j]) * c.sw[r];
         }
         if constexpr (EPI == EPI_QKV) {
-          const int sec = n / a.d;
           const int cc = n - sec * a.d;
           const int head = cc / a.Dh;
           const int dh = cc - head * a.Dh;
@@ -248,9 +308,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
               y[2 * p] = u0 * cs.x - u1 * cs.y;
               y[2 * p + 1] = u0 * cs.y + u1 * cs.x;
             }
-            if (mval[j])
+            if constexpr (STAGED)
+              stage_vals(i, j, y);
+            else if (mval[j])
               store4<OUTF32>(sec == 0 ? a.q : a.k, ((int64_t)head * a.M + m) * a.Dh + dh, y[0],
                              y[1], y[2], y[3]);
+          } else if constexpr (STAGED) {
+            stage_vals(i, j, y);
           } else if (mval[j]) {
             const int64_t base = ((int64_t)head * a.Dh + dh) * a.M + m;
 #pragma unroll
@@ -284,6 +348,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
     constexpr int i = I;
     if constexpr (i + PF < TN) load_chunk(buf[(i + PF) % (PF + 1)], i + PF);
     store_chunk(buf[i % (PF + 1)], i);
+    if constexpr (STAGED && (i & 3) == 3) stage_flush(n_base + (i - 3) * 16);
   });
 }
 
@@ -445,8 +510,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
       tile_copy_setup(m0n, n0n, brs, ars, oA);
       H3K_PP_COPY(0);
     }
+    // LDS from buffer 1 on is free until the next tile's first loop iteration (its stage 0
+    // goes to buffer 0): each wave stages there
     gemm_epilogue<TN, TM, BF16, EPI, OUTF32, RESF32>(a, acc, n0 + grp * TN * 16,
-                                                   m0 + wq * TM * 16, lane);
+                                                   m0 + wq * TM * 16, lane,
+                                                   smem + PP_STAGE + wave * kStageBytes);
     if (!more) break;
     t = tn;
     m0 = m0n;
@@ -479,7 +547,8 @@ static hipError_t compute_units(int *n) {
 template <bool BF16, int EPI, bool OUTF32, bool RESF32>
 static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
   auto kern = gemm_pp_kernel<BF16, EPI, OUTF32, RESF32>;
-  constexpr size_t lds = (size_t)2 * PP_STAGE;
+  constexpr size_t lds = (size_t)PP_STAGE + 8 * kStageBytes;  // > 2 stages
+  static_assert(lds >= (size_t)2 * PP_STAGE && lds <= 160 * 1024, "LDS budget");
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)lds, lds_set);
       e != hipSuccess)
@@ -506,6 +575,7 @@ static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
 //   RESID  residual/out: bf16/fp32, fp32/fp32, fp32/bf16 (int8 and bf16 operands)
 static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) {
   const bool B = a.bf16_ops, OF = a.out_f32, RF = a.res_f32;
+  if (kind == EPI_QKV && !OF && a.M % 8) return hipErrorInvalidValue;  // staged V^T rows
   switch (kind) {
     case EPI_QKV:
       if (B) return OF ? hipErrorInvalidValue : gemm_tiles<true, EPI_QKV, false, false>(a, s);
