@@ -424,11 +424,15 @@ constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
 // Phase 1 of an iteration, interleaved by hand in 16 steps (a scheduling barrier ends each
 // step): step i reads K fragment i + PD, issues the two MFMAs of fragment i (S^T tile t4 =
 // i % 4, head-dim step kk = i / 4, both query tiles) into nxt, and does one sixteenth of the
-// softmax of cur: two exp2, one bf16 pair packed into pb, one dot2 into the row sum.
+// softmax of cur: two exp2, one bf16 pair packed into pb, one dot2 into the row sum. Steps
+// 0, 4, 8 and 12 also issue the wave's four global -> LDS copies of a later stage
+// (copy_piece(0..3)); issued together at the start of the iteration by all eight waves, the
+// copies queued behind each other and stalled the waves' issue.
+template <typename CopyF>
 __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4][2],
                                             v8bf (&pb)[2][2], const v8bf (&qf)[2][4],
                                             const uint8_t *kb, int koff, const float (&m)[2],
-                                            float (&l)[2], float sl2) {
+                                            float (&l)[2], float sl2, CopyF &&copy_piece) {
   const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
   v8bf kf[PD + 1];
   static_for<PD>([&](auto I) {
@@ -439,6 +443,7 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
   uint32_t u[4];
   static_for<16>([&](auto I) {
     constexpr int i = I;
+    if constexpr (i % 4 == 0) copy_piece(i / 4);  // one copy instruction every fourth step
     if constexpr (i + PD < 16)
       kf[(i + PD) % (PD + 1)] =
           *(const v8bf *)(kb + ((i + PD) % 4) * 4096 + (koff ^ (((i + PD) / 4) * 64)));
@@ -569,28 +574,27 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
       __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, (int)0xffffffffu, 0x00020000);
+  // piece 0, 1: K rows of copy instruction wave + 8 piece; piece 2, 3: V^T rows likewise
+  auto copy_piece = [&](int u, int piece) {
+    uint8_t *dst = smem + (u % NB) * STAGE;
+    if (piece < 2) {
+      const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;
+      const uint32_t key = min(kt0 + (uint32_t)kkey[piece], Lu - 1u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,
+          (__attribute__((address_space(3))) void *)(dst + (wave + 8 * piece) * 1024), 16,
+          (key * DH + kcol[piece]) * 2, 0, 0, 0);
+    } else {
+      const uint32_t vt0 = (uint32_t)(u >= 1 ? u - 1 : 0) * BK;
+      const uint32_t col = min(vt0 + (uint32_t)vcol, Lu - 8u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs,
+          (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * (piece - 2)) * 1024),
+          16, ((uint32_t)vrow[piece - 2] * Lu + col) * 2, 0, 0, 0);
+    }
+  };
 #define H3K_V2_COPY(u_)                                                                        \
   {                                                                                            \
-    const int u = (u_);                                                                        \
-    uint8_t *dst = smem + (u % NB) * STAGE;                                                    \
-    const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;                               \
-    const uint32_t vt0 = (uint32_t)(u >= 1 ? u - 1 : 0) * BK;                                  \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                            \
-      const uint32_t key = min(kt0 + (uint32_t)kkey[q], Lu - 1u);                              \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,                                            \
-          (__attribute__((address_space(3))) void *)(dst + (wave + 8 * q) * 1024), 16,         \
-          (key * DH + kcol[q]) * 2, 0, 0, 0);                                                  \
-    }                                                                                          \
-    const uint32_t col = min(vt0 + (uint32_t)vcol, Lu - 8u);                                   \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                              \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs,                                            \
-          (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * q) * 1024),   \
-          16, ((uint32_t)vrow[q] * Lu + col) * 2, 0, 0, 0);                                    \
+    _Pragma("unroll") for (int pc = 0; pc < 4; ++pc) copy_piece((u_), pc);                     \
   }
-  // fragment offsets inside a stage: K row t4*16 + c16, chunk 4kk + g; V^T row dt*16 + c16,
-  // chunk 4ks + g (the kk / ks part is applied as an XOR of kk*64 / ks*64)
-  const int koff = c16 * 256 + ((g ^ c16) * 16);
-  const int voff = K_BYTES + c16 * 128 + ((g ^ (c16 & 7)) * 16);
 
   v4f o[8][2];
 #pragma unroll
@@ -618,10 +622,11 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #define H3K_V2_ITER(CUR, NXT, j_, MASK)                                                        \
   {                                                                                            \
     const int jj = (j_);                                                                       \
-    if (jj + DIST <= nkt) H3K_V2_COPY(jj + DIST);                                             \
     const uint8_t *sb_ = smem + ((jj + 1) % NB) * STAGE;                                       \
     if (pend) rescale(o, l, alpha);                                                            \
-    phase_s_exp(NXT, CUR, pb, qf, sb_, koff, m, l, sl2);                                       \
+    phase_s_exp(NXT, CUR, pb, qf, sb_, koff, m, l, sl2, [&](int pc) {                          \
+      if (jj + DIST <= nkt) copy_piece(jj + DIST, pc);                                         \
+    });                                                                                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
     const bool grow_ = phase_pv_max(o, pb, NXT, sb_, voff, m, mnew, sl2);                      \
     pend = rescale_decision(grow_, mnew, m, alpha);                                            \
