@@ -595,6 +595,10 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   {                                                                                            \
     _Pragma("unroll") for (int pc = 0; pc < 4; ++pc) copy_piece((u_), pc);                     \
   }
+  // fragment offsets inside a stage: K row t4*16 + c16, chunk 4kk + g; V^T row dt*16 + c16,
+  // chunk 4ks + g (the kk / ks part is applied as an XOR of kk*64 / ks*64)
+  const int koff = c16 * 256 + ((g ^ c16) * 16);
+  const int voff = K_BYTES + c16 * 128 + ((g ^ (c16 & 7)) * 16);
 
   v4f o[8][2];
 #pragma unroll
