@@ -536,8 +536,13 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int head = blockIdx.y;
-  const int64_t q0 = (int64_t)blockIdx.x * BQ + wave * 32;
+  // work-group b runs on XCD b % 8; each XCD takes a contiguous range of (query block,
+  // head) pairs, query block fastest, so its concurrent work-groups share one head's K/V in L2
+  const int64_t nqb = (L + BQ - 1) / BQ, total = nqb * H;
+  int64_t t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int head = (int)(t / nqb);
+  const int64_t q0 = (t - (int64_t)head * nqb) * BQ + wave * 32;
   const uint16_t *Qh = Q + (int64_t)head * L * DH;
   const uint16_t *Kh = K + (int64_t)head * L * DH;
   const uint16_t *Vh = Vt + (int64_t)head * DH * L;
@@ -774,7 +779,9 @@ static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o,
   if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)v2::LDS, lds_set);
       e != hipSuccess)
     return e;
-  dim3 grid((unsigned)((L + v2::BQ - 1) / v2::BQ), (unsigned)H);
+  const int64_t nwg = ((L + v2::BQ - 1) / v2::BQ) * H;
+  if (nwg > 0x7fffffff) return hipErrorInvalidValue;  // one-dimensional grid
+  dim3 grid((unsigned)nwg);
   kern<<<grid, 512, v2::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
                                   (const uint16_t *)vt, o, H, L, sl2);
   return hipGetLastError();
