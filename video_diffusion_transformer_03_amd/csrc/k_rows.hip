@@ -190,6 +190,10 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
                                                   float *__restrict__ sc,
                                                   uint16_t *__restrict__ hout) {
   __shared__ float red[4];
+  // one-wave rows (d <= 5120): the block's four rows share shift and scale through LDS, so
+  // each row reads them from L2 a quarter as often and their loads overlap the row's
+  constexpr bool LDSP = (MODE == RM_LNQ || MODE == RM_LN_BF16) && WPR == 1 && MAXV <= 10;
+  __shared__ float4 lss[LDSP ? MAXV * 64 * 4 : 1];  // shift vectors, then scale vectors
   constexpr int NT = WPR * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
@@ -211,6 +215,17 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
 #pragma unroll
       for (int t = 0; t < 8; ++t) v[i][t] = 0.f;
     }
+  }
+
+  if constexpr (LDSP) {
+    const int nv = cols / 8;  // <= MAXV * 64
+    for (int c = threadIdx.x; c < nv; c += 256) {
+      lss[2 * c] = *(const float4 *)(shift + c * 8);
+      lss[2 * c + 1] = *(const float4 *)(shift + c * 8 + 4);
+      lss[MAXV * 128 + 2 * c] = *(const float4 *)(scale + c * 8);
+      lss[MAXV * 128 + 2 * c + 1] = *(const float4 *)(scale + c * 8 + 4);
+    }
+    __syncthreads();
   }
 
   if constexpr (MODE == RM_LNQ || MODE == RM_LN_BF16) {
@@ -239,8 +254,17 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
       int c = tid + i * NT;
       if (c < nvec) {
         float sh[8], sca[8];
-        load8(shift + c * 8, sh);
-        load8(scale + c * 8, sca);
+        if constexpr (LDSP) {
+          const float4 a0 = lss[2 * c], a1 = lss[2 * c + 1];
+          const float4 b0 = lss[MAXV * 128 + 2 * c], b1 = lss[MAXV * 128 + 2 * c + 1];
+          sh[0] = a0.x; sh[1] = a0.y; sh[2] = a0.z; sh[3] = a0.w;
+          sh[4] = a1.x; sh[5] = a1.y; sh[6] = a1.z; sh[7] = a1.w;
+          sca[0] = b0.x; sca[1] = b0.y; sca[2] = b0.z; sca[3] = b0.w;
+          sca[4] = b1.x; sca[5] = b1.y; sca[6] = b1.z; sca[7] = b1.w;
+        } else {
+          load8(shift + c * 8, sh);
+          load8(scale + c * 8, sca);
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t) v[i][t] = (v[i][t] - mean) * rstd * (1.0f + sca[t]) + sh[t];
       } else {
