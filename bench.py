@@ -99,7 +99,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "h3k runs on one GPU; --gpus must be 1 (the sharded design is described, not implemented)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
