@@ -74,7 +74,14 @@ def cpu_baseline(wl, x, c, bw, n_rows: int):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": (f"{wl.name}: LN+quant+QKV+RoPE for all {wl.L} tokens ({prefix:.1f} s), then "
                        f"attention, out-proj and MLP for {n_rows} evenly spaced tokens "
                        f"({rest:.1f} s); tokens/s = 1 / (prefix/{wl.L} + rest/{n_rows})"),
@@ -200,6 +207,10 @@ def main():
         result["roofline"] = {"kernel": dom, "bound": "mfma" if work[dom][0] == "ops" else "hbm",
                               "achieved": dk.get("achieved"), "peak": dk.get("peak"),
                               "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": traffic}
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count,
+                        "hbm_gib": round(props.total_memory / 2**30, 1)}
     result["kernels"] = kernels
     if not args.no_extras and args.variant == "w8a8" and args.workload == "block_l16384":
         del ws, out
