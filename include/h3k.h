@@ -125,10 +125,9 @@ typedef struct {
   size_t qg;                    /* int8 [L, F]                                          */
   size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied                */
   size_t vt;                    /* T [H, Dh, L] head-major, transposed                  */
-  size_t o;                     /* [L, d] attention output, head e in columns e*Dh ..;
-                                   fp32, or bf16 when the output projection is bf16      */
-  size_t x1;                    /* fp32 [L, d] residual stream after the attention half */
-  size_t g;                     /* [L, F] GELU output; fp32, or bf16 when the MLP is bf16 */
+  size_t o;                     /* T [L, d] attention output, head e in columns e*Dh .. */
+  size_t x1;                    /* T [L, d] residual stream after the attention half    */
+  size_t g;                     /* T [L, F] GELU output                                 */
   size_t h, h2;                 /* bf16 [L, d] modulated activations feeding a bf16 QKV /
                                    MLP projection (0 when unused)                       */
   size_t total;                 /* bytes needed (= h3k_workspace_bytes)                */

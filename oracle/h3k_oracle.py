@@ -247,7 +247,7 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
                   w_scale: float = 1.0, w_offset: float = 0.0,
                   eps: float = LN_EPS, theta: float = ROPE_THETA,
                   attn_inputs: str = "fp64", dense_inputs: str = "fp64",
-                  return_parts: bool = False):
+                  act_store: str = "fp64", return_parts: bool = False):
     """One DiT block forward. x [L, d] (fp64 view of the input values), cond [d_cond];
     w holds w_ada and, per projection, int8 codes q_* with fp32 scales s_* and/or the
     dense matrices w_*. variant selects the projections computed in W8A8 (see
@@ -260,6 +260,10 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     "Metal 4 및 TensorOps": BF16 QKV projection routed into head-major attention inputs).
     dense_inputs: "fp64" multiplies dense projections by the exact activations; "bf16"
     rounds each dense projection's activation operand to bfloat16 first (see _linear).
+    act_store: "fp64" keeps the attention output O, the residual stream x1, the GELU output
+    g and the block output exact; "bf16" rounds each of them to bfloat16 where it is
+    produced, as on a path whose kernels hand each other bf16 activation tensors (the
+    same two passages: bf16 tensors between the int8/bf16 projections and attention).
 
     rows: token rows whose output is wanted (all if None). Q, K and V are formed for
     every token (attention needs them); everything after attention is per token and is
@@ -281,12 +285,18 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     elif attn_inputs != "fp64":
         raise ValueError(attn_inputs)
     sel = np.arange(L) if rows is None else np.asarray(rows)
-    o = attention(q, k, v, sel).reshape(len(sel), d)
+    if act_store == "bf16":
+        store = round_bf16
+    elif act_store == "fp64":
+        store = lambda t: t
+    else:
+        raise ValueError(act_store)
+    o = store(attention(q, k, v, sel).reshape(len(sel), d))
     xs = x[sel]
-    x1 = xs + mod["gate1"] * _linear(o, w, "_o", variant, dense_inputs)
+    x1 = store(xs + mod["gate1"] * _linear(o, w, "_o", variant, dense_inputs))
     h2 = modulate(layer_norm(x1, eps), mod["shift2"], mod["scale2"])
-    g = gelu(_linear(h2, w, "_up", variant, dense_inputs))
-    x2 = x1 + mod["gate2"] * _linear(g, w, "_down", variant, dense_inputs)
+    g = store(gelu(_linear(h2, w, "_up", variant, dense_inputs)))
+    x2 = store(x1 + mod["gate2"] * _linear(g, w, "_down", variant, dense_inputs))
     if return_parts:
         return x2, {"m": np.concatenate([mod[k] for k in mod]), "h": h, "q": q, "k": k,
                     "v": v, "o": o, "x1": x1, "h2": h2, "g": g, "rows": sel}
@@ -317,9 +327,10 @@ def token_unpair(x_pre, xr_out, xr_in, grid) -> np.ndarray:
 
 def stack_forward(x, cond, blocks, *, n_heads: int, head_dim: int, grid,
                   tr_begin: int = 0, tr_end: int = 0, variant: str = "w8a8",
-                  attn_inputs: str = "fp64"):
+                  attn_inputs: str = "fp64", act_store: str = "fp64"):
     """Blocks 0..n-1 in order, sharing cond. Blocks [tr_begin, tr_end) run on the
-    horizontally paired grid (T, Hg, Wg/2) with w positions 2j + 0.5."""
+    horizontally paired grid (T, Hg, Wg/2) with w positions 2j + 0.5. With act_store
+    "bf16" the paired and unpaired token tensors are rounded to bfloat16 as well."""
     x = np.asarray(x, np.float64)
     T, Hg, Wg = grid
     tr_on = tr_end > tr_begin
@@ -328,16 +339,22 @@ def stack_forward(x, cond, blocks, *, n_heads: int, head_dim: int, grid,
         if tr_on and b == tr_begin:
             x_pre = x
             x = token_pair(x, grid)
+            if act_store == "bf16":
+                x = round_bf16(x)
             xr_in = x
         if tr_on and tr_begin <= b < tr_end:
             x = block_forward(x, cond, w, n_heads=n_heads, head_dim=head_dim,
                               grid=(T, Hg, Wg // 2), variant=variant,
-                              w_scale=2.0, w_offset=0.5, attn_inputs=attn_inputs)
+                              w_scale=2.0, w_offset=0.5, attn_inputs=attn_inputs,
+                              act_store=act_store)
         else:
             x = block_forward(x, cond, w, n_heads=n_heads, head_dim=head_dim,
-                              grid=grid, variant=variant, attn_inputs=attn_inputs)
+                              grid=grid, variant=variant, attn_inputs=attn_inputs,
+                              act_store=act_store)
         if tr_on and b == tr_end - 1:
             x = token_unpair(x_pre, x, xr_in, grid)
+            if act_store == "bf16":
+                x = round_bf16(x)
     return x
 
 

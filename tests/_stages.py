@@ -53,12 +53,12 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     stats["q"], stats["k"], stats["v"] = rel_l2(q_g, q_ref), rel_l2(k_g, k_ref), rel_l2(v_g, v_ref)
     assert max(stats["q"], stats["k"], stats["v"]) < tol_s, stats
 
-    # attention rows from the GPU's full Q, K, V (O is kept in fp32 for its quantiser)
+    # attention rows from the GPU's full Q, K, V (O stored in the activation type)
     qf = np64(q_all).transpose(1, 0, 2)
     kf = np64(k_all).transpose(1, 0, 2)
     vf = np64(vt_all).transpose(2, 0, 1)
     o_ref = O.attention(qf, kf, vf, rows).reshape(len(rows), d)
-    o_g = np64(V("o", torch.float32, (L, d))[tq])
+    o_g = np64(V("o", T, (L, d))[tq])
     stats["o"] = rel_l2(o_g, o_ref)
     assert stats["o"] < (1e-5 if f32 else 1e-2), stats
 
@@ -69,9 +69,9 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
 
     # out-projection + gated residual from the GPU's O codes
     x1_ref = x + mod["gate1"] * (O.int8_matmul(qo, w["q_o"]) * so.astype(np.float64)[:, None] * w["s_o"])
-    x1 = np64(V("x1", torch.float32, (L, d))[tq])
-    stats["x1"] = rel_l2(x1, x1_ref)
-    assert stats["x1"] < 1e-6, stats
+    x1 = np64(V("x1", T, (L, d))[tq])
+    stats["x1"] = rel_l2(x1, x1_ref if f32 else O.round_bf16(x1_ref))
+    assert stats["x1"] < (1e-6 if f32 else 1e-4), stats
 
     # second LN + quantiser from the GPU's x1
     qa2_ref, sa2_ref = O.quantize_rows(O.modulate(O.layer_norm(x1), mod["shift2"], mod["scale2"]))
@@ -83,9 +83,9 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
 
     # MLP up + GELU from the GPU's codes
     g_ref = O.gelu(O.int8_matmul(qa2, w["q_up"]) * sa2.astype(np.float64)[:, None] * w["s_up"])
-    g_g = np64(V("g", torch.float32, (L, F))[tq])
-    stats["g"] = rel_l2(g_g, g_ref)
-    assert stats["g"] < 1e-5, stats
+    g_g = np64(V("g", T, (L, F))[tq])
+    stats["g"] = rel_l2(g_g, g_ref if f32 else O.round_bf16(g_ref))
+    assert stats["g"] < (1e-5 if f32 else 1e-4), stats
     qg, sg = O.quantize_rows(g_g)
     stats["qg_match"], _ = code_match(V("qg", torch.int8, (L, F))[tq].cpu().numpy(), qg)
     assert stats["qg_match"] == 1.0

@@ -54,7 +54,8 @@ def test_workspace_monotone_and_layout():
         # int8 buffers hold L x d (or L x F) bytes, bf16 buffers 2 bytes per element
         spans = sorted([(lay["qa"], L * 256), (lay["qo"], L * 256), (lay["qa2"], L * 256),
                         (lay["qg"], L * 1024), (lay["q"], 2 * L * 256), (lay["k"], 2 * L * 256),
-                        (lay["vt"], 2 * L * 256), (lay["o"], 2 * L * 256), (lay["g"], 2 * L * 1024),
+                        (lay["vt"], 2 * L * 256), (lay["o"], 2 * L * 256), (lay["x1"], 2 * L * 256),
+                        (lay["g"], 2 * L * 1024),
                         (lay["m"], 6 * 256 * 4), (lay["s_a"], 4 * L), (lay["s_g"], 4 * L)])
         for (o1, n1), (o2, _) in zip(spans, spans[1:]):
             assert o1 + n1 <= o2
@@ -66,7 +67,8 @@ def test_workspace_monotone_and_layout():
                                    h3k.F_BF16_QKV | h3k.F_BF16_OUT, h3k.F_BF16_GEMM])
 def test_workspace_mixed_precision(flags):
     # each projection's buffers follow its own precision: a bf16 projection has no int8
-    # codes, and its input is a bf16 tensor (h, O or h2/g) instead of an fp32 one
+    # codes and reads a bf16 tensor (h, O, h2 or g); O, x1 and g are bf16 on every path
+    # but the fp32 debug one
     L, d, F = 512, 256, 1024
     dm = tiny_dims()
     lay = h3k.workspace_layout(dm, L, flags)
@@ -77,8 +79,7 @@ def test_workspace_mixed_precision(flags):
     assert (lay["qo"] == 0) == bo
     assert (lay["qa2"] == 0) == bm and (lay["qg"] == 0) == bm and (lay["h2"] != 0) == bm
     spans = [(lay["q"], 2 * L * d), (lay["k"], 2 * L * d), (lay["vt"], 2 * L * d),
-             (lay["o"], (2 if bo else 4) * L * d), (lay["x1"], 4 * L * d),
-             (lay["g"], (2 if bm else 4) * L * F)]
+             (lay["o"], 2 * L * d), (lay["x1"], 2 * L * d), (lay["g"], 2 * L * F)]
     for name, n in (("qa", L * d), ("qo", L * d), ("qa2", L * d), ("qg", L * F),
                     ("h", 2 * L * d), ("h2", 2 * L * d)):
         if lay[name]:

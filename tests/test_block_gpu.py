@@ -49,15 +49,15 @@ def run_gpu(wl, flags=0, zero_gates=False, gen_device="cpu"):
 
 def oracle_full(wl, r, variant="w8a8", rows=None, attn_inputs=None):
     """The oracle block on the run's inputs. On the bf16 path the attention consumes bf16
-    Q, K, V and every bf16 projection bf16 activations, so the oracle rounds them there
-    (attn_inputs = dense_inputs = "bf16"); the fp32 debug path is compared with the
-    all-fp64 oracle."""
+    Q, K, V, every bf16 projection bf16 activations, and O, x1, g and the output are stored
+    as bf16, so the oracle rounds them there (attn_inputs = dense_inputs = act_store =
+    "bf16"); the fp32 debug path is compared with the all-fp64 oracle."""
     if attn_inputs is None:
         attn_inputs = "fp64" if r["flags"] & h3k.F_FP32_DEBUG else "bf16"
     w = oracle_weights(r["bw"], r["dense"] if variant != "w8a8" else None)
     return O.block_forward(np64(r["x"]), np64(r["c"]), w, n_heads=wl.n_heads, head_dim=wl.head_dim,
                            grid=wl.grid, variant=variant, rows=rows, attn_inputs=attn_inputs,
-                           dense_inputs=attn_inputs)
+                           dense_inputs=attn_inputs, act_store=attn_inputs)
 
 
 # ----------------------------------------------------------------------------- tiny, full oracle

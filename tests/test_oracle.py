@@ -206,9 +206,22 @@ def test_gelu_textbook():
 
 
 # ----------------------------------------------------------------------------- block (brute force)
-def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_dense=False):
+def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_dense=False,
+              round_qkv=False, round_store=False):
     """Independent scalar-loop implementation of the block on tiny shapes. round_dense:
-    dense projections take bf16-rounded activations (torch's RNE conversion)."""
+    dense projections take bf16-rounded activations; round_qkv: Q, K (after RoPE) and V are
+    rounded to bf16 before attention; round_store: the attention output, the residual after
+    the attention half, the GELU output and the block output are rounded to bf16 where they
+    are produced. Every rounding is torch's RNE conversion."""
+
+    def rb(vals):
+        return torch.tensor(vals, dtype=torch.float64).to(torch.bfloat16).double().tolist()
+
+    def rq(vals):
+        return rb(vals) if round_qkv else vals
+
+    def rs(vals):
+        return rb(vals) if round_store else vals
     L, d = len(x), len(x[0])
     F = len(w["w_up"])
     m = [math.fsum(w["w_ada"][i][j] * c[j] for j in range(len(c))) for i in range(6 * d)]
@@ -266,9 +279,9 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_de
         return out
 
     qkv = [lin(ln_mod(x[l], sh1, sc1), "_qkv") for l in range(L)]
-    Q = [[rope(qkv[l][e * Dh:(e + 1) * Dh], l) for e in range(H)] for l in range(L)]
-    K = [[rope(qkv[l][d + e * Dh:d + (e + 1) * Dh], l) for e in range(H)] for l in range(L)]
-    V = [[qkv[l][2 * d + e * Dh:2 * d + (e + 1) * Dh] for e in range(H)] for l in range(L)]
+    Q = [[rq(rope(qkv[l][e * Dh:(e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
+    K = [[rq(rope(qkv[l][d + e * Dh:d + (e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
+    V = [[rq(qkv[l][2 * d + e * Dh:2 * d + (e + 1) * Dh]) for e in range(H)] for l in range(L)]
     out = []
     for l in range(L):
         o = []
@@ -278,12 +291,12 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_de
             p = [math.exp(t - mx) for t in s]
             z = math.fsum(p)
             o += [math.fsum(p[j] * V[j][e][i] for j in range(L)) / z for i in range(Dh)]
-        y = lin(o, "_o")
-        x1 = [x[l][i] + g1[i] * y[i] for i in range(d)]
+        y = lin(rs(o), "_o")
+        x1 = rs([x[l][i] + g1[i] * y[i] for i in range(d)])
         u = lin(ln_mod(x1, sh2, sc2), "_up")
-        g = [0.5 * t * (1 + math.erf(t / math.sqrt(2))) for t in u]
+        g = rs([0.5 * t * (1 + math.erf(t / math.sqrt(2))) for t in u])
         y2 = lin(g, "_down")
-        out.append([x1[i] + g2[i] * y2[i] for i in range(d)])
+        out.append(rs([x1[i] + g2[i] * y2[i] for i in range(d)]))
     return np.array(out)
 
 
@@ -334,6 +347,32 @@ def test_block_bruteforce_dense_bf16_inputs(variant):
     # rounding the operands changes the result (the option is not a no-op)
     plain = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant)
     assert not np.allclose(got, plain, rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("variant", ["w8a8", "bf16gemm"])
+@pytest.mark.parametrize("attn_inputs,act_store", [("bf16", "fp64"), ("fp64", "bf16"), ("bf16", "bf16")])
+def test_block_bruteforce_bf16_handoffs(variant, attn_inputs, act_store):
+    d, H, Dh, F, dc, grid = 12, 2, 6, 24, 5, (2, 2, 2)
+    w = _tiny_weights(d, F, dc, 13)
+    r = np.random.default_rng(14)
+    x = _bf16(r.standard_normal((8, d)))
+    c = r.standard_normal(dc)
+    got = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
+                          attn_inputs=attn_inputs, act_store=act_store)
+    ref = _bf_block(x.tolist(), c.tolist(), {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()},
+                    H, Dh, grid, variant, round_qkv=attn_inputs == "bf16", round_store=act_store == "bf16")
+    assert np.allclose(got, ref, rtol=1e-9, atol=1e-9)
+    plain = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant)
+    assert not np.allclose(got, plain, rtol=1e-9, atol=1e-9)
+    if act_store == "bf16":
+        assert np.array_equal(got, O.round_bf16(got))
+    # the stored intermediates are bf16 values and x2 is built from them
+    x2, parts = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
+                                attn_inputs=attn_inputs, act_store=act_store, return_parts=True)
+    assert np.array_equal(x2, got)
+    if act_store == "bf16":
+        for name in ("o", "x1", "g"):
+            assert np.array_equal(parts[name], O.round_bf16(parts[name])), name
 
 
 def test_block_zero_gates_identity():

@@ -145,10 +145,10 @@ void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
   w->q = take(H * Lz * Dh * T);
   w->k = take(H * Lz * Dh * T);
   w->vt = take(H * Lz * Dh * T);
-  // O, x1 and g feed quantisers (fp32) or a bf16 GEMM (bf16)
-  w->o = take(Lz * d * (p.out ? 2 : 4));
-  w->x1 = take(Lz * d * 4);
-  w->g = take(Lz * F * (p.mlp ? 2 : 4));
+  // O, x1 and g in the activation type (bf16; fp32 on the debug path)
+  w->o = take(Lz * d * T);
+  w->x1 = take(Lz * d * T);
+  w->g = take(Lz * F * T);
   w->h = p.qkv ? take(Lz * d * 2) : 0;
   w->h2 = p.mlp ? take(Lz * d * 2) : 0;
   w->total = off;
@@ -260,19 +260,19 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
-                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !p.out, s);
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, f32, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
   // quantise O
   if (!p.out) {
     Launch l(H3K_K_ROWQUANT_O, s, flags);
-    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), true, nullptr, nullptr, L, d, 0.f,
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), f32, nullptr, nullptr, L, d, 0.f,
                                  at<int8_t>(ws, lay.qo), at<float>(ws, lay.s_o), nullptr, s),
                      fn, "rowquant_o")))
       return rc;
   }
-  // out-proj + gated residual -> x1 (fp32, workspace)
-  float *x1 = at<float>(ws, lay.x1);
+  // out-proj + gated residual -> x1 (workspace, activation type)
+  void *x1 = at<void>(ws, lay.x1);
   {
     GemmArgs a = ga;
     a.bf16_ops = p.out;
@@ -283,7 +283,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.sa = at<float>(ws, lay.s_o);
     a.sw = w->s_o;
     a.out = x1;
-    a.out_f32 = true;
+    a.out_f32 = f32;
     a.res = x_in;
     a.res_f32 = f32;
     a.gate = gate1;
@@ -293,9 +293,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // LN + modulate (+ quant) of x1
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
-    hipError_t e = p.mlp ? launch_rows(1, x1, true, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
+    hipError_t e = p.mlp ? launch_rows(1, x1, f32, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
                                        at<uint16_t>(ws, lay.h2), s)
-                      : launch_rows(0, x1, true, shift2, scale2, L, d, dm->ln_eps,
+                      : launch_rows(0, x1, f32, shift2, scale2, L, d, dm->ln_eps,
                                     at<int8_t>(ws, lay.qa2), at<float>(ws, lay.s_a2), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant_2"))) return rc;
   }
@@ -310,14 +310,14 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.sa = at<float>(ws, lay.s_a2);
     a.sw = w->s_up;
     a.out = at<void>(ws, lay.g);
-    a.out_f32 = !p.mlp;
+    a.out_f32 = f32;
     Launch l(H3K_K_GEMM_UP, s, flags);
     if ((rc = l.done(launch_gemm(EPI_GELU, a, s), fn, "gemm_up"))) return rc;
   }
   // quantise g
   if (!p.mlp) {
     Launch l(H3K_K_ROWQUANT_G, s, flags);
-    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), true, nullptr, nullptr, L, F, 0.f,
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), f32, nullptr, nullptr, L, F, 0.f,
                                  at<int8_t>(ws, lay.qg), at<float>(ws, lay.s_g), nullptr, s),
                      fn, "rowquant_g")))
       return rc;
@@ -335,7 +335,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.out = x_out;
     a.out_f32 = f32;
     a.res = x1;
-    a.res_f32 = true;
+    a.res_f32 = f32;
     a.gate = gate2;
     Launch l(H3K_K_GEMM_DOWN, s, flags);
     if ((rc = l.done(launch_gemm(EPI_RESID, a, s), fn, "gemm_down"))) return rc;

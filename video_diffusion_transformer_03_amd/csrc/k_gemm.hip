@@ -569,10 +569,10 @@ static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
   return run_gemm_pp<BF16, EPI, OUTF32, RESF32>(a, s);
 }
 
-// instantiated type combinations:
+// instantiated type combinations (operands -> outputs):
 //   QKV    int8 -> bf16 | int8 -> fp32 | bf16 -> bf16
-//   GELU   int8 -> fp32 | bf16 -> bf16
-//   RESID  residual/out: bf16/fp32, fp32/fp32, fp32/bf16 (int8 and bf16 operands)
+//   GELU   int8 -> bf16 | int8 -> fp32 | bf16 -> bf16
+//   RESID  residual and output bf16 (int8 or bf16 operands) | fp32 (int8 operands)
 static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) {
   const bool B = a.bf16_ops, OF = a.out_f32, RF = a.res_f32;
   if (kind == EPI_QKV && !OF && a.M % 8) return hipErrorInvalidValue;  // staged V^T rows
@@ -583,17 +583,14 @@ static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) 
                 : gemm_tiles<false, EPI_QKV, false, false>(a, s);
     case EPI_GELU:
       if (B) return OF ? hipErrorInvalidValue : gemm_tiles<true, EPI_GELU, false, false>(a, s);
-      return OF ? gemm_tiles<false, EPI_GELU, true, false>(a, s) : hipErrorInvalidValue;
+      return OF ? gemm_tiles<false, EPI_GELU, true, false>(a, s)
+                : gemm_tiles<false, EPI_GELU, false, false>(a, s);
     case EPI_RESID:
-      if (!RF && OF)
-        return B ? gemm_tiles<true, EPI_RESID, true, false>(a, s)
-                 : gemm_tiles<false, EPI_RESID, true, false>(a, s);
-      if (RF && OF)
-        return B ? hipErrorInvalidValue : gemm_tiles<false, EPI_RESID, true, true>(a, s);
-      if (RF && !OF)
-        return B ? gemm_tiles<true, EPI_RESID, false, true>(a, s)
-                 : gemm_tiles<false, EPI_RESID, false, true>(a, s);
-      return hipErrorInvalidValue;
+      // residual and output share the activation type: bf16, or fp32 on the debug path
+      if (RF != OF) return hipErrorInvalidValue;
+      if (OF) return B ? hipErrorInvalidValue : gemm_tiles<false, EPI_RESID, true, true>(a, s);
+      return B ? gemm_tiles<true, EPI_RESID, false, false>(a, s)
+               : gemm_tiles<false, EPI_RESID, false, false>(a, s);
     default:
       return hipErrorInvalidValue;
   }
