@@ -123,7 +123,9 @@ typedef struct {
   size_t s_a, s_o, s_a2, s_g;   /* fp32 [L] per-token scales of the four quantisers     */
   size_t qa, qo, qa2;           /* int8 [L, d]                                          */
   size_t qg;                    /* int8 [L, F]                                          */
-  size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied                */
+  size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied; in bf16, q is
+                                   stored times log2(e)/sqrt(Dh) (the base-2 softmax
+                                   scale, applied before its one rounding)              */
   size_t vt;                    /* T [H, Dh, L] head-major, transposed                  */
   size_t o;                     /* T [L, d] attention output, head e in columns e*Dh .. */
   size_t x1;                    /* T [L, d] residual stream after the attention half    */

@@ -176,6 +176,14 @@ def apply_rope(u, ang) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- attention
+def q_handoff_scale(head_dim: int) -> float:
+    """log2(e) / sqrt(Dh): softmax(Q K^T / sqrt(Dh)) equals a base-2 softmax of
+    (Q * this) K^T, so a path may hand attention Q already multiplied by it and round
+    that product to its storage type once. Pure mathematics (exp(x) = 2^(x log2 e)); the
+    value matters only for where the bf16 rounding of Q happens."""
+    return math.log2(math.e) / math.sqrt(head_dim)
+
+
 def attention(q, k, v, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Multi-head softmax attention, no mask. q, k, v [L, H, Dh] -> O [n, H, Dh] for the
     query rows `rows` (all rows if None). S = q k^T / sqrt(Dh); softmax over keys with
@@ -258,6 +266,9 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     before attention, as on the path whose QKV projection hands the attention bf16
     tensors (page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
     "Metal 4 및 TensorOps": BF16 QKV projection routed into head-major attention inputs).
+    Q is handed over with the softmax scale in base 2 already applied, so its one
+    rounding is of Q * q_handoff_scale(head_dim); the oracle divides that back out and
+    runs its attention on the exact value of the rounded tensor (see q_handoff_scale).
     dense_inputs: "fp64" multiplies dense projections by the exact activations; "bf16"
     rounds each dense projection's activation operand to bfloat16 first (see _linear).
     act_store: "fp64" keeps the attention output O, the residual stream x1, the GELU output
@@ -281,7 +292,8 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     q = apply_rope(q, ang)
     k = apply_rope(k, ang)
     if attn_inputs == "bf16":
-        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+        c = q_handoff_scale(head_dim)
+        q, k, v = round_bf16(q * c) / c, round_bf16(k), round_bf16(v)
     elif attn_inputs != "fp64":
         raise ValueError(attn_inputs)
     sel = np.arange(L) if rows is None else np.asarray(rows)

@@ -46,6 +46,9 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     q_all = V("q", T, (H, L, Dh))
     k_all = V("k", T, (H, L, Dh))
     vt_all = V("vt", T, (H, Dh, L))
+    # on the bf16 path Q is stored with the base-2 softmax scale applied
+    qs = 1.0 if f32 else O.q_handoff_scale(Dh)
+    q_ref = q_ref * qs
     q_g = np64(q_all[:, tq, :]).transpose(1, 0, 2)
     k_g = np64(k_all[:, tq, :]).transpose(1, 0, 2)
     v_g = np64(vt_all[:, :, tq]).transpose(2, 0, 1)
@@ -54,7 +57,7 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     assert max(stats["q"], stats["k"], stats["v"]) < tol_s, stats
 
     # attention rows from the GPU's full Q, K, V (O stored in the activation type)
-    qf = np64(q_all).transpose(1, 0, 2)
+    qf = np64(q_all).transpose(1, 0, 2) / qs
     kf = np64(k_all).transpose(1, 0, 2)
     vf = np64(vt_all).transpose(2, 0, 1)
     o_ref = O.attention(qf, kf, vf, rows).reshape(len(rows), d)

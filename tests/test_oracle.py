@@ -279,7 +279,13 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_de
         return out
 
     qkv = [lin(ln_mod(x[l], sh1, sc1), "_qkv") for l in range(L)]
-    Q = [[rq(rope(qkv[l][e * Dh:(e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
+    # Q is rounded as handed to a base-2 softmax: times 1 / (sqrt(Dh) ln 2), then back
+    cq = 1.0 / (math.sqrt(Dh) * math.log(2.0))
+
+    def rqs(vals):
+        return [t / cq for t in rb([t * cq for t in vals])] if round_qkv else vals
+
+    Q = [[rqs(rope(qkv[l][e * Dh:(e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
     K = [[rq(rope(qkv[l][d + e * Dh:d + (e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
     V = [[rq(qkv[l][2 * d + e * Dh:2 * d + (e + 1) * Dh]) for e in range(H)] for l in range(L)]
     out = []
@@ -373,6 +379,17 @@ def test_block_bruteforce_bf16_handoffs(variant, attn_inputs, act_store):
     if act_store == "bf16":
         for name in ("o", "x1", "g"):
             assert np.array_equal(parts[name], O.round_bf16(parts[name])), name
+
+
+def test_q_handoff_scale_base2_softmax():
+    # a base-2 softmax of (Q * c) K^T is the softmax of Q K^T / sqrt(Dh)
+    r = np.random.default_rng(21)
+    for dh in (64, 128):
+        q, k = r.standard_normal(dh), r.standard_normal((40, dh))
+        e = np.exp(k @ q / math.sqrt(dh))
+        b = 2.0 ** (k @ (q * O.q_handoff_scale(dh)))
+        assert np.allclose(e / e.sum(), b / b.sum(), rtol=1e-12, atol=0)
+    assert O.q_handoff_scale(128) == pytest.approx(0.12752, abs=1e-5)
 
 
 def test_block_zero_gates_identity():

@@ -253,6 +253,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.Dh = Dh;
     a.rope = rope;
     a.rg = rg;
+    // bf16 path: Q leaves the epilogue multiplied by log2(e) / sqrt(Dh), so that attention
+    // exponentiates its scores without a scaling step (one rounding of Q either way)
+    if (!f32) a.q_scale = (1.0f / sqrtf((float)Dh)) * 1.4426950408889634f;
     Launch l(H3K_K_GEMM_QKV, s, flags);
     if ((rc = l.done(launch_gemm(EPI_QKV, a, s), fn, "gemm_qkv"))) return rc;
   }
@@ -260,7 +263,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
-                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, f32, s);
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !f32, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
   // quantise O
@@ -451,7 +454,7 @@ int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t 
   hipStream_t s = (hipStream_t)stream;
   Launch l(H3K_K_ATTENTION, s, flags);
   const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
-  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, f32, f32, s),
+  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, f32, false, s),
                 fn, "attention");
 }
 

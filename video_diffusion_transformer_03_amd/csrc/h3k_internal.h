@@ -134,6 +134,7 @@ struct GemmArgs {
   int d, H, Dh;
   const float2 *rope;
   RopeGeom rg;
+  float q_scale = 1.0f;  // EPI_QKV: factor applied to Q after RoPE, before it is rounded
   // EPI_GELU: out [M, N]; EPI_RESID: out[m,n] = res[m,n] + gate[n] * y
   void *out;
   const void *res;
@@ -156,11 +157,11 @@ inline hipError_t ensure_dynamic_lds(const void *kern, int bytes, std::atomic<ui
   return hipSuccess;
 }
 
-// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. in_f32: fp32 inputs (plain
-// FMA kernel, fp32 output); otherwise bf16 inputs on the matrix cores with a bf16 or
-// (out_f32) fp32 output.
+// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. f32: fp32 inputs and output
+// (plain FMA kernel); otherwise bf16 inputs and output on the matrix cores. q_prescaled
+// (bf16 only): q already carries scale * log2(e), the factor of the base-2 softmax.
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, float scale, bool in_f32, bool out_f32,
+                            int64_t L, int Dh, float scale, bool f32, bool q_prescaled,
                             hipStream_t s);
 
 }  // namespace h3k

@@ -164,7 +164,7 @@ __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH 
   }
 }
 
-template <int DH, bool OF32>
+template <int DH>
 __global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ Vt, void *__restrict__ Ov, int H, int64_t L, float sl2) {
@@ -268,13 +268,8 @@ __global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         v4f v = st.o[dt][qt];
-        if constexpr (OF32) {
-          *(float4 *)((float *)Ov + obase + dt * 16) =
-              make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-        } else {
-          *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
-              make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
-        }
+        *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
+            make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
       }
     }
   }
@@ -327,7 +322,9 @@ __device__ __forceinline__ void s_tile(v4f (&s)[4][2], const v8bf (&qf)[2][4],
 }
 
 // P = exp2(S sl2 - m) rounded to bf16 (the P^T operand, keys 8g .. 8g+7 of each 32-key
-// step), l += sum of the rounded P
+// step), l += sum of the rounded P. QPRE: S already holds the exponent (scaled scores
+// minus m), P = exp2(S).
+template <bool QPRE>
 __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
                                          const float (&m)[2], float (&l)[2], float sl2) {
   const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -340,8 +337,13 @@ __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
       float p[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks][qt][r], sl2, mneg));
-        p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks + 1][qt][r], sl2, mneg));
+        if constexpr (QPRE) {
+          p[r] = __builtin_amdgcn_exp2f(s[2 * ks][qt][r]);
+          p[4 + r] = __builtin_amdgcn_exp2f(s[2 * ks + 1][qt][r]);
+        } else {
+          p[r] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks][qt][r], sl2, mneg));
+          p[4 + r] = __builtin_amdgcn_exp2f(fmaf(s[2 * ks + 1][qt][r], sl2, mneg));
+        }
       }
       uint4 u;
       u.x = pack_bf2(p[0], p[1]);
@@ -374,7 +376,8 @@ __device__ __forceinline__ void pv_tile(v4f (&o)[8][2], const v8bf (&pb)[2][2],
 
 // Row maxima of a score tile in the exp2 domain (with MASK, keys >= kmax of the tile are
 // set to -inf first); grow = some row exceeds the running maximum m by more than 2^8.
-template <bool MASK>
+// QPRE: the tile already holds exponents relative to m, and mnew is that relative maximum.
+template <bool MASK, bool QPRE>
 __device__ __forceinline__ bool max_vals(v4f (&s)[4][2], const float (&m)[2], float (&mnew)[2],
                                          float sl2, int g, int kmax) {
   if (MASK && kmax < BK) {
@@ -398,25 +401,49 @@ __device__ __forceinline__ bool max_vals(v4f (&s)[4][2], const float (&m)[2], fl
     mx = fmaxf(fmaxf(mx, s[3][qt][1]), s[3][qt][2]);
     mx = fmaxf(mx, s[3][qt][3]);
     mx = rows_max(mx);
-    mnew[qt] = mx * sl2;
-    grow |= mnew[qt] > m[qt] + kRescaleLog2;
+    if constexpr (QPRE) {
+      mnew[qt] = mx;
+      grow |= mx > kRescaleLog2;
+    } else {
+      mnew[qt] = mx * sl2;
+      grow |= mnew[qt] > m[qt] + kRescaleLog2;
+    }
   }
   return grow;
 }
 
 // Lazy rescale decision: the running maximum m moves only when a row's maximum exceeds it
 // by more than 2^8 (P then stays <= 256). Returns whether any row of the wave moved
-// (alpha then holds the factors for O and l).
+// (alpha then holds the factors for O and l; QPRE: shift holds how far m moved, to be
+// taken off the pending score tile, which was formed relative to the old m).
+template <bool QPRE>
 __device__ __forceinline__ bool rescale_decision(bool grow, const float (&mnew)[2],
-                                                 float (&m)[2], float (&alpha)[2]) {
+                                                 float (&m)[2], float (&alpha)[2],
+                                                 float (&shift)[2]) {
   if (!(__builtin_amdgcn_read_exec() & __ballot(grow))) return false;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float mref = mnew[qt] > m[qt] + kRescaleLog2 ? mnew[qt] : m[qt];
-    alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mref);
-    m[qt] = mref;
+    if constexpr (QPRE) {
+      shift[qt] = mnew[qt] > kRescaleLog2 ? mnew[qt] : 0.f;
+      alpha[qt] = __builtin_amdgcn_exp2f(-shift[qt]);
+      m[qt] += shift[qt];
+    } else {
+      const float mref = mnew[qt] > m[qt] + kRescaleLog2 ? mnew[qt] : m[qt];
+      alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mref);
+      m[qt] = mref;
+    }
   }
   return true;
+}
+
+// QPRE: a score tile formed relative to an older m, brought to the current one
+__device__ __forceinline__ void shift_tile(v4f (&s)[4][2], const float (&shift)[2]) {
+#pragma unroll
+  for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[t4][qt][r] -= shift[qt];
 }
 
 constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
@@ -428,11 +455,14 @@ constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
 // 0, 4, 8 and 12 also issue the wave's four global -> LDS copies of a later stage
 // (copy_piece(0..3)); issued together at the start of the iteration by all eight waves, the
 // copies queued behind each other and stalled the waves' issue.
-template <typename CopyF>
+// QPRE: Q carries the base-2 softmax scale, each S tile starts from cq = -m (the MFMA's C
+// operand), so it comes out as the exponents themselves and exp2 reads it directly.
+template <bool QPRE, typename CopyF>
 __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4][2],
                                             v8bf (&pb)[2][2], const v8bf (&qf)[2][4],
                                             const uint8_t *kb, int koff, const float (&m)[2],
-                                            float (&l)[2], float sl2, CopyF &&copy_piece) {
+                                            const v4f (&cq)[2], float (&l)[2], float sl2,
+                                            CopyF &&copy_piece) {
   const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
   v8bf kf[PD + 1];
   static_for<PD>([&](auto I) {
@@ -450,13 +480,17 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
     constexpr int t4 = i % 4, kk = i / 4;
     const v8bf k = kf[i % (PD + 1)];
     const v4f z = {0.f, 0.f, 0.f, 0.f};
-    nxt[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[0][kk], kk ? nxt[t4][0] : z, 0, 0, 0);
-    nxt[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[1][kk], kk ? nxt[t4][1] : z, 0, 0, 0);
+    nxt[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[0][kk],
+                                                         kk ? nxt[t4][0] : (QPRE ? cq[0] : z), 0, 0, 0);
+    nxt[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[1][kk],
+                                                         kk ? nxt[t4][1] : (QPRE ? cq[1] : z), 0, 0, 0);
     // softmax slice: chunk c = i / 4 is (query tile qt, 32-key step ks), part i % 4 a pair
     constexpr int c = i / 4, part = i % 4, qt = c >> 1, ks = c & 1;
     constexpr int tt = 2 * ks + (part >> 1), r0 = (part & 1) * 2;
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0], sl2, mneg[qt]));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0 + 1], sl2, mneg[qt]));
+    const float p0 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][qt][r0])
+                          : __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0], sl2, mneg[qt]));
+    const float p1 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][qt][r0 + 1])
+                          : __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0 + 1], sl2, mneg[qt]));
     u[part] = pack_bf2(p0, p1);
     lacc[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u[part]), ones, lacc[qt], false);
     if constexpr (part == 3) pb[ks][qt] = __builtin_bit_cast(v8bf, make_uint4(u[0], u[1], u[2], u[3]));
@@ -469,6 +503,7 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
 // Phase 2, same shape: step i reads V^T fragment i + PD, issues the two MFMAs of fragment i
 // (head-dim tile dt = i % 8, key step ks = i / 8) into o, and advances the row maximum of
 // nxt (query tile i / 8, two scores per step; the cross-lane part ends each half).
+template <bool QPRE>
 __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2][2],
                                              const v4f (&nxt)[4][2], const uint8_t *vb, int voff,
                                              const float (&m)[2], float (&mnew)[2], float sl2) {
@@ -495,8 +530,13 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2]
       mx = fmaxf(fmaxf(mx, a0), a1);
     if constexpr (st == 7) {
       mx = rows_max(mx);
-      mnew[qt] = mx * sl2;
-      grow |= mnew[qt] > m[qt] + kRescaleLog2;
+      if constexpr (QPRE) {
+        mnew[qt] = mx;
+        grow |= mx > kRescaleLog2;
+      } else {
+        mnew[qt] = mx * sl2;
+        grow |= mnew[qt] > m[qt] + kRescaleLog2;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -526,7 +566,8 @@ __device__ __forceinline__ void rescale(v4f (&o)[8][2], float (&l)[2], const flo
 }
 }  // namespace v2
 
-template <bool OF32>
+// QPRE: Q arrives multiplied by log2(e) / sqrt(Dh) (sl2 is then unused)
+template <bool QPRE>
 __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict__ Q,
                                                       const uint16_t *__restrict__ K,
                                                       const uint16_t *__restrict__ Vt,
@@ -609,6 +650,8 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i][0] = o[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f};
+  float shift[2] = {0.f, 0.f};
+  v4f cq[2];  // QPRE: the C operand {-m, -m, -m, -m} each new S tile starts from
   v4f sa[4][2], sb[4][2];
   v8bf pb[2][2];
 
@@ -619,8 +662,20 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   H3K_PP_SYNC();
   s_tile(sa, qf, smem, koff);
   float mnew[2];
-  bool pend = max_vals<true>(sa, m, mnew, sl2, g, (int)min((int64_t)BK, L));
-  pend = rescale_decision(pend, mnew, m, alpha);
+  bool pend = max_vals<true, QPRE>(sa, m, mnew, sl2, g, (int)min((int64_t)BK, L));
+  if constexpr (QPRE) {
+    // the first tile sets m to its row maxima (every row has a valid key) and is shifted by
+    // them; O and l are still zero, so nothing is pending
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      m[qt] = shift[qt] = mnew[qt];
+      cq[qt] = v4f{-m[qt], -m[qt], -m[qt], -m[qt]};
+    }
+    shift_tile(sa, shift);
+    pend = false;
+  } else {
+    pend = rescale_decision<false>(pend, mnew, m, alpha, shift);
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));
   H3K_PP_SYNC();
 
@@ -632,13 +687,20 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   {                                                                                            \
     const int jj = (j_);                                                                       \
     const uint8_t *sb_ = smem + ((jj + 1) % NB) * STAGE;                                       \
-    if (pend) rescale(o, l, alpha);                                                            \
-    phase_s_exp(NXT, CUR, pb, qf, sb_, koff, m, l, sl2, [&](int pc) {                          \
+    if (pend) {                                                                                \
+      rescale(o, l, alpha);                                                                    \
+      if constexpr (QPRE) {                                                                    \
+        shift_tile(CUR, shift);                                                                \
+        _Pragma("unroll") for (int qt = 0; qt < 2; ++qt)                                       \
+          cq[qt] = v4f{-m[qt], -m[qt], -m[qt], -m[qt]};                                        \
+      }                                                                                        \
+    }                                                                                          \
+    phase_s_exp<QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, l, sl2, [&](int pc) {                \
       if (jj + DIST <= nkt) copy_piece(jj + DIST, pc);                                         \
     });                                                                                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
-    const bool grow_ = phase_pv_max(o, pb, NXT, sb_, voff, m, mnew, sl2);                      \
-    pend = rescale_decision(grow_, mnew, m, alpha);                                            \
+    const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, sb_, voff, m, mnew, sl2);                \
+    pend = rescale_decision<QPRE>(grow_, mnew, m, alpha, shift);                               \
     if (jj + DIST <= nkt)                                                                      \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
     else                                                                                       \
@@ -648,8 +710,11 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #define H3K_V2_LAST(CUR)                                                                       \
   {                                                                                            \
     const uint8_t *sb_ = smem + (nkt % NB) * STAGE;                                            \
-    if (pend) rescale(o, l, alpha);                                                            \
-    exp_tile(CUR, pb, m, l, sl2);                                                              \
+    if (pend) {                                                                                \
+      rescale(o, l, alpha);                                                                    \
+      if constexpr (QPRE) shift_tile(CUR, shift);                                              \
+    }                                                                                          \
+    exp_tile<QPRE>(CUR, pb, m, l, sl2);                                                        \
     pv_tile(o, pb, sb_, voff);                                                                 \
   }
   // nkt - 1 iterations in pairs (the score tiles swap roles); only the last iteration, whose
@@ -689,13 +754,8 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const v4f v = o[dt][qt];
-        if constexpr (OF32) {
-          *(float4 *)((float *)Ov + obase + dt * 16) =
-              make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-        } else {
-          *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
-              make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
-        }
+        *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
+            make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
       }
     }
   }
@@ -771,10 +831,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
   }
 }
 
-template <bool OF32>
+template <bool QPRE>
 static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o, int H,
                           int64_t L, float sl2, hipStream_t s) {
-  auto kern = attn_v2_kernel<OF32>;
+  auto kern = attn_v2_kernel<QPRE>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)v2::LDS, lds_set);
       e != hipSuccess)
@@ -787,45 +847,43 @@ static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o,
   return hipGetLastError();
 }
 
-template <int DH, bool OF32>
-static hipError_t attn_mfma(const void *q, const void *k, const void *vt, void *o, int H,
+template <int DH>
+static hipError_t attn_bf16(const void *q, const void *k, const void *vt, void *o, int H,
                             int64_t L, float sl2, hipStream_t s) {
-  if constexpr (DH == 128) {
-    return attn_v2<OF32>(q, k, vt, o, H, L, sl2, s);
-  } else {
-    using C = AttnCfg<DH>;
-    auto kern = attn_bf16_kernel<DH, OF32>;
-    static std::atomic<uint64_t> lds_set{0};
-    if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)C::LDS, lds_set);
-        e != hipSuccess)
-      return e;
-    dim3 grid((unsigned)((L + C::BQ - 1) / C::BQ), (unsigned)H);
-    kern<<<grid, 256, C::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
-                                   (const uint16_t *)vt, o, H, L, sl2);
-    return hipGetLastError();
-  }
+  using C = AttnCfg<DH>;
+  auto kern = attn_bf16_kernel<DH>;
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)C::LDS, lds_set);
+      e != hipSuccess)
+    return e;
+  dim3 grid((unsigned)((L + C::BQ - 1) / C::BQ), (unsigned)H);
+  kern<<<grid, 256, C::LDS, s>>>((const uint16_t *)q, (const uint16_t *)k,
+                                 (const uint16_t *)vt, o, H, L, sl2);
+  return hipGetLastError();
 }
 
 template <int DH>
-static hipError_t attn_dispatch(const void *q, const void *k, const void *vt, void *o, int H,
-                                int64_t L, float sl2, bool in_f32, bool out_f32, hipStream_t s) {
-  if (in_f32) {
-    dim3 grid((unsigned)((L + 63) / 64), (unsigned)H);
-    attn_f32_kernel<DH><<<grid, 256, 0, s>>>((const float *)q, (const float *)k,
-                                             (const float *)vt, (float *)o, H, L, sl2);
-    return hipGetLastError();
-  }
-  return out_f32 ? attn_mfma<DH, true>(q, k, vt, o, H, L, sl2, s)
-                 : attn_mfma<DH, false>(q, k, vt, o, H, L, sl2, s);
+static hipError_t attn_f32(const void *q, const void *k, const void *vt, void *o, int H,
+                           int64_t L, float sl2, hipStream_t s) {
+  dim3 grid((unsigned)((L + 63) / 64), (unsigned)H);
+  attn_f32_kernel<DH><<<grid, 256, 0, s>>>((const float *)q, (const float *)k,
+                                           (const float *)vt, (float *)o, H, L, sl2);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, float scale, bool in_f32, bool out_f32,
+                            int64_t L, int Dh, float scale, bool f32, bool q_prescaled,
                             hipStream_t s) {
   const float sl2 = scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2(e))
-  if (Dh == 128) return attn_dispatch<128>(q, k, vt, o, H, L, sl2, in_f32, out_f32, s);
-  if (Dh == 64) return attn_dispatch<64>(q, k, vt, o, H, L, sl2, in_f32, out_f32, s);
-  return hipErrorInvalidValue;
+  if (Dh != 64 && Dh != 128) return hipErrorInvalidValue;
+  if (f32) {
+    if (q_prescaled) return hipErrorInvalidValue;
+    return Dh == 128 ? attn_f32<128>(q, k, vt, o, H, L, sl2, s)
+                     : attn_f32<64>(q, k, vt, o, H, L, sl2, s);
+  }
+  if (Dh == 64) return attn_bf16<64>(q, k, vt, o, H, L, q_prescaled ? 1.0f : sl2, s);
+  return q_prescaled ? attn_v2<true>(q, k, vt, o, H, L, sl2, s)
+                     : attn_v2<false>(q, k, vt, o, H, L, sl2, s);
 }
 
 }  // namespace h3k

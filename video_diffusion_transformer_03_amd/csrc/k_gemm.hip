@@ -308,6 +308,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
               y[2 * p] = u0 * cs.x - u1 * cs.y;
               y[2 * p + 1] = u0 * cs.y + u1 * cs.x;
             }
+            if (sec == 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) y[r] *= a.q_scale;
+            }
             if constexpr (STAGED)
               stage_vals(i, j, y);
             else if (mval[j])
