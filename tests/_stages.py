@@ -85,10 +85,16 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     assert np.allclose(sa2, sa2_ref, rtol=1e-6, atol=0)
 
     # MLP up + GELU from the GPU's codes
-    g_ref = O.gelu(O.int8_matmul(qa2, w["q_up"]) * sa2.astype(np.float64)[:, None] * w["s_up"])
+    u_ref = O.int8_matmul(qa2, w["q_up"]) * sa2.astype(np.float64)[:, None] * w["s_up"]
+    g_ref = O.gelu(u_ref)
     g_g = np64(V("g", T, (L, F))[tq])
     stats["g"] = rel_l2(g_g, g_ref if f32 else O.round_bf16(g_ref))
     assert stats["g"] < (1e-5 if f32 else 1e-4), stats
+    # pointwise: the fp32 dequant and the erf approximation stay within 1e-6 (1 + |u|); storing
+    # g in bf16 (8 significant bits) adds at most 2^-8 of |g|
+    bound = 1e-6 * (1 + np.abs(u_ref)) + (0 if f32 else 2.0 ** -8 * (np.abs(g_ref) + 1e-6 * (1 + np.abs(u_ref))))
+    stats["g_pw"] = float(np.max(np.abs(g_g - g_ref) / bound))
+    assert stats["g_pw"] <= 1.0, stats
     qg, sg = O.quantize_rows(g_g)
     stats["qg_match"], _ = code_match(V("qg", torch.int8, (L, F))[tq].cpu().numpy(), qg)
     assert stats["qg_match"] == 1.0

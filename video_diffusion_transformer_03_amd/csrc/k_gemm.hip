@@ -55,25 +55,25 @@ __device__ __forceinline__ void store1(void *base, int64_t idx, float y) {
     ((uint16_t *)base)[idx] = f2bf(y);
 }
 
-// erf without branches: Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26, erf(x) = 1 - (a1 t + ... + a5 t^5) e^(-x^2), t = 1 / (1 + p x) for x >= 0, odd in
-// x; absolute error <= 1.5e-7 (about one fp32 ulp of 1), with the hardware reciprocal and
-// exp2 adding about an ulp each.
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-(ax * ax) * 1.4426950408889634f);
-  return copysignf(fmaf(-poly, e, 1.0f), x);
-}
-
-// exact (erf) GELU, x * Phi(x)
+// Exact (erf) GELU, z Phi(z), written as max(z, 0) - |z| erfc(|z| / sqrt 2) / 2 (the same
+// value for either sign of z, with no 1 + erf cancellation for negative z). erfc without
+// branches: Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26,
+// erfc(a) = (a1 t + ... + a5 t^5) e^(-a^2), t = 1 / (1 + p a), a >= 0, absolute error
+// <= 1.5e-7; here a = |z| / sqrt 2, with 1/2 folded into the coefficients and 1 / sqrt 2
+// into p. The hardware reciprocal and exp2 add about an ulp each; in fp32 the GELU error
+// stays below 1e-7 (1 + |z|).
 __device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f));
+  constexpr float kP = 0.3275911f * 0.70710678118654752f;
+  constexpr float kE = -0.5f * 1.4426950408889634f;  // e^(-z^2 / 2) = 2^(kE z^2)
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(kP, az, 1.0f));
+  float poly = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  poly = fmaf(poly, t, 0.5f * 1.421413741f);
+  poly = fmaf(poly, t, 0.5f * -0.284496736f);
+  poly = fmaf(poly, t, 0.5f * 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f((z * z) * kE);
+  return fmaf(-az, poly * e, fmaxf(z, 0.f));
 }
 
 // Table offsets of token l's three axes: pair i of head_dim turns by tbl[ofs.x + i] (i < Pt),

@@ -193,7 +193,13 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
   // one-wave rows (d <= 5120): the block's four rows share shift and scale through LDS, so
   // each row reads them from L2 a quarter as often and their loads overlap the row's
   constexpr bool LDSP = (MODE == RM_LNQ || MODE == RM_LN_BF16) && WPR == 1 && MAXV <= 10;
-  __shared__ float4 lss[LDSP ? MAXV * 64 * 4 : 1];  // shift vectors, then scale vectors
+  // four planes of MAXV * 64 float4: shift[8c .. 8c+3], shift[8c+4 ..], scale likewise, so
+  // that lane c's 16-byte reads of a plane are consecutive (no bank conflicts)
+  constexpr int LP = LDSP ? MAXV * 64 : 1;
+  __shared__ float4 lss[4 * LP];
+  // bf16 rows of a LayerNorm stay packed through the mean and variance passes (half the
+  // registers of an fp32 copy; the modulated fp32 values replace them one vector at a time)
+  constexpr bool PACKED = std::is_same<Tin, uint16_t>::value && MODE != RM_Q;
   constexpr int NT = WPR * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
@@ -203,10 +209,13 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
   const Tin *xr = x + (active ? row : 0) * (int64_t)cols;
 
   float v[MAXV][8];
+  uint4 raw[PACKED ? MAXV : 1];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     int c = tid + i * NT;
-    if (active && c < nvec) {
+    if constexpr (PACKED) {
+      raw[i] = (active && c < nvec) ? *(const uint4 *)(xr + (int64_t)c * 8) : make_uint4(0, 0, 0, 0);
+    } else if (active && c < nvec) {
       if constexpr (MODE == RM_Q)  // O and g are read once
         load8_nt(xr + (int64_t)c * 8, v[i]);
       else
@@ -220,20 +229,41 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
   if constexpr (LDSP) {
     const int nv = cols / 8;  // <= MAXV * 64
     for (int c = threadIdx.x; c < nv; c += 256) {
-      lss[2 * c] = *(const float4 *)(shift + c * 8);
-      lss[2 * c + 1] = *(const float4 *)(shift + c * 8 + 4);
-      lss[MAXV * 128 + 2 * c] = *(const float4 *)(scale + c * 8);
-      lss[MAXV * 128 + 2 * c + 1] = *(const float4 *)(scale + c * 8 + 4);
+      lss[c] = *(const float4 *)(shift + c * 8);
+      lss[LP + c] = *(const float4 *)(shift + c * 8 + 4);
+      lss[2 * LP + c] = *(const float4 *)(scale + c * 8);
+      lss[3 * LP + c] = *(const float4 *)(scale + c * 8 + 4);
     }
     __syncthreads();
   }
 
   if constexpr (MODE == RM_LNQ || MODE == RM_LN_BF16) {
     float s = 0.f;
+    if constexpr (PACKED) {
+      // pairs of bf16 summed exactly by a dot product with (1, 1)
+      const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i)
+      for (int i = 0; i < MAXV; ++i) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) s += v[i][t];
+        for (int t = 0; t < 4; ++t)
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, w[t]), ones, s, false);
+      }
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[i][2 * t] = __uint_as_float(w[t] << 16);
+          v[i][2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) s += v[i][t];
+    }
     const float mean = group_reduce<WPR>(s, false, red) / (float)cols;
     float ss = 0.f;
 #pragma unroll
@@ -255,8 +285,8 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
       if (c < nvec) {
         float sh[8], sca[8];
         if constexpr (LDSP) {
-          const float4 a0 = lss[2 * c], a1 = lss[2 * c + 1];
-          const float4 b0 = lss[MAXV * 128 + 2 * c], b1 = lss[MAXV * 128 + 2 * c + 1];
+          const float4 a0 = lss[c], a1 = lss[LP + c];
+          const float4 b0 = lss[2 * LP + c], b1 = lss[3 * LP + c];
           sh[0] = a0.x; sh[1] = a0.y; sh[2] = a0.z; sh[3] = a0.w;
           sh[4] = a1.x; sh[5] = a1.y; sh[6] = a1.z; sh[7] = a1.w;
           sca[0] = b0.x; sca[1] = b0.y; sca[2] = b0.z; sca[3] = b0.w;
