@@ -59,9 +59,12 @@ hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStr
   return hipGetLastError();
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 // ============================================================== AdaLN GEMV
 // m[i] = sum_j W[i, j] c[j]. One wave per output row; each lane keeps the slice of c
-// it multiplies in registers (MAXC 16-byte chunks of W per lane).
+// it multiplies in registers (MAXC 16-byte chunks of W per lane). W is read once, with
+// nontemporal loads (12% faster than cached loads at 6d x d_c = 30720 x 5120).
 template <int MAXC>
 __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t *__restrict__ W,
                                                     const float *__restrict__ c,
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t *__restrict__
     for (int i = 0; i < MAXC; ++i) {
       int ch = lane + 64 * i;
       if (ch < nch) {
-        uint4 u = *(const uint4 *)(wr + ch * 8);
-        uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        const v4u u = __builtin_nontemporal_load((const v4u *)(wr + ch * 8));
+        const uint32_t w4[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           acc = fmaf(__uint_as_float(w4[t] << 16), cv[i][2 * t], acc);
@@ -141,7 +144,6 @@ __device__ __forceinline__ void load8(const float *p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // streaming variants for inputs read exactly once (nontemporal: no cache allocation)
 __device__ __forceinline__ void load8_nt(const uint16_t *p, float v[8]) {
   const v4u u = __builtin_nontemporal_load((const v4u *)p);
@@ -197,9 +199,10 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
   // that lane c's 16-byte reads of a plane are consecutive (no bank conflicts)
   constexpr int LP = LDSP ? MAXV * 64 : 1;
   __shared__ float4 lss[4 * LP];
-  // bf16 rows of a LayerNorm stay packed through the mean and variance passes (half the
-  // registers of an fp32 copy; the modulated fp32 values replace them one vector at a time)
-  constexpr bool PACKED = std::is_same<Tin, uint16_t>::value && MODE != RM_Q;
+  // bf16 rows stay packed in registers (half the registers of an fp32 copy): a LayerNorm
+  // row through its mean and variance passes (the modulated fp32 values then replace it),
+  // a quantiser row throughout (absmax on the bit patterns, unpacked again for the codes)
+  constexpr bool PACKED = std::is_same<Tin, uint16_t>::value;
   constexpr int NT = WPR * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
@@ -213,7 +216,13 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     int c = tid + i * NT;
-    if constexpr (PACKED) {
+    if constexpr (PACKED && MODE == RM_Q) {  // O and g are read once
+      raw[i] = make_uint4(0, 0, 0, 0);
+      if (active && c < nvec) {
+        const v4u u = __builtin_nontemporal_load((const v4u *)(xr + (int64_t)c * 8));
+        raw[i] = make_uint4(u[0], u[1], u[2], u[3]);
+      }
+    } else if constexpr (PACKED) {
       raw[i] = (active && c < nvec) ? *(const uint4 *)(xr + (int64_t)c * 8) : make_uint4(0, 0, 0, 0);
     } else if (active && c < nvec) {
       if constexpr (MODE == RM_Q)  // O and g are read once
@@ -320,11 +329,25 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
       }
     }
   } else {
+    constexpr bool RAWQ = PACKED && MODE == RM_Q;
     float a = 0.f;
+    if constexpr (RAWQ) {
+      // |bf16| orders like its 15 magnitude bits read as an integer: the row's largest
+      // magnitude is an integer maximum over the halves, then widened to fp32 once
+      uint32_t mi = 0;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i)
+      for (int i = 0; i < MAXV; ++i) {
+        const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(v[i][t]));
+        for (int t = 0; t < 4; ++t) mi = max(mi, max(w[t] & 0x7fffu, (w[t] >> 16) & 0x7fffu));
+      }
+      a = __uint_as_float(mi << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a = fmaxf(a, fabsf(v[i][t]));
+    }
     a = group_reduce<WPR>(a, true, red);
     const float inv = a > 0.f ? 127.0f / a : 0.f;
     if (active) {
@@ -333,11 +356,22 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
       for (int i = 0; i < MAXV; ++i) {
         int c = tid + i * NT;
         if (c < nvec) {
+          float e[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) e[t] = v[i][t];
+          if constexpr (RAWQ) {
+            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              e[2 * t] = __uint_as_float(w[t] << 16);
+              e[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+            }
+          }
           uint32_t lo = 0, hi = 0;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            lo |= ((uint32_t)quant_code(v[i][t], inv) & 0xffu) << (8 * t);
-            hi |= ((uint32_t)quant_code(v[i][t + 4], inv) & 0xffu) << (8 * t);
+            lo |= ((uint32_t)quant_code(e[t], inv) & 0xffu) << (8 * t);
+            hi |= ((uint32_t)quant_code(e[t + 4], inv) & 0xffu) << (8 * t);
           }
           *(uint2 *)(q + row * (int64_t)cols + (int64_t)c * 8) = make_uint2(lo, hi);
         }
