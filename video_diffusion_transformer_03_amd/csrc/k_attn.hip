@@ -448,13 +448,35 @@ __device__ __forceinline__ void shift_tile(v4f (&s)[4][2], const float (&shift)[
 
 constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
 
-// Phase 1 of an iteration, interleaved by hand in 16 steps (a scheduling barrier ends each
-// step): step i reads K fragment i + PD, issues the two MFMAs of fragment i (S^T tile t4 =
-// i % 4, head-dim step kk = i / 4, both query tiles) into nxt, and does one sixteenth of the
-// softmax of cur: two exp2, one bf16 pair packed into pb, one dot2 into the row sum. Steps
-// 0, 4, 8 and 12 also issue the wave's four global -> LDS copies of a later stage
-// (copy_piece(0..3)); issued together at the start of the iteration by all eight waves, the
-// copies queued behind each other and stalled the waves' issue.
+// One slice of the softmax of a score tile: the pair of scores PART of query tile QT in
+// 32-key step KS -> two exp2, one bf16 pair packed into u[PART] (pb[KS][QT] once the four
+// parts are done), one dot2 of the rounded pair into the row sum.
+template <bool QPRE, int QT, int KS, int PART>
+__device__ __forceinline__ void softmax_slice(const v4f (&cur)[4][2], uint32_t (&u)[4],
+                                              float (&lacc)[2], v8bf (&pb)[2][2],
+                                              const float (&mneg)[2], float sl2) {
+  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+  constexpr int tt = 2 * KS + (PART >> 1), r0 = (PART & 1) * 2;
+  const float p0 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][QT][r0])
+                        : __builtin_amdgcn_exp2f(fmaf(cur[tt][QT][r0], sl2, mneg[QT]));
+  const float p1 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][QT][r0 + 1])
+                        : __builtin_amdgcn_exp2f(fmaf(cur[tt][QT][r0 + 1], sl2, mneg[QT]));
+  u[PART] = pack_bf2(p0, p1);
+  lacc[QT] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u[PART]), ones, lacc[QT], false);
+  if constexpr (PART == 3) pb[KS][QT] = __builtin_bit_cast(v8bf, make_uint4(u[0], u[1], u[2], u[3]));
+}
+
+// An iteration runs two phases of 16 hand-ordered steps (a scheduling barrier ends each
+// step). The softmax of the current tile is split between them by 32-key step, so that each
+// phase's VALU work fits beside its 32 MFMAs: with all of it in phase 1, that phase's VALU
+// issue exceeded its matrix-core time while phase 2 carried only the row maximum.
+//
+// Phase 1: step i reads K fragment i + PD, issues the two MFMAs of fragment i (S^T tile t4 =
+// i % 4, head-dim step kk = i / 4, both query tiles) into nxt; every odd step does one slice
+// of the softmax of cur's first 32 keys (pb[0]). Steps 0, 4, 8 and 12 also issue the wave's
+// four global -> LDS copies of a later stage (copy_piece(0..3)); issued together at the
+// start of the iteration by all eight waves, the copies queued behind each other and stalled
+// the waves' issue.
 // QPRE: Q carries the base-2 softmax scale, each S tile starts from cq = -m (the MFMA's C
 // operand), so it comes out as the exponents themselves and exp2 reads it directly.
 template <bool QPRE, typename CopyF>
@@ -463,7 +485,6 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
                                             const uint8_t *kb, int koff, const float (&m)[2],
                                             const v4f (&cq)[2], float (&l)[2], float sl2,
                                             CopyF &&copy_piece) {
-  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
   v8bf kf[PD + 1];
   static_for<PD>([&](auto I) {
     kf[I] = *(const v8bf *)(kb + (I % 4) * 4096 + (koff ^ ((I / 4) * 64)));
@@ -484,16 +505,10 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
                                                          kk ? nxt[t4][0] : (QPRE ? cq[0] : z), 0, 0, 0);
     nxt[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[1][kk],
                                                          kk ? nxt[t4][1] : (QPRE ? cq[1] : z), 0, 0, 0);
-    // softmax slice: chunk c = i / 4 is (query tile qt, 32-key step ks), part i % 4 a pair
-    constexpr int c = i / 4, part = i % 4, qt = c >> 1, ks = c & 1;
-    constexpr int tt = 2 * ks + (part >> 1), r0 = (part & 1) * 2;
-    const float p0 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][qt][r0])
-                          : __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0], sl2, mneg[qt]));
-    const float p1 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][qt][r0 + 1])
-                          : __builtin_amdgcn_exp2f(fmaf(cur[tt][qt][r0 + 1], sl2, mneg[qt]));
-    u[part] = pack_bf2(p0, p1);
-    lacc[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u[part]), ones, lacc[qt], false);
-    if constexpr (part == 3) pb[ks][qt] = __builtin_bit_cast(v8bf, make_uint4(u[0], u[1], u[2], u[3]));
+    if constexpr (i % 2 == 1) {
+      constexpr int sl = i / 2;
+      softmax_slice<QPRE, sl / 4, 0, sl % 4>(cur, u, lacc, pb, mneg, sl2);
+    }
     __builtin_amdgcn_sched_barrier(0);
   });
   l[0] = lacc[0];
@@ -502,15 +517,21 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
 
 // Phase 2, same shape: step i reads V^T fragment i + PD, issues the two MFMAs of fragment i
 // (head-dim tile dt = i % 8, key step ks = i / 8) into o, and advances the row maximum of
-// nxt (query tile i / 8, two scores per step; the cross-lane part ends each half).
+// nxt (query tile i / 8, two scores per step; the cross-lane part ends each half). Steps
+// 0 .. 7 also do the softmax slices of cur's last 32 keys (pb[1]), which the MFMAs of steps
+// 8 .. 15 consume.
 template <bool QPRE>
-__device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2][2],
-                                             const v4f (&nxt)[4][2], const uint8_t *vb, int voff,
-                                             const float (&m)[2], float (&mnew)[2], float sl2) {
+__device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], v8bf (&pb)[2][2],
+                                             const v4f (&nxt)[4][2], const v4f (&cur)[4][2],
+                                             const uint8_t *vb, int voff, const float (&m)[2],
+                                             float (&mnew)[2], float (&l)[2], float sl2) {
   v8bf vf[PD + 1];
   static_for<PD>([&](auto I) {
     vf[I] = *(const v8bf *)(vb + (I % 8) * 2048 + (voff ^ ((I / 8) * 64)));
   });
+  const float mneg[2] = {-m[0], -m[1]};
+  float lacc[2] = {l[0], l[1]};
+  uint32_t u[4];
   float mx = 0.f;
   bool grow = false;
   static_for<16>([&](auto I) {
@@ -522,6 +543,7 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2]
     const v8bf v = vf[i % (PD + 1)];
     o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][0], o[dt][0], 0, 0, 0);
     o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][1], o[dt][1], 0, 0, 0);
+    if constexpr (i < 8) softmax_slice<QPRE, i / 4, 1, i % 4>(cur, u, lacc, pb, mneg, sl2);
     constexpr int qt = i / 8, st = i % 8;  // scores 2 st, 2 st + 1 of query tile qt
     const float a0 = nxt[st >> 1][qt][(st & 1) * 2], a1 = nxt[st >> 1][qt][(st & 1) * 2 + 1];
     if constexpr (st == 0)
@@ -540,6 +562,8 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], const v8bf (&pb)[2]
     }
     __builtin_amdgcn_sched_barrier(0);
   });
+  l[0] = lacc[0];
+  l[1] = lacc[1];
   return grow;
 }
 
@@ -699,7 +723,7 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
       if (jj + DIST <= nkt) copy_piece(jj + DIST, pc);                                         \
     });                                                                                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
-    const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, sb_, voff, m, mnew, sl2);                \
+    const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, l, sl2);        \
     pend = rescale_decision<QPRE>(grow_, mnew, m, alpha, shift);                               \
     if (jj + DIST <= nkt)                                                                      \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
