@@ -112,7 +112,8 @@ def test_gemm_i8_extremes():
 
 
 # ----------------------------------------------------------------------------- attention
-@pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 200, 128), (3, 1000, 64), (1, 4096, 128)])
+@pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 56, 128), (1, 72, 128), (2, 200, 128), (3, 1000, 64),
+                                    (1, 4096, 128)])
 def test_attention_bf16(H, L, Dh):
     q = randn((H, L, Dh), 21, 1.0)
     k = randn((H, L, Dh), 22, 1.0)

@@ -599,7 +599,8 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
                                                       float sl2) {
   using namespace v2;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index made visibly uniform: the copies' LDS destinations are then scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   // work-group b runs on XCD b % 8; each XCD takes a contiguous range of (query block,
   // head) pairs, query block fastest, so its concurrent work-groups share one head's K/V in L2
@@ -644,10 +645,29 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
       __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, (int)0xffffffffu, 0x00020000);
+  // Per-lane byte offsets of a full tile's copies, tile 0; a full tile adds its start as the
+  // instructions' scalar offset, so these copies cost no vector instructions. Only the last
+  // partial tiles take the clamped path.
+  uint32_t kvo[2], vvo[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    kvo[q] = ((uint32_t)kkey[q] * DH + (uint32_t)kcol[q]) * 2;
+    vvo[q] = ((uint32_t)vrow[q] * Lu + (uint32_t)vcol) * 2;
+  }
+  const int nfull = (int)(L / BK);  // key tiles 0 .. nfull - 1 hold BK valid keys
   // piece 0, 1: K rows of copy instruction wave + 8 piece; piece 2, 3: V^T rows likewise
   auto copy_piece = [&](int u, int piece) {
     uint8_t *dst = smem + (u % NB) * STAGE;
-    if (piece < 2) {
+    if (piece < 2 && u < nfull) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,
+          (__attribute__((address_space(3))) void *)(dst + (wave + 8 * piece) * 1024), 16,
+          kvo[piece], (uint32_t)u * (BK * DH * 2), 0, 0);
+    } else if (piece >= 2 && (u >= 1 ? u - 1 : 0) < nfull) {
+      const uint32_t vt = u >= 1 ? (uint32_t)(u - 1) : 0u;  // V^T tile u - 1 (stage 0: tile 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs,
+          (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * (piece - 2)) * 1024),
+          16, vvo[piece - 2], vt * (BK * 2), 0, 0);
+    } else if (piece < 2) {
       const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;
       const uint32_t key = min(kt0 + (uint32_t)kkey[piece], Lu - 1u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,
