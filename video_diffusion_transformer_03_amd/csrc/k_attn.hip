@@ -322,16 +322,13 @@ __device__ __forceinline__ void s_tile(v4f (&s)[4][2], const v8bf (&qf)[2][4],
 }
 
 // P = exp2(S sl2 - m) rounded to bf16 (the P^T operand, keys 8g .. 8g+7 of each 32-key
-// step), l += sum of the rounded P. QPRE: S already holds the exponent (scaled scores
-// minus m), P = exp2(S).
+// step). QPRE: S already holds the exponent (scaled scores minus m), P = exp2(S).
 template <bool QPRE>
 __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
-                                         const float (&m)[2], float (&l)[2], float sl2) {
-  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+                                         const float (&m)[2], float sl2) {
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const float mneg = -m[qt];
-    float acc = l[qt];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float p[8];
@@ -350,21 +347,27 @@ __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
       u.y = pack_bf2(p[2], p[3]);
       u.z = pack_bf2(p[4], p[5]);
       u.w = pack_bf2(p[6], p[7]);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.x), ones, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.y), ones, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.z), ones, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.w), ones, acc, false);
       pb[ks][qt] = __builtin_bit_cast(v8bf, u);
     }
-    l[qt] = acc;
   }
 }
 
-// O^T += V^T P^T for one V^T tile
-__device__ __forceinline__ void pv_tile(v4f (&o)[8][2], const v8bf (&pb)[2][2],
+// Accumulator block NO = 8 of O^T holds the row sum: its V^T operand is all ones, so every
+// row of the block is the sum over keys of the rounded P the other blocks consume
+constexpr int NO = 9;
+__device__ __forceinline__ v8bf ones_frag() {
+  const __bf16 one = (__bf16)1.0f;
+  return v8bf{one, one, one, one, one, one, one, one};
+}
+
+// O^T += V^T P^T for one V^T tile (and the row-sum block)
+__device__ __forceinline__ void pv_tile(v4f (&o)[NO][2], const v8bf (&pb)[2][2],
                                         const uint8_t *vb, int voff) {
+  const v8bf ones = ones_frag();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
+    o[8][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][0], o[8][0], 0, 0, 0);
+    o[8][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][1], o[8][1], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const v8bf vf = *(const v8bf *)(vb + dt * 2048 + (voff ^ (ks * 64)));
@@ -449,20 +452,18 @@ __device__ __forceinline__ void shift_tile(v4f (&s)[4][2], const float (&shift)[
 constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
 
 // One slice of the softmax of a score tile: the pair of scores PART of query tile QT in
-// 32-key step KS -> two exp2, one bf16 pair packed into u[PART] (pb[KS][QT] once the four
-// parts are done), one dot2 of the rounded pair into the row sum.
+// 32-key step KS -> two exp2 and one bf16 pair packed into u[PART] (pb[KS][QT] once the four
+// parts are done). The row sum comes from the matrix cores (accumulator block 8).
 template <bool QPRE, int QT, int KS, int PART>
 __device__ __forceinline__ void softmax_slice(const v4f (&cur)[4][2], uint32_t (&u)[4],
-                                              float (&lacc)[2], v8bf (&pb)[2][2],
-                                              const float (&mneg)[2], float sl2) {
-  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+                                              v8bf (&pb)[2][2], const float (&mneg)[2],
+                                              float sl2) {
   constexpr int tt = 2 * KS + (PART >> 1), r0 = (PART & 1) * 2;
   const float p0 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][QT][r0])
                         : __builtin_amdgcn_exp2f(fmaf(cur[tt][QT][r0], sl2, mneg[QT]));
   const float p1 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][QT][r0 + 1])
                         : __builtin_amdgcn_exp2f(fmaf(cur[tt][QT][r0 + 1], sl2, mneg[QT]));
   u[PART] = pack_bf2(p0, p1);
-  lacc[QT] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u[PART]), ones, lacc[QT], false);
   if constexpr (PART == 3) pb[KS][QT] = __builtin_bit_cast(v8bf, make_uint4(u[0], u[1], u[2], u[3]));
 }
 
@@ -483,14 +484,12 @@ template <bool QPRE, typename CopyF>
 __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4][2],
                                             v8bf (&pb)[2][2], const v8bf (&qf)[2][4],
                                             const uint8_t *kb, int koff, const float (&m)[2],
-                                            const v4f (&cq)[2], float (&l)[2], float sl2,
-                                            CopyF &&copy_piece) {
+                                            const v4f (&cq)[2], float sl2, CopyF &&copy_piece) {
   v8bf kf[PD + 1];
   static_for<PD>([&](auto I) {
     kf[I] = *(const v8bf *)(kb + (I % 4) * 4096 + (koff ^ ((I / 4) * 64)));
   });
   const float mneg[2] = {-m[0], -m[1]};
-  float lacc[2] = {l[0], l[1]};
   uint32_t u[4];
   static_for<16>([&](auto I) {
     constexpr int i = I;
@@ -507,12 +506,10 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
                                                          kk ? nxt[t4][1] : (QPRE ? cq[1] : z), 0, 0, 0);
     if constexpr (i % 2 == 1) {
       constexpr int sl = i / 2;
-      softmax_slice<QPRE, sl / 4, 0, sl % 4>(cur, u, lacc, pb, mneg, sl2);
+      softmax_slice<QPRE, sl / 4, 0, sl % 4>(cur, u, pb, mneg, sl2);
     }
     __builtin_amdgcn_sched_barrier(0);
   });
-  l[0] = lacc[0];
-  l[1] = lacc[1];
 }
 
 // Phase 2, same shape: step i reads V^T fragment i + PD, issues the two MFMAs of fragment i
@@ -521,16 +518,16 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
 // 0 .. 7 also do the softmax slices of cur's last 32 keys (pb[1]), which the MFMAs of steps
 // 8 .. 15 consume.
 template <bool QPRE>
-__device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], v8bf (&pb)[2][2],
+__device__ __forceinline__ bool phase_pv_max(v4f (&o)[NO][2], v8bf (&pb)[2][2],
                                              const v4f (&nxt)[4][2], const v4f (&cur)[4][2],
                                              const uint8_t *vb, int voff, const float (&m)[2],
-                                             float (&mnew)[2], float (&l)[2], float sl2) {
+                                             float (&mnew)[2], float sl2) {
+  const v8bf ones = ones_frag();
   v8bf vf[PD + 1];
   static_for<PD>([&](auto I) {
     vf[I] = *(const v8bf *)(vb + (I % 8) * 2048 + (voff ^ ((I / 8) * 64)));
   });
   const float mneg[2] = {-m[0], -m[1]};
-  float lacc[2] = {l[0], l[1]};
   uint32_t u[4];
   float mx = 0.f;
   bool grow = false;
@@ -543,7 +540,11 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], v8bf (&pb)[2][2],
     const v8bf v = vf[i % (PD + 1)];
     o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][0], o[dt][0], 0, 0, 0);
     o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][1], o[dt][1], 0, 0, 0);
-    if constexpr (i < 8) softmax_slice<QPRE, i / 4, 1, i % 4>(cur, u, lacc, pb, mneg, sl2);
+    if constexpr (i < 8) softmax_slice<QPRE, i / 4, 1, i % 4>(cur, u, pb, mneg, sl2);
+    if constexpr (dt == 7) {  // row sums of this key step's P
+      o[8][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][0], o[8][0], 0, 0, 0);
+      o[8][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][1], o[8][1], 0, 0, 0);
+    }
     constexpr int qt = i / 8, st = i % 8;  // scores 2 st, 2 st + 1 of query tile qt
     const float a0 = nxt[st >> 1][qt][(st & 1) * 2], a1 = nxt[st >> 1][qt][(st & 1) * 2 + 1];
     if constexpr (st == 0)
@@ -562,8 +563,6 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[8][2], v8bf (&pb)[2][2],
     }
     __builtin_amdgcn_sched_barrier(0);
   });
-  l[0] = lacc[0];
-  l[1] = lacc[1];
   return grow;
 }
 
@@ -580,13 +579,11 @@ __device__ __forceinline__ void mask_tile(v4f (&s)[4][2], int g, int kmax) {
   }
 }
 
-__device__ __forceinline__ void rescale(v4f (&o)[8][2], float (&l)[2], const float (&alpha)[2]) {
+__device__ __forceinline__ void rescale(v4f (&o)[NO][2], const float (&alpha)[2]) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    l[qt] *= alpha[qt];
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt][qt] *= alpha[qt];
-  }
+    for (int dt = 0; dt < NO; ++dt) o[dt][qt] *= alpha[qt];
 }
 }  // namespace v2
 
@@ -690,10 +687,10 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   const int koff = c16 * 256 + ((g ^ c16) * 16);
   const int voff = K_BYTES + c16 * 128 + ((g ^ (c16 & 7)) * 16);
 
-  v4f o[8][2];
+  v4f o[NO][2];  // O^T blocks 0..7, row sums in block 8
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i][0] = o[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f};
+  for (int i = 0; i < NO; ++i) o[i][0] = o[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, alpha[2] = {1.f, 1.f};
   float shift[2] = {0.f, 0.f};
   v4f cq[2];  // QPRE: the C operand {-m, -m, -m, -m} each new S tile starts from
   v4f sa[4][2], sb[4][2];
@@ -732,18 +729,18 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
     const int jj = (j_);                                                                       \
     const uint8_t *sb_ = smem + ((jj + 1) % NB) * STAGE;                                       \
     if (pend) {                                                                                \
-      rescale(o, l, alpha);                                                                    \
+      rescale(o, alpha);                                                                       \
       if constexpr (QPRE) {                                                                    \
         shift_tile(CUR, shift);                                                                \
         _Pragma("unroll") for (int qt = 0; qt < 2; ++qt)                                       \
           cq[qt] = v4f{-m[qt], -m[qt], -m[qt], -m[qt]};                                        \
       }                                                                                        \
     }                                                                                          \
-    phase_s_exp<QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, l, sl2, [&](int pc) {                \
+    phase_s_exp<QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, sl2, [&](int pc) {                   \
       if (jj + DIST <= nkt) copy_piece(jj + DIST, pc);                                         \
     });                                                                                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
-    const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, l, sl2);        \
+    const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, sl2);           \
     pend = rescale_decision<QPRE>(grow_, mnew, m, alpha, shift);                               \
     if (jj + DIST <= nkt)                                                                      \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
@@ -755,10 +752,10 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   {                                                                                            \
     const uint8_t *sb_ = smem + (nkt % NB) * STAGE;                                            \
     if (pend) {                                                                                \
-      rescale(o, l, alpha);                                                                    \
+      rescale(o, alpha);                                                                       \
       if constexpr (QPRE) shift_tile(CUR, shift);                                              \
     }                                                                                          \
-    exp_tile<QPRE>(CUR, pb, m, l, sl2);                                                        \
+    exp_tile<QPRE>(CUR, pb, m, sl2);                                                           \
     pv_tile(o, pb, sb_, voff);                                                                 \
   }
   // nkt - 1 iterations in pairs (the score tiles swap roles); only the last iteration, whose
@@ -789,9 +786,7 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   const int64_t ldo = (int64_t)H * DH;
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    float lt = l[qt];
-    lt = rows_sum(lt);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / o[8][qt][0];  // every lane's block-8 values are its query's row sum
     const int64_t qi = q0 + qt * 16 + c16;
     if (qi < L) {
       const int64_t obase = qi * ldo + (int64_t)head * DH + g * 4;
