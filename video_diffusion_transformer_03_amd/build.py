@@ -22,11 +22,15 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-result",
 ]
+# Per-source flags. Attention takes row maxima of matrix-core results, which the compiler
+# would otherwise quiet (a self-max per value, against signalling NaNs) before each max;
+# its inputs are finite and -inf is still honoured.
+EXTRA = {"k_attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, build_dir: str) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
