@@ -126,6 +126,30 @@ def test_attention_bf16(H, L, Dh):
     assert err < 1e-2, err
 
 
+@pytest.mark.parametrize("Dh", [64, 128])
+def test_attention_running_max_per_query_tile(Dh):
+    # Some queries' scores climb to ~460 (in log2 units) over the keys, the others' fall: the
+    # running maximum of the climbing rows must move many times, tile by tile, and a maximum
+    # taken from the wrong query (another 16-query tile, or another column of one) would
+    # overflow exp2 (inf / NaN). Query l climbs iff (l % 32 < 16) differs from (l % 16 < 8),
+    # so neighbouring tiles and the two halves of a tile have opposite signs.
+    L = 1024
+    q = torch.zeros((1, L, Dh))
+    k = torch.zeros((1, L, Dh))
+    l = torch.arange(L)
+    sign = torch.where(((l % 32) < 16) != ((l % 16) < 8), 1.0, -1.0)
+    q[0, :, 0] = 60.0 * sign
+    k[0, :, 0] = 60.0 * torch.arange(L) / L
+    v = randn((1, L, Dh), 27, 1.0)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    vt = v.transpose(1, 2).contiguous()
+    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).float().cpu().numpy()
+    assert np.all(np.isfinite(o))
+    ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
+                      np64(v).transpose(1, 0, 2)).reshape(L, Dh)
+    assert rel_l2(o, ref) < 1e-2
+
+
 @pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 264, 128)])
 def test_attention_fp32(H, L, Dh):
     q = randn((H, L, Dh), 31, 1.0, torch.float32)
