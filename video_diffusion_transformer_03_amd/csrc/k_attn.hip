@@ -280,15 +280,18 @@ __global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
 // inside each wave, the matrix-core products of one tile with the softmax arithmetic of
 // another (a wave's own VALU work issues between its MFMAs; work of a second wave on the
 // same SIMD overlaps far less):
-//   phase 1: S(j+1) = K(j+1) Q^T        with  P(j) = exp2(S(j) - m), row sums
-//   phase 2: O += V(j) P(j)^T           with  row maximum of S(j+1), rescale decision
-// The O / l rescale a new maximum calls for is applied at the start of the next iteration,
-// after phase 2 has added the tile scaled by the old maximum.
+//   phase 1: S(j+1) = K(j+1) Q^T        with  P(j) = exp2(S(j) - m) of its first 32 keys
+//   phase 2: O += V(j) P(j)^T           with  P(j) of its last 32 keys, row maximum of
+//                                             S(j+1), rescale decision
+// The row sums l come out of phase 2's matrix-core work (an extra accumulator block with
+// an all-ones V^T operand). The O / l rescale a new maximum calls for is applied at the
+// start of the next iteration, after phase 2 has added the tile scaled by the old maximum.
 //
 // K and V^T tiles reach LDS through direct global -> LDS copies into four resident
 // stages; stage u holds K tile u and V^T tile u - 1 (what iteration u - 1 reads), and
-// iteration j issues the copies of stage j + 4. LDS layouts (16-byte chunks, XOR swizzles keep fragment reads free of bank
-// conflicts; every copy instruction fills 1 KB and reads whole 128-byte lines):
+// iteration j issues the copies of stage j + 4. LDS layouts (16-byte chunks, XOR swizzles
+// keep fragment reads free of bank conflicts; every copy instruction fills 1 KB and reads
+// whole 128-byte lines):
 //   K   64 rows x 256 B: row R holds key kof(R) of the tile (the kperm order above), chunk
 //       c at position c ^ (R % 16)
 //   V^T 128 rows (head dims) x 128 B (64 keys): chunk c at position c ^ (R % 8)
