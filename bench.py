@@ -95,7 +95,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block_l16384")
     ap.add_argument("--variant", default="w8a8", choices=["w8a8", "bf16gemm", "fp32"])
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the 50-block stack and L=65536 measurements")
