@@ -153,8 +153,14 @@ template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
                                               int n_base, int64_t m_base, int lane,
                                               uint8_t *stage) {
-  constexpr int PF = (EPI == EPI_QKV || RESF32) ? 1 : 2;  // column blocks loaded ahead
   constexpr bool STAGED = !OUTF32 && EPI != EPI_RAW_I32;
+  // A bf16 residual is read in whole lines too: each 64-channel slice of it is loaded 16
+  // bytes per lane in the row order of the stage, written into the stage, and each chunk
+  // reads its residual from the stage position its output then overwrites (same lane).
+  // The next slice's lines are loaded during the second half of the current slice.
+  constexpr bool LRES = STAGED && EPI == EPI_RESID && !RESF32;
+  // column blocks whose per-channel operands are loaded ahead
+  constexpr int PF = (EPI == EPI_QKV || RESF32 || LRES) ? 1 : 2;
   // QKV: the wave's 128 channels lie in one section (d % 128 == 0); V^T is stored transposed
   const int sec = EPI == EPI_QKV ? n_base / a.d : 0;
   const bool vsec = EPI == EPI_QKV && sec == 2;
@@ -192,6 +198,21 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
       }
     }
   };
+  v4i rl[LRES ? 8 : 1];  // residual lines of one slice: rows 8 k + lane / 8, bytes 16 (lane % 8)
+  auto load_res_slice = [&](int sl) {
+    static_for<LRES ? 8 : 0>([&](auto K) {
+      constexpr int k = K;
+      const int64_t m = m_base + k * 8 + (lane >> 3);
+      rl[k] = *(const v4i *)((const uint16_t *)a.res + (m < a.M ? m : a.M - 1) * a.N + n_base +
+                             sl * 64 + (lane & 7) * 8);
+    });
+  };
+  auto put_res_slice = [&]() {
+    static_for<LRES ? 8 : 0>([&](auto K) {
+      constexpr int k = K;
+      *(v4i *)(stage + (k * 8 + (lane >> 3)) * kStagePitch + (lane & 7) * 16) = rl[k];
+    });
+  };
   // bf16 values of column block i, token tile j (channels 4 (lane >> 4) .. + 3 of the block)
   auto stage_vals = [&](int i, int j, const float (&v)[4]) {
     const int t = j * 16 + (lane & 15);           // token within the wave's 64
@@ -227,7 +248,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
       const float4 g4 = *(const float4 *)(a.gate + n);
       c.g[0] = g4.x; c.g[1] = g4.y; c.g[2] = g4.z; c.g[3] = g4.w;
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
+      for (int j = 0; j < (LRES ? 0 : TM); ++j) {
         if constexpr (RESF32) {
           const uint4 u = *(const uint4 *)((const float *)a.res + mrow[j] * a.N + n);
           c.r[j][0] = u.x; c.r[j][1] = u.y; c.r[j][2] = u.z; c.r[j][3] = u.w;
@@ -329,7 +350,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
           emit(i, j, v);
         } else if constexpr (EPI == EPI_RESID) {
           float r4[4];
-          if constexpr (RESF32) {
+          if constexpr (LRES) {
+            const int t = j * 16 + (lane & 15), cb = (i & 3) * 16 + (lane >> 4) * 4;
+            const uint2 u = *(const uint2 *)(stage + t * kStagePitch + cb * 2);
+            r4[0] = __uint_as_float(u.x << 16);
+            r4[1] = __uint_as_float(u.x & 0xffff0000u);
+            r4[2] = __uint_as_float(u.y << 16);
+            r4[3] = __uint_as_float(u.y & 0xffff0000u);
+          } else if constexpr (RESF32) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) r4[r] = __uint_as_float(c.r[j][r]);
           } else {
@@ -347,9 +375,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
   };
 
   EpiChunk<TM, RESF32> buf[PF + 1];
+  if constexpr (LRES) load_res_slice(0);
   static_for<PF>([&](auto I) { load_chunk(buf[I], I); });
   static_for<TN>([&](auto I) {
     constexpr int i = I;
+    // this slice's residual into the stage; the next slice's loads once two column blocks
+    // have freed their accumulator registers
+    if constexpr (LRES && (i & 3) == 0) put_res_slice();
+    if constexpr (LRES && (i & 3) == 2 && i + 2 < TN) load_res_slice(i / 4 + 1);
     if constexpr (i + PF < TN) load_chunk(buf[(i + PF) % (PF + 1)], i + PF);
     store_chunk(buf[i % (PF + 1)], i);
     if constexpr (STAGED && (i & 3) == 3) stage_flush(n_base + (i - 3) * 16);
