@@ -422,11 +422,21 @@ __device__ __forceinline__ bool max_vals(v4f (&s)[4][2], const float (&m)[2], fl
 // by more than 2^8 (P then stays <= 256). Returns whether any row of the wave moved
 // (alpha then holds the factors for O and l; QPRE: shift holds how far m moved, to be
 // taken off the pending score tile, which was formed relative to the old m).
-template <bool QPRE>
-__device__ __forceinline__ bool rescale_decision(bool grow, const float (&mnew)[2],
+// PART: mnew holds each lane's partial maximum over its own keys and grow that lane's
+// test; a row's maximum exceeds the bound exactly when one of its lanes' partials does,
+// so the cross-lane reduction runs only when some lane of the wave saw growth.
+template <bool QPRE, bool PART = false>
+__device__ __forceinline__ bool rescale_decision(bool grow, float (&mnew)[2],
                                                  float (&m)[2], float (&alpha)[2],
-                                                 float (&shift)[2]) {
+                                                 float (&shift)[2], float sl2 = 1.f) {
   if (!(__builtin_amdgcn_read_exec() & __ballot(grow))) return false;
+  if constexpr (PART) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      mnew[qt] = rows_max(mnew[qt]);
+      if constexpr (!QPRE) mnew[qt] *= sl2;
+    }
+  }
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     if constexpr (QPRE) {
@@ -516,8 +526,8 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
 }
 
 // Phase 2, same shape: step i reads V^T fragment i + PD, issues the two MFMAs of fragment i
-// (head-dim tile dt = i % 8, key step ks = i / 8) into o, and advances the row maximum of
-// nxt (query tile i / 8, two scores per step; the cross-lane part ends each half). Steps
+// (head-dim tile dt = i % 8, key step ks = i / 8) into o, and advances the lane's partial
+// row maximum of nxt (query tile i / 8, two scores per step). Steps
 // 0 .. 7 also do the softmax slices of cur's last 32 keys (pb[1]), which the MFMAs of steps
 // 8 .. 15 consume.
 template <bool QPRE>
@@ -554,15 +564,12 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[NO][2], v8bf (&pb)[2][2],
       mx = fmaxf(a0, a1);
     else
       mx = fmaxf(fmaxf(mx, a0), a1);
-    if constexpr (st == 7) {
-      mx = rows_max(mx);
-      if constexpr (QPRE) {
-        mnew[qt] = mx;
+    if constexpr (st == 7) {  // the lane's partial maximum and its own test (see rescale_decision)
+      mnew[qt] = mx;
+      if constexpr (QPRE)
         grow |= mx > kRescaleLog2;
-      } else {
-        mnew[qt] = mx * sl2;
-        grow |= mnew[qt] > m[qt] + kRescaleLog2;
-      }
+      else
+        grow |= mx * sl2 > m[qt] + kRescaleLog2;
     }
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -744,7 +751,7 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
     });                                                                                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
     const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, sl2);           \
-    pend = rescale_decision<QPRE>(grow_, mnew, m, alpha, shift);                               \
+    pend = rescale_decision<QPRE, true>(grow_, mnew, m, alpha, shift, sl2);                    \
     if (jj + DIST <= nkt)                                                                      \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
     else                                                                                       \
