@@ -182,8 +182,10 @@ def main():
                            frac=round(rate / HBM_GBS, 4))
         kernels[name] = ent
 
+    label = {"w8a8": "W8A8", "bf16gemm": "BF16", "fp32": "int8 GEMM + fp32"}[args.variant]
     result = {
-        "metric": "DiT block tokens/s (W8A8, d=5120, L=16384) + % of peak int8/bf16 MFMA",
+        # the headline workload's metric name; other workloads and variants say what ran
+        "metric": f"DiT block tokens/s ({label}, d={wl.d}, L={L}) + % of peak int8/bf16 MFMA",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
