@@ -25,7 +25,6 @@ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // fp32 -> bf16, round to nearest even (hardware conversion on gfx950)
 __device__ __forceinline__ uint16_t f2bf(float f) {
   __bf16 h = (__bf16)f;

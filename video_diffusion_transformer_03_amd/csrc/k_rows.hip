@@ -144,15 +144,8 @@ __device__ __forceinline__ void load8(const float *p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// streaming variants for inputs read exactly once (nontemporal: no cache allocation)
-__device__ __forceinline__ void load8_nt(const uint16_t *p, float v[8]) {
-  const v4u u = __builtin_nontemporal_load((const v4u *)p);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    v[2 * t] = __uint_as_float(u[t] << 16);
-    v[2 * t + 1] = __uint_as_float(u[t] & 0xffff0000u);
-  }
-}
+// streaming variant for fp32 inputs read exactly once (nontemporal: no cache allocation);
+// bf16 rows of the quantisers stay packed and load their own way
 __device__ __forceinline__ void load8_nt(const float *p, float v[8]) {
   const v4f a = __builtin_nontemporal_load((const v4f *)p);
   const v4f b = __builtin_nontemporal_load((const v4f *)(p + 4));
