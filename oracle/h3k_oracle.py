@@ -115,6 +115,11 @@ def adaln_modulation(w_ada, cond) -> np.ndarray:
     return np.asarray(w_ada, np.float64) @ np.asarray(cond, np.float64)
 
 
+def round_f32(v) -> np.ndarray:
+    """Round to the nearest fp32 value (RNE), returned as fp64."""
+    return np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+
+
 def split_modulation(m, d: int) -> Dict[str, np.ndarray]:
     names = ("shift1", "scale1", "gate1", "shift2", "scale2", "gate2")
     return {k: m[i * d:(i + 1) * d] for i, k in enumerate(names)}
@@ -282,7 +287,8 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     x = np.asarray(x, np.float64)
     L, d = x.shape
     assert d == n_heads * head_dim and L == grid[0] * grid[1] * grid[2]
-    mod = split_modulation(adaln_modulation(w["w_ada"], cond), d)
+    # the modulation is stored as an fp32 vector for the kernels that use it
+    mod = split_modulation(round_f32(adaln_modulation(w["w_ada"], cond)), d)
     h = modulate(layer_norm(x, eps), mod["shift1"], mod["scale1"])
     y = _linear(h, w, "_qkv", variant, dense_inputs)
     q = y[:, 0:d].reshape(L, n_heads, head_dim)

@@ -107,3 +107,47 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     print(label or wl.name, {k: (f"{v:.3e}" if isinstance(v, float) else v) for k, v in stats.items()})
     assert stats["x2"] < (1e-6 if f32 else 4e-3), stats
     return stats
+
+
+def code_forced_output(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0):
+    """The oracle's block output on `rows` with every quantiser's integer codes taken from
+    the GPU run in `r` (qa for all tokens, qo, qa2 and qg for `rows`); everything else (scales,
+    int8 products, RoPE, attention, LayerNorm, GELU, residuals) is the oracle's own. Codes may
+    legitimately differ at near-ties between fp32 and fp64 inputs; forcing them isolates the
+    float arithmetic of the path from the way a flipped code spreads (a flipped code changes a
+    token's Q, K and V, and attention hands that to every query). On the bf16 path the same
+    tensors are rounded to bf16 as the path stores them."""
+    grid = wl.grid if grid is None else grid
+    L = grid[0] * grid[1] * grid[2]
+    d, F, H, Dh = wl.d, wl.d_ff, wl.n_heads, wl.head_dim
+    f32 = bool(r["flags"] & h3k.F_FP32_DEBUG)
+    rb = (lambda t: t) if f32 else O.round_bf16
+    ws, lay = r["ws"], r["lay"]
+    V = lambda n, dt, shape: h3k.ws_view(ws, lay, n, dt, shape)
+    w = oracle_weights(r["bw"])
+    rows = np.asarray(rows)
+    tq = torch.as_tensor(rows, device="cuda")
+    codes = lambda n, cols: V(n, torch.int8, (L, cols))[tq].cpu().numpy()
+
+    mod = O.split_modulation(O.adaln_modulation(w["w_ada"], np64(r["c"])), d)
+    x = np64(r["x"])
+    _, sa = O.quantize_rows(O.modulate(O.layer_norm(x), mod["shift1"], mod["scale1"]))
+    qa = V("qa", torch.int8, (L, d)).cpu().numpy()
+    y = O.int8_matmul(qa, w["q_qkv"]) * sa.astype(np.float64)[:, None] * w["s_qkv"]
+    ang = O.rope_angles(O.token_positions(grid, w_scale, w_offset), Dh)
+    q = O.apply_rope(y[:, :d].reshape(L, H, Dh), ang)
+    k = O.apply_rope(y[:, d:2 * d].reshape(L, H, Dh), ang)
+    v = y[:, 2 * d:].reshape(L, H, Dh)
+    if not f32:
+        c = O.q_handoff_scale(Dh)
+        q, k, v = O.round_bf16(q * c) / c, O.round_bf16(k), O.round_bf16(v)
+    o = rb(O.attention(q, k, v, rows).reshape(len(rows), d))
+    _, so = O.quantize_rows(o)
+    x1 = rb(x[rows] + mod["gate1"] * (O.int8_matmul(codes("qo", d), w["q_o"]) *
+                                      so.astype(np.float64)[:, None] * w["s_o"]))
+    _, sa2 = O.quantize_rows(O.modulate(O.layer_norm(x1), mod["shift2"], mod["scale2"]))
+    g = rb(O.gelu(O.int8_matmul(codes("qa2", d), w["q_up"]) * sa2.astype(np.float64)[:, None] *
+                  w["s_up"]))
+    _, sg = O.quantize_rows(g)
+    return rb(x1 + mod["gate2"] * (O.int8_matmul(codes("qg", F), w["q_down"]) *
+                                   sg.astype(np.float64)[:, None] * w["s_down"]))

@@ -224,7 +224,8 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_de
         return rb(vals) if round_store else vals
     L, d = len(x), len(x[0])
     F = len(w["w_up"])
-    m = [math.fsum(w["w_ada"][i][j] * c[j] for j in range(len(c))) for i in range(6 * d)]
+    # the modulation is stored as fp32 (nearest, ties to even)
+    m = [float(np.float32(math.fsum(w["w_ada"][i][j] * c[j] for j in range(len(c))))) for i in range(6 * d)]
     sh1, sc1, g1, sh2, sc2, g2 = (m[i * d:(i + 1) * d] for i in range(6))
 
     def ln_mod(row, sh, sc):

@@ -213,7 +213,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
 
   {
     Launch l(H3K_K_ADALN, s, flags);
-    if ((rc = l.done(launch_adaln(w->w_ada, cond, m, 6 * (int64_t)d, dm->d_cond, s), fn, "adaln"))) return rc;
+    if ((rc = l.done(launch_adaln(w->w_ada, cond, m, 6 * (int64_t)d, dm->d_cond, f32, s), fn, "adaln"))) return rc;
   }
   RopeGeom rg = rope_geom(Dh, T, Hg, Wg, w_scale, w_offset);
   {
@@ -657,7 +657,7 @@ int h3k_adaln_modulation(const uint16_t *w_ada, const float *cond, float *m, int
   H3K_CHECK_PTR(m);
   if (n_out <= 0 || d_cond <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
   if (d_cond % 8 || d_cond > 8192) return fail(H3K_EUNSUPPORTED, "%s: d_cond must be a multiple of 8, <= 8192", fn);
-  hipError_t e = launch_adaln(w_ada, cond, m, n_out, d_cond, (hipStream_t)stream);
+  hipError_t e = launch_adaln(w_ada, cond, m, n_out, d_cond, false, (hipStream_t)stream);
   if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return H3K_OK;
 }

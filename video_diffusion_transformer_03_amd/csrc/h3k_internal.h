@@ -98,7 +98,7 @@ size_t rope_table_entries(const RopeGeom &g);
 // all return hipError_t of the launch (hipGetLastError)
 hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStream_t s);
 hipError_t launch_adaln(const uint16_t *w, const float *c, float *m, int64_t n_out, int dc,
-                        hipStream_t s);
+                        bool f64, hipStream_t s);
 // mode: 0 = LN + modulate + int8 quant, 1 = LN + modulate -> bf16, 2 = int8 quant only
 hipError_t launch_rows(int mode, const void *x, bool x_f32, const float *shift,
                        const float *scale, int64_t rows, int cols, float eps, int8_t *q,

@@ -62,10 +62,19 @@ hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStr
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // ============================================================== AdaLN GEMV
+// sum over the 64 lanes of a wave in fp64 (lane shuffles; fp64 paths only)
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 // m[i] = sum_j W[i, j] c[j]. One wave per output row; each lane keeps the slice of c
 // it multiplies in registers (MAXC 16-byte chunks of W per lane). W is read once, with
 // nontemporal loads (12% faster than cached loads at 6d x d_c = 30720 x 5120).
-template <int MAXC>
+// F64: products and sums in fp64 (a bf16 x fp32 product is exact there), one rounding to
+// fp32 at the end, so m is the fp32 value nearest the exact sum (fp32 debug path).
+template <int MAXC, bool F64>
 __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t *__restrict__ W,
                                                     const float *__restrict__ c,
                                                     float *__restrict__ m, int64_t n_out,
@@ -92,6 +101,7 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t *__restrict__
     if (row >= n_out) break;
     const uint16_t *wr = W + row * dc;
     float acc = 0.f;
+    double acc64 = 0.0;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       int ch = lane + 64 * i;
@@ -100,28 +110,34 @@ __global__ __launch_bounds__(256) void adaln_kernel(const uint16_t *__restrict__
         const uint32_t w4[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          acc = fmaf(__uint_as_float(w4[t] << 16), cv[i][2 * t], acc);
-          acc = fmaf(__uint_as_float(w4[t] & 0xffff0000u), cv[i][2 * t + 1], acc);
+          if constexpr (F64) {
+            acc64 = fma((double)__uint_as_float(w4[t] << 16), (double)cv[i][2 * t], acc64);
+            acc64 = fma((double)__uint_as_float(w4[t] & 0xffff0000u), (double)cv[i][2 * t + 1], acc64);
+          } else {
+            acc = fmaf(__uint_as_float(w4[t] << 16), cv[i][2 * t], acc);
+            acc = fmaf(__uint_as_float(w4[t] & 0xffff0000u), cv[i][2 * t + 1], acc);
+          }
         }
       }
     }
-    acc = wave_sum(acc);
+    if constexpr (F64) acc = (float)wave_sum_f64(acc64);
+    else acc = wave_sum(acc);
     if (lane == 0) m[row] = acc;
   }
 }
 
 hipError_t launch_adaln(const uint16_t *w, const float *c, float *m, int64_t n_out, int dc,
-                        hipStream_t s) {
+                        bool f64, hipStream_t s) {
   const int rpw = 4;
   int64_t waves = (n_out + rpw - 1) / rpw;
   dim3 grid((unsigned)((waves + 3) / 4));
   int maxc = (dc / 8 + 63) / 64;
   if (maxc <= 4)
-    adaln_kernel<4><<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
+    (f64 ? adaln_kernel<4, true> : adaln_kernel<4, false>)<<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
   else if (maxc <= 10)
-    adaln_kernel<10><<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
+    (f64 ? adaln_kernel<10, true> : adaln_kernel<10, false>)<<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
   else
-    adaln_kernel<16><<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
+    (f64 ? adaln_kernel<16, true> : adaln_kernel<16, false>)<<<grid, 256, 0, s>>>(w, c, m, n_out, dc, rpw);
   return hipGetLastError();
 }
 
@@ -174,6 +190,25 @@ __device__ __forceinline__ float group_reduce(float v, bool is_max, float *red) 
   }
 }
 
+// sum over the WPR waves of a row in fp64 (shuffles within a wave, then LDS)
+template <int WPR>
+__device__ __forceinline__ double group_sum_f64(double v, double *red) {
+  v = wave_sum_f64(v);
+  if constexpr (WPR == 1) {
+    return v;
+  } else {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();  // earlier readers of red are done
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const int g0 = (wave / WPR) * WPR;
+    double r = red[g0];
+#pragma unroll
+    for (int j = 1; j < WPR; ++j) r += red[g0 + j];
+    return r;
+  }
+}
+
 enum { RM_LNQ = 0, RM_LN_BF16 = 1, RM_Q = 2 };
 
 template <int MODE, typename Tin, int WPR, int MAXV>
@@ -185,6 +220,11 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
                                                   float *__restrict__ sc,
                                                   uint16_t *__restrict__ hout) {
   __shared__ float red[4];
+  // fp32 rows of the LayerNorm quantiser (fp32 debug path): mean, variance and modulation in
+  // fp64, one rounding of h to fp32 before the quantiser, so that h is the fp32 value
+  // nearest the exact one and the codes do not depend on the summation order
+  constexpr bool F64 = std::is_same<Tin, float>::value && MODE == RM_LNQ;
+  __shared__ double red64[F64 ? 4 : 1];
   // one-wave rows (d <= 5120): the block's four rows share shift and scale through LDS, so
   // each row reads them from L2 a quarter as often and their loads overlap the row's
   constexpr bool LDSP = (MODE == RM_LNQ || MODE == RM_LN_BF16) && WPR == 1 && MAXV <= 10;
@@ -239,7 +279,52 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
     __syncthreads();
   }
 
-  if constexpr (MODE == RM_LNQ || MODE == RM_LN_BF16) {
+  if constexpr (F64) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) s += (double)v[i][t];
+    const double mean = group_sum_f64<WPR>(s, red64) / (double)cols;
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      int c = tid + i * NT;
+      if (c < nvec) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const double dlt = (double)v[i][t] - mean;
+          ss = fma(dlt, dlt, ss);
+        }
+      }
+    }
+    const double var = group_sum_f64<WPR>(ss, red64) / (double)cols;
+    const double rstd = 1.0 / sqrt(var + (double)eps);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      int c = tid + i * NT;
+      if (c < nvec) {
+        float sh[8], sca[8];
+        if constexpr (LDSP) {
+          const float4 a0 = lss[c], a1 = lss[LP + c];
+          const float4 b0 = lss[2 * LP + c], b1 = lss[3 * LP + c];
+          sh[0] = a0.x; sh[1] = a0.y; sh[2] = a0.z; sh[3] = a0.w;
+          sh[4] = a1.x; sh[5] = a1.y; sh[6] = a1.z; sh[7] = a1.w;
+          sca[0] = b0.x; sca[1] = b0.y; sca[2] = b0.z; sca[3] = b0.w;
+          sca[4] = b1.x; sca[5] = b1.y; sca[6] = b1.z; sca[7] = b1.w;
+        } else {
+          load8(shift + c * 8, sh);
+          load8(scale + c * 8, sca);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          v[i][t] = (float)(((double)v[i][t] - mean) * rstd * (1.0 + (double)sca[t]) + (double)sh[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[i][t] = 0.f;
+      }
+    }
+  } else if constexpr (MODE == RM_LNQ || MODE == RM_LN_BF16) {
     float s = 0.f;
     if constexpr (PACKED) {
       // pairs of bf16 summed exactly by a dot product with (1, 1)
