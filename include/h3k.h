@@ -70,7 +70,9 @@ enum {
   H3K_F_BF16_GEMM = 1u,  /* no activation quantisation: bf16 x bf16 GEMMs on the dense
                             bf16 weights wb_* (the pages' BF16 baseline)              */
   H3K_F_FP32_DEBUG = 2u, /* fp32 activations end to end (x_in/x_out fp32), same int8
-                            GEMMs, fp32 attention without matrix cores               */
+                            GEMMs, fp32 attention without matrix cores; the AdaLN
+                            modulation and the LayerNorm statistics are computed in
+                            fp64 and rounded to fp32 once                             */
   H3K_F_SYNC = 4u,       /* synchronise the stream and check for errors after every
                             launch (debugging)                                        */
   /* Per-projection precision, for the pages' precision series (BF16 -> int8 MLP -> int8
