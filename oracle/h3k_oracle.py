@@ -280,6 +280,8 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     g and the block output exact; "bf16" rounds each of them to bfloat16 where it is
     produced, as on a path whose kernels hand each other bf16 activation tensors (the
     same two passages: bf16 tensors between the int8/bf16 projections and attention).
+    "fp32" (attn_inputs and act_store): the same tensors rounded to fp32 (Q unscaled), as a
+    path that computes in higher precision and stores fp32 tensors hands them over.
 
     rows: token rows whose output is wanted (all if None). Q, K and V are formed for
     every token (attention needs them); everything after attention is per token and is
@@ -300,11 +302,15 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     if attn_inputs == "bf16":
         c = q_handoff_scale(head_dim)
         q, k, v = round_bf16(q * c) / c, round_bf16(k), round_bf16(v)
+    elif attn_inputs == "fp32":
+        q, k, v = round_f32(q), round_f32(k), round_f32(v)
     elif attn_inputs != "fp64":
         raise ValueError(attn_inputs)
     sel = np.arange(L) if rows is None else np.asarray(rows)
     if act_store == "bf16":
         store = round_bf16
+    elif act_store == "fp32":
+        store = round_f32
     elif act_store == "fp64":
         store = lambda t: t
     else:

@@ -207,14 +207,17 @@ def test_gelu_textbook():
 
 # ----------------------------------------------------------------------------- block (brute force)
 def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_dense=False,
-              round_qkv=False, round_store=False):
+              round_qkv=False, round_store=False, f32=False):
     """Independent scalar-loop implementation of the block on tiny shapes. round_dense:
     dense projections take bf16-rounded activations; round_qkv: Q, K (after RoPE) and V are
     rounded to bf16 before attention; round_store: the attention output, the residual after
     the attention half, the GELU output and the block output are rounded to bf16 where they
-    are produced. Every rounding is torch's RNE conversion."""
+    are produced. Every rounding is torch's RNE conversion; f32: round_qkv and round_store
+    round to fp32 instead (Q without the softmax scale)."""
 
     def rb(vals):
+        if f32:
+            return [float(np.float32(t)) for t in vals]
         return torch.tensor(vals, dtype=torch.float64).to(torch.bfloat16).double().tolist()
 
     def rq(vals):
@@ -284,6 +287,8 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_de
     cq = 1.0 / (math.sqrt(Dh) * math.log(2.0))
 
     def rqs(vals):
+        if f32:
+            return rq(vals)
         return [t / cq for t in rb([t * cq for t in vals])] if round_qkv else vals
 
     Q = [[rqs(rope(qkv[l][e * Dh:(e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
@@ -357,7 +362,8 @@ def test_block_bruteforce_dense_bf16_inputs(variant):
 
 
 @pytest.mark.parametrize("variant", ["w8a8", "bf16gemm"])
-@pytest.mark.parametrize("attn_inputs,act_store", [("bf16", "fp64"), ("fp64", "bf16"), ("bf16", "bf16")])
+@pytest.mark.parametrize("attn_inputs,act_store", [("bf16", "fp64"), ("fp64", "bf16"), ("bf16", "bf16"),
+                                                   ("fp32", "fp32")])
 def test_block_bruteforce_bf16_handoffs(variant, attn_inputs, act_store):
     d, H, Dh, F, dc, grid = 12, 2, 6, 24, 5, (2, 2, 2)
     w = _tiny_weights(d, F, dc, 13)
@@ -366,20 +372,23 @@ def test_block_bruteforce_bf16_handoffs(variant, attn_inputs, act_store):
     c = r.standard_normal(dc)
     got = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
                           attn_inputs=attn_inputs, act_store=act_store)
+    f32 = attn_inputs == "fp32"
     ref = _bf_block(x.tolist(), c.tolist(), {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()},
-                    H, Dh, grid, variant, round_qkv=attn_inputs == "bf16", round_store=act_store == "bf16")
+                    H, Dh, grid, variant, round_qkv=attn_inputs != "fp64", round_store=act_store != "fp64",
+                    f32=f32)
     assert np.allclose(got, ref, rtol=1e-9, atol=1e-9)
     plain = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant)
     assert not np.allclose(got, plain, rtol=1e-9, atol=1e-9)
-    if act_store == "bf16":
-        assert np.array_equal(got, O.round_bf16(got))
+    rnd = O.round_f32 if act_store == "fp32" else O.round_bf16
+    if act_store != "fp64":
+        assert np.array_equal(got, rnd(got))
     # the stored intermediates are bf16 values and x2 is built from them
     x2, parts = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
                                 attn_inputs=attn_inputs, act_store=act_store, return_parts=True)
     assert np.array_equal(x2, got)
-    if act_store == "bf16":
+    if act_store != "fp64":
         for name in ("o", "x1", "g"):
-            assert np.array_equal(parts[name], O.round_bf16(parts[name])), name
+            assert np.array_equal(parts[name], rnd(parts[name])), name
 
 
 def test_q_handoff_scale_base2_softmax():
