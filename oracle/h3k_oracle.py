@@ -209,10 +209,13 @@ def attention(q, k, v, rows: Optional[Sequence[int]] = None) -> np.ndarray:
 
 
 def gelu(z) -> np.ndarray:
-    """Exact GELU: z * Phi(z) = z/2 * (1 + erf(z / sqrt(2)))."""
-    from scipy.special import erf
+    """Exact GELU: z * Phi(z) with the standard normal CDF Phi(z) = erfc(-z / sqrt(2)) / 2,
+    the same function as z/2 * (1 + erf(z / sqrt(2))) written without the cancellation of
+    1 + erf for negative z, so that the tail keeps its relative accuracy (Phi(-10) is
+    7.6e-24; 1 + erf(-10 / sqrt 2) is 0 in fp64)."""
+    from scipy.special import erfc
     z = np.asarray(z, np.float64)
-    return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
+    return 0.5 * z * erfc(-z / math.sqrt(2.0))
 
 
 # --------------------------------------------------------------------------- block

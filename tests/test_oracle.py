@@ -199,10 +199,28 @@ def test_gelu_textbook():
         if line.startswith("#") or not line.strip():
             continue
         z, phi = map(float, line.split())
-        assert math.isclose(float(O.gelu(z)), z * phi, rel_tol=1e-12, abs_tol=1e-15)
+        # relative accuracy everywhere, the deep negative tail included
+        assert math.isclose(float(O.gelu(z)), z * phi, rel_tol=1e-12, abs_tol=0.0), z
     z = rng.standard_normal(100) * 4
     assert np.allclose(O.gelu(z) - O.gelu(-z), z, atol=1e-13)
     assert O.gelu(0.0) == 0.0
+
+
+def test_normal_tail_fixture_matches_asymptotic_series():
+    # the tail rows of the CDF fixture against A&S 26.2.12, summed to its 20th term
+    for line in open(os.path.join(GOLD, "normal_cdf.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        z, phi = map(float, line.split())
+        if z > -8:
+            continue
+        x = -z
+        term, acc = 1.0, 0.0
+        for n in range(20):
+            acc += term
+            term *= -(2 * n + 1) / (x * x)
+        series = math.exp(-x * x / 2) / math.sqrt(2 * math.pi) / x * acc
+        assert math.isclose(phi, series, rel_tol=1e-11), (z, phi, series)
 
 
 # ----------------------------------------------------------------------------- block (brute force)
