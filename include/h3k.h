@@ -70,9 +70,11 @@ enum {
   H3K_F_BF16_GEMM = 1u,  /* no activation quantisation: bf16 x bf16 GEMMs on the dense
                             bf16 weights wb_* (the pages' BF16 baseline)              */
   H3K_F_FP32_DEBUG = 2u, /* fp32 activations end to end (x_in/x_out fp32), same int8
-                            GEMMs, fp32 attention without matrix cores; the AdaLN
-                            modulation and the LayerNorm statistics are computed in
-                            fp64 and rounded to fp32 once                             */
+                            GEMMs; every step between the stored tensors is computed
+                            in fp64 and rounded to fp32 once where it is stored: AdaLN
+                            modulation, LayerNorm statistics, the GEMM epilogues
+                            (dequant, RoPE, GELU, gated residual) and attention
+                            (without matrix cores)                                     */
   H3K_F_SYNC = 4u,       /* synchronise the stream and check for errors after every
                             launch (debugging)                                        */
   /* Per-projection precision, for the pages' precision series (BF16 -> int8 MLP -> int8
@@ -121,7 +123,7 @@ typedef struct {
  * use the block's activation type T (bf16, or fp32 under H3K_F_FP32_DEBUG). */
 typedef struct {
   size_t m;          /* fp32 [6d] modulation                                          */
-  size_t rope;       /* fp32 rotation table (internal layout)                         */
+  size_t rope;       /* rotation table, fp32 (fp64 with H3K_F_FP32_DEBUG), internal layout */
   size_t s_a, s_o, s_a2, s_g;   /* fp32 [L] per-token scales of the four quantisers     */
   size_t qa, qo, qa2;           /* int8 [L, d]                                          */
   size_t qg;                    /* int8 [L, F]                                          */
@@ -174,9 +176,11 @@ int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
  * o[l, e*Dh + j] = sum_k softmax_k(q[e,l,:] . k[e,k,:] * softmax_scale) v[e,k,j].
  * q, k: bf16 [H, L, Dh]; v: bf16 [H, Dh, L] (transposed, as the QKV projection writes
  * it); o: bf16 [L, H*Dh]. All device. head_dim 64 or 128. With H3K_F_FP32_DEBUG in
- * flags every array is fp32 instead and no matrix cores are used. */
+ * flags every array is fp32 instead, the arithmetic fp64 (no matrix cores) and o is
+ * rounded to fp32 once. softmax_scale > 0 (else H3K_EINVAL) is taken as given on the
+ * fp64 path; the bf16 path uses softmax_scale * log2(e) rounded to fp32. */
 int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
-                  int64_t L, int32_t head_dim, float softmax_scale, uint32_t flags,
+                  int64_t L, int32_t head_dim, double softmax_scale, uint32_t flags,
                   void *stream);
 
 /* Workspace bytes for h3k_stack_forward (block workspace plus two reduced-token

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle as O
+from tests import _stages
 from tests._util import code_match, np64, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -159,7 +160,10 @@ def test_attention_fp32(H, L, Dh):
                       flags=h3k.F_FP32_DEBUG).cpu().numpy()
     ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
                       np64(v).transpose(1, 0, 2)).reshape(L, H * Dh)
-    assert rel_l2(o, ref) < 1e-5
+    # fp64 arithmetic, O rounded once to fp32: the oracle's value rounded to fp32
+    ok, (eq, rel) = _stages.f32_stored_ok(o.astype(np.float64), ref)
+    print(f"fp32 attention H={H} L={L} Dh={Dh}: identical {eq:.6f}, rel-L2 {rel:.3e}")
+    assert ok
 
 
 @pytest.mark.parametrize("L,Dh", [(16384, 128), (4104, 64)])

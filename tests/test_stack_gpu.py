@@ -44,8 +44,8 @@ def test_stack_tiny(tr, flags):
     torch.cuda.synchronize()
     ref = O.stack_forward(np64(x), np64(c), [oracle_weights(b) for b in blocks],
                           n_heads=wl.n_heads, head_dim=wl.head_dim, grid=wl.grid,
-                          tr_begin=tr[0], tr_end=tr[1], attn_inputs="fp64" if flags else "bf16",
-                          act_store="fp64" if flags else "bf16")
+                          tr_begin=tr[0], tr_end=tr[1], attn_inputs="fp32" if flags else "bf16",
+                          act_store="fp32" if flags else "bf16")
     err = rel_l2(np64(out), ref)
     print(f"tiny stack tr={tr} flags={flags}: rel-L2 {err:.3e}")
     assert err <= (1e-3 if flags else 2e-2)
@@ -182,8 +182,8 @@ def test_denoise_tiny(steps, reuse, core_reuse, layers, tr, flags):
     ow = [oracle_weights(b) for b in blocks[:layers]]
     core = lambda xs: O.stack_forward(xs, np64(c), ow, n_heads=wl.n_heads, head_dim=wl.head_dim,  # noqa: E731
                                       grid=wl.grid, tr_begin=tr[0], tr_end=tr[1],
-                                      attn_inputs="fp64" if flags else "bf16",
-                                      act_store="fp64" if flags else "bf16")
+                                      attn_inputs="fp32" if flags else "bf16",
+                                      act_store="fp32" if flags else "bf16")
     ref = O.denoise(x0, core, steps=steps, reuse=reuse, core_reuse=core_reuse, store_bf16=not flags)
     err = rel_l2(np64(got), ref)
     print(f"denoise steps={steps} reuse={reuse} core_reuse={core_reuse} layers={layers} tr={tr} "

@@ -133,7 +133,9 @@ void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
     return o;
   };
   w->m = take(6 * d * 4);
-  w->rope = take((size_t)(dm->grid_t + dm->grid_h + dm->grid_w) * (Dh / 2) * 8);
+  // (cos, sin) per entry, fp32 or (the debug path's fp64 QKV epilogue) fp64
+  w->rope = take((size_t)(dm->grid_t + dm->grid_h + dm->grid_w) * (Dh / 2) *
+                 ((flags & H3K_F_FP32_DEBUG) ? 16 : 8));
   w->s_a = take(Lz * 4);
   w->s_o = take(Lz * 4);
   w->s_a2 = take(Lz * 4);
@@ -208,7 +210,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   h3k_ws_layout lay;
   plan(dm, L, flags, &lay);
   float *m = at<float>(ws, lay.m);
-  float2 *rope = at<float2>(ws, lay.rope);
+  void *rope = at<void>(ws, lay.rope);
   int rc;
 
   {
@@ -218,7 +220,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   RopeGeom rg = rope_geom(Dh, T, Hg, Wg, w_scale, w_offset);
   {
     Launch l(H3K_K_ROPE_TABLE, s, flags);
-    if ((rc = l.done(launch_rope_table(rope, rg, dm->rope_theta, s), fn, "rope_table"))) return rc;
+    if ((rc = l.done(launch_rope_table(rope, rg, dm->rope_theta, f32, s), fn, "rope_table"))) return rc;
   }
   const float *shift1 = m, *scale1 = m + d, *gate1 = m + 2 * d;
   const float *shift2 = m + 3 * d, *scale2 = m + 4 * d, *gate2 = m + 5 * d;
@@ -263,7 +265,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
-                                    at<void>(ws, lay.o), H, L, Dh, 1.0f / sqrtf((float)Dh), f32, !f32, s);
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0 / sqrt((double)Dh), f32, !f32, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
   // quantise O
@@ -438,7 +440,7 @@ int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
 }
 
 int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
-                  int64_t L, int32_t head_dim, float softmax_scale, uint32_t flags,
+                  int64_t L, int32_t head_dim, double softmax_scale, uint32_t flags,
                   void *stream) {
   const char *fn = "h3k_attention";
   H3K_CHECK_PTR(q);
@@ -450,7 +452,7 @@ int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t 
   if (head_dim != 64 && head_dim != 128) return fail(H3K_EUNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
   if (L % 8) return fail(H3K_EUNSUPPORTED, "%s: L must be a multiple of 8", fn);
   if (L > (int64_t)1 << 24 || n_heads > 65535) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
-  if (!(softmax_scale > 0.f)) return fail(H3K_EINVAL, "%s: softmax_scale must be positive", fn);
+  if (!(softmax_scale > 0.0)) return fail(H3K_EINVAL, "%s: softmax_scale must be positive", fn);
   hipStream_t s = (hipStream_t)stream;
   Launch l(H3K_K_ATTENTION, s, flags);
   const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;

@@ -96,7 +96,7 @@ size_t rope_table_entries(const RopeGeom &g);
 
 // ---------------------------------------------------------------- launchers
 // all return hipError_t of the launch (hipGetLastError)
-hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStream_t s);
+hipError_t launch_rope_table(void *tbl, const RopeGeom &g, float theta, bool f64, hipStream_t s);
 hipError_t launch_adaln(const uint16_t *w, const float *c, float *m, int64_t n_out, int dc,
                         bool f64, hipStream_t s);
 // mode: 0 = LN + modulate + int8 quant, 1 = LN + modulate -> bf16, 2 = int8 quant only
@@ -131,7 +131,7 @@ struct GemmArgs {
   // EPI_QKV: q, k [H, M, Dh], vt [H, Dh, M]
   void *q, *k, *vt;
   int d, H, Dh;
-  const float2 *rope;
+  const void *rope;    // (cos, sin) table: float2, or double2 with fp32 outputs
   RopeGeom rg;
   float q_scale = 1.0f;  // EPI_QKV: factor applied to Q after RoPE, before it is rounded
   // EPI_GELU: out [M, N]; EPI_RESID: out[m,n] = res[m,n] + gate[n] * y
@@ -156,11 +156,12 @@ inline hipError_t ensure_dynamic_lds(const void *kern, int bytes, std::atomic<ui
   return hipSuccess;
 }
 
-// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. f32: fp32 inputs and output
-// (plain FMA kernel); otherwise bf16 inputs and output on the matrix cores. q_prescaled
-// (bf16 only): q already carries scale * log2(e), the factor of the base-2 softmax.
+// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. f32: fp32 inputs and output,
+// fp64 arithmetic (plain FMA kernel); otherwise bf16 inputs and output on the matrix cores.
+// q_prescaled (bf16 only): q already carries scale * log2(e), the factor of the base-2
+// softmax.
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, float scale, bool f32, bool q_prescaled,
+                            int64_t L, int Dh, double scale, bool f32, bool q_prescaled,
                             hipStream_t s);
 
 }  // namespace h3k

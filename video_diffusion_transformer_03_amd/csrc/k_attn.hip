@@ -811,14 +811,15 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------- fp32
-// Debug path: fp32 everywhere, plain FMA arithmetic. 64 queries per work-group, four
-// threads per query, each owning DH/4 head dims; 32-key tiles of K and V^T in LDS.
+// Debug path: fp32 tensors, fp64 arithmetic (scores, softmax, P V), O rounded once to fp32.
+// Plain FMA code: 64 queries per work-group, four threads per query, each owning DH/4 head
+// dims; 32-key tiles of K and V^T in LDS, kept as fp32 (exact values of the inputs).
 template <int DH>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__ Q,
                                                        const float *__restrict__ K,
                                                        const float *__restrict__ Vt,
                                                        float *__restrict__ O, int H, int64_t L,
-                                                       float sl2) {
+                                                       double sl2) {
   constexpr int TK = 32, DP = DH / 4;
   __shared__ float sK[TK][DH + 1];
   __shared__ float sV[DH][TK + 1];
@@ -828,13 +829,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
   const float *Qh = Q + (int64_t)head * L * DH;
   const float *Kh = K + (int64_t)head * L * DH;
   const float *Vh = Vt + (int64_t)head * DH * L;
-  float q[DP], o[DP];
+  float q[DP];
+  double o[DP];
 #pragma unroll
   for (int e = 0; e < DP; ++e) {
     q[e] = qi < L ? Qh[qi * DH + part * DP + e] : 0.f;
-    o[e] = 0.f;
+    o[e] = 0.0;
   }
-  float mrow = -INFINITY, lsum = 0.f;
+  double mrow = -INFINITY, lsum = 0.0;
   for (int64_t k0 = 0; k0 < L; k0 += TK) {
     __syncthreads();
     for (int i = tid; i < TK * DH; i += 256) {
@@ -846,37 +848,36 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
       sV[r][c] = (k0 + c < L) ? Vh[(int64_t)r * L + k0 + c] : 0.f;
     }
     __syncthreads();
-    float s[TK];
-    float mx = -INFINITY;
+    double s[TK];
+    double mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < TK; ++j) {
-      float a = 0.f;
+      double a = 0.0;
 #pragma unroll
-      for (int e = 0; e < DP; ++e) a = fmaf(q[e], sK[j][part * DP + e], a);
+      for (int e = 0; e < DP; ++e) a = fma((double)q[e], (double)sK[j][part * DP + e], a);
       a += __shfl_xor(a, 1, 64);
       a += __shfl_xor(a, 2, 64);
       s[j] = (k0 + j < L) ? a * sl2 : -INFINITY;
-      mx = fmaxf(mx, s[j]);
+      mx = fmax(mx, s[j]);
     }
-    const float mnew = fmaxf(mrow, mx);
-    const float alpha = exp2f(mrow - mnew);
+    const double mnew = fmax(mrow, mx);
+    const double alpha = exp2(mrow - mnew);
     mrow = mnew;
     lsum *= alpha;
 #pragma unroll
     for (int e = 0; e < DP; ++e) o[e] *= alpha;
 #pragma unroll
     for (int j = 0; j < TK; ++j) {
-      const float p = exp2f(s[j] - mnew);
+      const double p = exp2(s[j] - mnew);
       lsum += p;
 #pragma unroll
-      for (int e = 0; e < DP; ++e) o[e] = fmaf(p, sV[part * DP + e][j], o[e]);
+      for (int e = 0; e < DP; ++e) o[e] = fma(p, (double)sV[part * DP + e][j], o[e]);
     }
   }
   if (qi < L) {
-    const float inv = 1.0f / lsum;
     float *orow = O + qi * (int64_t)H * DH + (int64_t)head * DH + part * DP;
 #pragma unroll
-    for (int e = 0; e < DP; ++e) orow[e] = o[e] * inv;
+    for (int e = 0; e < DP; ++e) orow[e] = (float)(o[e] / lsum);
   }
 }
 
@@ -913,7 +914,7 @@ static hipError_t attn_bf16(const void *q, const void *k, const void *vt, void *
 
 template <int DH>
 static hipError_t attn_f32(const void *q, const void *k, const void *vt, void *o, int H,
-                           int64_t L, float sl2, hipStream_t s) {
+                           int64_t L, double sl2, hipStream_t s) {
   dim3 grid((unsigned)((L + 63) / 64), (unsigned)H);
   attn_f32_kernel<DH><<<grid, 256, 0, s>>>((const float *)q, (const float *)k,
                                            (const float *)vt, (float *)o, H, L, sl2);
@@ -921,14 +922,15 @@ static hipError_t attn_f32(const void *q, const void *k, const void *vt, void *o
 }
 
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, float scale, bool f32, bool q_prescaled,
+                            int64_t L, int Dh, double scale, bool f32, bool q_prescaled,
                             hipStream_t s) {
-  const float sl2 = scale * 1.4426950408889634f;  // exp(x) = exp2(x * log2(e))
+  const double sl2d = scale * 1.44269504088896340736;  // exp(x) = exp2(x * log2(e))
+  const float sl2 = (float)sl2d;
   if (Dh != 64 && Dh != 128) return hipErrorInvalidValue;
   if (f32) {
     if (q_prescaled) return hipErrorInvalidValue;
-    return Dh == 128 ? attn_f32<128>(q, k, vt, o, H, L, sl2, s)
-                     : attn_f32<64>(q, k, vt, o, H, L, sl2, s);
+    return Dh == 128 ? attn_f32<128>(q, k, vt, o, H, L, sl2d, s)
+                     : attn_f32<64>(q, k, vt, o, H, L, sl2d, s);
   }
   if (Dh == 64) return attn_bf16<64>(q, k, vt, o, H, L, q_prescaled ? 1.0f : sl2, s);
   return q_prescaled ? attn_v2<true>(q, k, vt, o, H, L, sl2, s)

@@ -75,6 +75,11 @@ __device__ __forceinline__ float gelu_erf(float z) {
   const float e = __builtin_amdgcn_exp2f((z * z) * kE);
   return fmaf(-az, poly * e, fmaxf(z, 0.f));
 }
+// fp64 GELU of the fp32 debug path: z Phi(z) = z erfc(-z / sqrt 2) / 2 with the math
+// library's double erfc (no cancellation for negative z either)
+__device__ __forceinline__ double gelu_erf(double z) {
+  return 0.5 * z * erfc(z * -0.70710678118654752440);
+}
 
 // Table offsets of token l's three axes: pair i of head_dim turns by tbl[ofs.x + i] (i < Pt),
 // tbl[ofs.y + i] (Pt <= i < Pt + Ph) or tbl[ofs.z + i] (the rest); the pair-index bases are
@@ -87,9 +92,10 @@ __device__ __forceinline__ int3 rope_offsets(const RopeGeom &g, int64_t l) {
   const int w = rem - h * g.Wg;
   return make_int3(t * g.Pt, g.base_h + h * g.Ph - g.Pt, g.base_w + w * g.Pw - g.Pt - g.Ph);
 }
-__device__ __forceinline__ float2 rope_cs(const float2 *tbl, const RopeGeom &g, int i, int3 ofs) {
+template <typename CS>
+__device__ __forceinline__ CS rope_cs(const void *tbl, const RopeGeom &g, int i, int3 ofs) {
   const int e = i < g.Pt ? ofs.x + i : (i < g.Pt + g.Ph ? ofs.y + i : ofs.z + i);
-  return tbl[e];
+  return ((const CS *)tbl)[e];
 }
 
 template <bool BF16>
@@ -124,13 +130,15 @@ __device__ __forceinline__ void tile_origin(const GemmArgs &a, int64_t t, int64_
 // Per-column-block operands of the epilogue (one 16-channel block i of a wave's tile),
 // loaded ahead of use so that the global-memory latency of one block overlaps the
 // arithmetic and stores of the blocks before it. Fields an epilogue does not use are never
-// touched and take no registers.
-template <int TM, bool RESF32>
+// touched and take no registers. F64: the fp32-output (debug) instantiations, whose
+// epilogue arithmetic is fp64 and whose RoPE table holds fp64 (cos, sin).
+template <int TM, bool RESF32, bool F64>
 struct EpiChunk {
   float sw[4];                  // weight scales of the lane's 4 channels
   float g[4];                   // gate (RESID)
   uint32_t r[TM][RESF32 ? 4 : 2];  // residual bits, fp32 or packed bf16 (RESID)
-  float2 cs[TM][2];             // RoPE (cos, sin) of the lane's two channel pairs (QKV)
+  typename std::conditional<F64, double2, float2>::type cs[TM][2];  // RoPE (cos, sin) of the
+                                                                     // lane's two pairs (QKV)
 };
 
 // LDS staging of bf16 epilogue outputs: 64 rows of 128 bytes per wave at this pitch
@@ -154,6 +162,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
                                               int n_base, int64_t m_base, int lane,
                                               uint8_t *stage) {
   constexpr bool STAGED = !OUTF32 && EPI != EPI_RAW_I32;
+  // fp32 outputs (the debug path): dequant, RoPE, GELU and the gated residual in fp64,
+  // rounded once to fp32 at the store
+  using E = typename std::conditional<OUTF32, double, float>::type;
+  using CS = typename std::conditional<OUTF32, double2, float2>::type;
   // A bf16 residual is read in whole lines too: each 64-channel slice of it is loaded 16
   // bytes per lane in the row order of the stage, written into the stage, and each chunk
   // reads its residual from the stage position its output then overwrites (same lane).
@@ -238,7 +250,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
     if constexpr (EPI == EPI_QKV) rofs[j] = rope_offsets(a.rg, mrow[j]);
   }
 
-  auto load_chunk = [&](EpiChunk<TM, RESF32> &c, int i) {
+  auto load_chunk = [&](EpiChunk<TM, RESF32, OUTF32> &c, int i) {
     const int n = n_base + i * 16 + (lane >> 4) * 4;
     if constexpr (!BF16 && EPI != EPI_RAW_I32) {
       const float4 t4 = *(const float4 *)(a.sw + n);
@@ -265,7 +277,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
 #pragma unroll
         for (int j = 0; j < TM; ++j)
 #pragma unroll
-          for (int p = 0; p < 2; ++p) c.cs[j][p] = rope_cs(a.rope, a.rg, dh / 2 + p, rofs[j]);
+          for (int p = 0; p < 2; ++p) c.cs[j][p] = rope_cs<CS>(a.rope, a.rg, dh / 2 + p, rofs[j]);
       }
     }
   };
@@ -298,7 +310,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
     }
   };
 
-  auto store_chunk = [&](const EpiChunk<TM, RESF32> &c, int i) {
+  auto store_chunk = [&](const EpiChunk<TM, RESF32, OUTF32> &c, int i) {
     const int n = n_base + i * 16 + (lane >> 4) * 4;
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
@@ -309,13 +321,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
           if (mval[j]) *(int4 *)(a.c32 + m * a.N + n) = make_int4(v[0], v[1], v[2], v[3]);
         }
       } else {
-        float y[4];
+        E y[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (BF16)
             y[r] = acc[i][j][r];
           else
-            y[r] = ((float)acc[i][j][r] * sa[j]) * c.sw[r];
+            y[r] = ((E)acc[i][j][r] * (E)sa[j]) * (E)c.sw[r];
         }
         if constexpr (EPI == EPI_QKV) {
           const int cc = n - sec * a.d;
@@ -324,8 +336,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
           if (sec < 2) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-              const float2 cs = c.cs[j][p];
-              const float u0 = y[2 * p], u1 = y[2 * p + 1];
+              const CS cs = c.cs[j][p];
+              const E u0 = y[2 * p], u1 = y[2 * p + 1];
               y[2 * p] = u0 * cs.x - u1 * cs.y;
               y[2 * p + 1] = u0 * cs.y + u1 * cs.x;
             }
@@ -336,20 +348,21 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
             if constexpr (STAGED)
               stage_vals(i, j, y);
             else if (mval[j])
-              store4<OUTF32>(sec == 0 ? a.q : a.k, ((int64_t)head * a.M + m) * a.Dh + dh, y[0],
-                             y[1], y[2], y[3]);
+              store4<OUTF32>(sec == 0 ? a.q : a.k, ((int64_t)head * a.M + m) * a.Dh + dh,
+                             (float)y[0], (float)y[1], (float)y[2], (float)y[3]);
           } else if constexpr (STAGED) {
             stage_vals(i, j, y);
           } else if (mval[j]) {
             const int64_t base = ((int64_t)head * a.Dh + dh) * a.M + m;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) store1<OUTF32>(a.vt, base + (int64_t)r * a.M, y[r]);
+            for (int r = 0; r < 4; ++r) store1<OUTF32>(a.vt, base + (int64_t)r * a.M, (float)y[r]);
           }
         } else if constexpr (EPI == EPI_GELU) {
-          float v[4] = {gelu_erf(y[0]), gelu_erf(y[1]), gelu_erf(y[2]), gelu_erf(y[3])};
+          float v[4] = {(float)gelu_erf(y[0]), (float)gelu_erf(y[1]), (float)gelu_erf(y[2]),
+                        (float)gelu_erf(y[3])};
           emit(i, j, v);
         } else if constexpr (EPI == EPI_RESID) {
-          float r4[4];
+          E r4[4];
           if constexpr (LRES) {
             const int t = j * 16 + (lane & 15), cb = (i & 3) * 16 + (lane >> 4) * 4;
             const uint2 u = *(const uint2 *)(stage + t * kStagePitch + cb * 2);
@@ -366,15 +379,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
             r4[2] = __uint_as_float(c.r[j][1] << 16);
             r4[3] = __uint_as_float(c.r[j][1] & 0xffff0000u);
           }
-          float v[4] = {r4[0] + c.g[0] * y[0], r4[1] + c.g[1] * y[1], r4[2] + c.g[2] * y[2],
-                        r4[3] + c.g[3] * y[3]};
+          float v[4] = {(float)(r4[0] + (E)c.g[0] * y[0]), (float)(r4[1] + (E)c.g[1] * y[1]),
+                        (float)(r4[2] + (E)c.g[2] * y[2]), (float)(r4[3] + (E)c.g[3] * y[3])};
           emit(i, j, v);
         }
       }
     }
   };
 
-  EpiChunk<TM, RESF32> buf[PF + 1];
+  EpiChunk<TM, RESF32, OUTF32> buf[PF + 1];
   if constexpr (LRES) load_res_slice(0);
   static_for<PF>([&](auto I) { load_chunk(buf[I], I); });
   static_for<TN>([&](auto I) {

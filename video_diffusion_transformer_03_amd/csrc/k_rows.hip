@@ -32,8 +32,10 @@ size_t rope_table_entries(const RopeGeom &g) {
   return (size_t)g.T * g.Pt + (size_t)g.Hg * g.Ph + (size_t)g.Wg * g.Pw;
 }
 
-// entry (axis a, position p, pair j) -> (cos, sin) of p * theta^(-j / P_a), in fp64
-__global__ void rope_table_kernel(float2 *tbl, RopeGeom g, double theta) {
+// entry (axis a, position p, pair j) -> (cos, sin) of p * theta^(-j / P_a), in fp64, stored
+// as float2, or as double2 for the fp32 debug path's fp64 QKV epilogue
+template <typename CS>
+__global__ void rope_table_kernel(CS *tbl, RopeGeom g, double theta) {
   int e = blockIdx.x * blockDim.x + threadIdx.x;
   int n = g.T * g.Pt + g.Hg * g.Ph + g.Wg * g.Pw;
   if (e >= n) return;
@@ -50,12 +52,16 @@ __global__ void rope_table_kernel(float2 *tbl, RopeGeom g, double theta) {
     pos = (double)(r / P) * (double)g.w_scale + (double)g.w_offset;
   }
   double ang = pos * pow(theta, -(double)j / (double)P);
-  tbl[e] = make_float2((float)cos(ang), (float)sin(ang));
+  tbl[e].x = cos(ang);
+  tbl[e].y = sin(ang);
 }
 
-hipError_t launch_rope_table(float2 *tbl, const RopeGeom &g, float theta, hipStream_t s) {
+hipError_t launch_rope_table(void *tbl, const RopeGeom &g, float theta, bool f64, hipStream_t s) {
   int n = (int)rope_table_entries(g);
-  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(tbl, g, (double)theta);
+  if (f64)
+    rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>((double2 *)tbl, g, (double)theta);
+  else
+    rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>((float2 *)tbl, g, (double)theta);
   return hipGetLastError();
 }
 

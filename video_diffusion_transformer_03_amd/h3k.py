@@ -70,7 +70,7 @@ def lib() -> C.CDLL:
                                             i64, u32, vp, sz, vp]),
             "h3k_block_forward_grid": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), C.POINTER(Dims),
                                                  i32, i32, i32, f32, f32, u32, vp, sz, vp]),
-            "h3k_attention": (C.c_int, [vp, vp, vp, vp, i32, i64, i32, f32, u32, vp]),
+            "h3k_attention": (C.c_int, [vp, vp, vp, vp, i32, i64, i32, C.c_double, u32, vp]),
             "h3k_stack_workspace_bytes": (sz, [C.POINTER(Dims), i64, i32, i32, u32]),
             "h3k_stack_forward": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), i32,
                                             C.POINTER(Dims), i64, i32, i32, u32, vp, sz, vp]),
