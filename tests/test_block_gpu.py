@@ -186,15 +186,18 @@ def test_block_ragged_full_width_sampled(flags, tol, tol_forced):
     assert err <= tol and forced <= tol_forced
 
 
-def test_block_l16384_fp32_sampled():
-    wl = S.WORKLOADS["block_l16384"]
+@pytest.mark.parametrize("name,n_rows", [("block_l4096", 32), ("block_l16384", 24), ("block_l65536", 8)])
+def test_block_fp32_sampled(name, n_rows):
+    # the fp32 debug path at each full-size workload (L = 65536: fp64 attention over 65536 keys
+    # and the oracle's Q, K, V for every token, about a minute in all)
+    wl = S.WORKLOADS[name]
     r = run_gpu(wl, h3k.F_FP32_DEBUG, gen_device="cuda")
-    rows = _sample_rows(wl.L, 24, 3)
-    check_stages(wl, r, rows)
+    rows = _sample_rows(wl.L, n_rows, 3)
+    check_stages(wl, r, rows, label=f"{name} fp32")
     got = np64(r["out"])[rows]
     err = rel_l2(got, oracle_full(wl, r, "w8a8", rows=rows))
     forced = rel_l2(got, _stages.code_forced_output(wl, r, rows))
-    print(f"l16384 fp32 end-to-end sampled rel-L2 {err:.3e}, with the GPU's codes {forced:.3e}")
+    print(f"{name} fp32 end-to-end sampled rel-L2 {err:.3e}, with the GPU's codes {forced:.3e}")
     assert err <= FP32_TOL and forced <= FP32_FORCED_TOL
 
 
