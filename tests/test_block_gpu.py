@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle as O
+from oracle import ref_abi as R
 import synth_inputs as S
 from tests import _stages
 from tests._util import code_match, gpu_block, np64, oracle_weights, rel_l2
@@ -106,6 +107,27 @@ def test_block_inplace_and_deterministic():
     xin = r["x"].clone()
     h3k.block_forward(xin, r["c"], r["bw"], r["dims"], 0, r["ws"], out=xin)  # x_out aliases x_in
     assert torch.equal(xin, r["out"])
+
+
+@pytest.mark.parametrize("flags,tol", [(0, 2e-2), (h3k.F_FP32_DEBUG, 1e-3),
+                                       (h3k.F_BF16_QKV | h3k.F_BF16_OUT, 2e-2)])
+def test_block_matches_cpu_twin(flags, tol):
+    # one call shape on both sides: h3k.block_forward on the device and the oracle's C-ABI
+    # twin h3k_ref_block_forward on host copies of the same buffers, with the binding's own
+    # dims struct and weight field names
+    wl = S.WORKLOADS["tiny"]
+    r = run_gpu(wl, flags)
+    host_w = {}
+    for f, _ in h3k.BlockWeightsC._fields_:
+        t = getattr(r["bw"], f)
+        host_w[f] = None if t is None else (t.cpu().numpy() if t.dtype == torch.int8
+                                            else t.float().cpu().numpy())
+    out = np.zeros((wl.L, wl.d), np.float32)
+    assert R.h3k_ref_block_forward(np64(r["x"]), out, np64(r["c"]), host_w, r["dims"], wl.L,
+                                   flags) == R.OK
+    err = rel_l2(np64(r["out"]), out.astype(np.float64))
+    print(f"tiny flags={flags}: GPU vs CPU twin rel-L2 {err:.3e}")
+    assert err <= tol
 
 
 # ----------------------------------------------------------------------------- stage checks
