@@ -162,6 +162,7 @@ def main():
     value = L * args.steps / (t1 - t0)
 
     work = kernel_work(wl, L)
+    copy_gbps = device_copy_gbps(torch)
     kernels = {}
     for name, (n, tot) in prof.items():
         if n == 0:
@@ -179,7 +180,7 @@ def main():
             else:
                 rate = wk[1] / (avg * 1e-3) / 1e9
                 ent.update(achieved=round(rate, 1), peak=HBM_GBS, unit="GB/s",
-                           frac=round(rate / HBM_GBS, 4))
+                           frac=round(rate / HBM_GBS, 4), frac_of_copy=round(rate / copy_gbps, 4))
         kernels[name] = ent
 
     label = {"w8a8": "W8A8", "bf16gemm": "BF16", "fp32": "int8 GEMM + fp32"}[args.variant]
@@ -213,6 +214,7 @@ def main():
     result["device"] = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
                         "hbm_gib": round(props.total_memory / 2**30, 1)}
+    result["device_copy_GBps"] = round(copy_gbps, 1)
     result["kernels"] = kernels
     if not args.no_extras and args.variant == "w8a8" and args.workload == "block_l16384":
         del ws, out
@@ -248,6 +250,23 @@ def measured_traffic(path, workload, kernel):
                 return None
             return round(ent["read_bytes"] + ent["write_bytes"])
     return None
+
+
+def device_copy_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Bandwidth of a plain device-to-device copy (bytes read plus bytes written per second):
+    the practical ceiling beside the nominal 8 TB/s for kernels that stream HBM."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    return 2 * nbytes / dt / 1e9
 
 
 def _time_steps(torch, fn, steps, warmup):
