@@ -394,14 +394,16 @@ def fresh_steps(steps: int, reuse: int) -> list:
 
 
 def denoise(x, core, *, steps: int, reuse: int = 1, core_reuse: int = 1,
-            store_bf16: bool = False) -> np.ndarray:
+            store_bf16: bool = False, store_f32: bool = False) -> np.ndarray:
     """Euler steps of a flow-matching sampler on t_k = 1 - k / steps (same page and section
     give the controls --steps, --reuse, --core-reuse; the formulas are the plainest reading):
     at fresh steps (fresh_steps) every core_reuse-th evaluation and the last one run the
     core, y = core(x), caching r = y - x and setting v = y; the other fresh steps set
     v = x + r; other steps keep v. Then x <- x + (t_{k+1} - t_k) v. core: callable on
     [L, d] arrays (the stack of the active blocks). store_bf16 rounds y and each new x to
-    bfloat16, as the path that stores activations in bf16 does."""
+    bfloat16, as the path that stores activations in bf16 does. store_f32 rounds y, r, a
+    reused v and each new x to fp32, as a path that computes in fp64 and keeps the sampler
+    state in fp32 does."""
     x = np.asarray(x, np.float64).copy()
     dt = -1.0 / steps
     fresh = set(fresh_steps(steps, reuse))
@@ -414,13 +416,21 @@ def denoise(x, core, *, steps: int, reuse: int = 1, core_reuse: int = 1,
                 y = core(x)
                 if store_bf16:
                     y = round_bf16(y)
+                if store_f32:
+                    y = round_f32(y)
                 r = y - x
+                if store_f32:
+                    r = round_f32(r)
                 v = y
             else:
                 v = x + r
+                if store_f32:
+                    v = round_f32(v)
             f += 1
         x = x + dt * v
         if store_bf16:
             x = round_bf16(x)
+        if store_f32:
+            x = round_f32(x)
     return x
 

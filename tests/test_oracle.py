@@ -505,3 +505,8 @@ def test_denoise_linear_core_closed_forms():
     # store_bf16 rounds every state: the result is exactly representable in bf16
     got = O.denoise(x0, core, steps=3, store_bf16=True)
     assert np.array_equal(got, O.round_bf16(got))
+    # store_f32 likewise in fp32, and within fp32 rounding of the exact closed form
+    core32 = lambda x: O.round_f32(a * x)  # noqa: E731
+    got = O.denoise(x0, core32, steps=3, core_reuse=2, store_f32=True)
+    assert np.array_equal(got, O.round_f32(got))
+    assert np.allclose(got, x3, rtol=1e-6, atol=0) and not np.array_equal(got, x3)

@@ -184,7 +184,8 @@ def test_denoise_tiny(steps, reuse, core_reuse, layers, tr, flags):
                                       grid=wl.grid, tr_begin=tr[0], tr_end=tr[1],
                                       attn_inputs="fp32" if flags else "bf16",
                                       act_store="fp32" if flags else "bf16")
-    ref = O.denoise(x0, core, steps=steps, reuse=reuse, core_reuse=core_reuse, store_bf16=not flags)
+    ref = O.denoise(x0, core, steps=steps, reuse=reuse, core_reuse=core_reuse, store_bf16=not flags,
+                    store_f32=bool(flags))
     err = rel_l2(np64(got), ref)
     print(f"denoise steps={steps} reuse={reuse} core_reuse={core_reuse} layers={layers} tr={tr} "
           f"flags={flags}: rel-L2 {err:.3e}")

@@ -569,7 +569,8 @@ int h3k_denoise(void *x, const float *cond, const h3k_block_weights *blocks, int
   uint8_t *y = (uint8_t *)ws + sw;
   float *v = (float *)(y + up256((size_t)n * (f32 ? 4 : 2)));
   float *r = (float *)((uint8_t *)v + up256((size_t)n * 4));
-  const float dt = -1.0f / (float)steps;
+  // the step: exact in fp64 on the fp32 debug path; the bf16 path uses it rounded to fp32
+  const double dt = f32 ? -1.0 / (double)steps : (double)(-1.0f / (float)steps);
   int fresh = 0;
   for (int k = 0; k < steps; ++k) {
     const bool last = k == steps - 1;

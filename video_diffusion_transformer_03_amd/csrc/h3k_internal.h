@@ -109,7 +109,7 @@ hipError_t launch_token_unpair(void *x, const void *xo, const void *xi, bool f32
                                int Hg, int Wg, int d, hipStream_t s);
 // denoising-loop element steps (see k_rows.hip); n % 8 == 0
 enum SamplerMode { SAMPLER_FRESH = 0, SAMPLER_REUSED = 1, SAMPLER_EULER = 2 };
-hipError_t launch_sampler(int mode, void *x, const void *y, float *v, float *r, float dt,
+hipError_t launch_sampler(int mode, void *x, const void *y, float *v, float *r, double dt,
                           int64_t n, bool f32, hipStream_t s);
 // dst = src, n16 16-byte chunks (both 16-byte aligned)
 hipError_t launch_copy16(void *dst, const void *src, int64_t n16, hipStream_t s);

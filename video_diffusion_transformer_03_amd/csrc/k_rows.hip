@@ -622,7 +622,10 @@ hipError_t launch_copy16(void *dst, const void *src, int64_t n16, hipStream_t s)
 template <typename T>
 __global__ __launch_bounds__(256) void sampler_kernel(int mode, T *__restrict__ x,
                                                       const T *__restrict__ y, float *__restrict__ v,
-                                                      float *__restrict__ r, float dt, int64_t n8) {
+                                                      float *__restrict__ r, double dt, int64_t n8) {
+  // fp32 activations (the debug path): fp64 arithmetic and the exact step, each stored value
+  // rounded once to fp32; bf16 activations: fp32 arithmetic
+  using A = typename std::conditional<sizeof(T) == 4, double, float>::type;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const int64_t o = i * 8;
@@ -633,16 +636,16 @@ __global__ __launch_bounds__(256) void sampler_kernel(int mode, T *__restrict__ 
     load8(y + o, ys);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      r[o + t] = ys[t] - xs[t];
+      r[o + t] = (float)((A)ys[t] - (A)xs[t]);
       v[o + t] = ys[t];
     }
   } else if (mode == SAMPLER_REUSED) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) v[o + t] = xs[t] + r[o + t];
+    for (int t = 0; t < 8; ++t) v[o + t] = (float)((A)xs[t] + (A)r[o + t]);
   } else {
     float out[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) out[t] = xs[t] + dt * v[o + t];
+    for (int t = 0; t < 8; ++t) out[t] = (float)((A)xs[t] + (A)dt * (A)v[o + t]);
     if constexpr (sizeof(T) == 2) {
       *(uint4 *)(x + o) = make_uint4(pack_bf2(out[0], out[1]), pack_bf2(out[2], out[3]),
                                      pack_bf2(out[4], out[5]), pack_bf2(out[6], out[7]));
@@ -653,7 +656,7 @@ __global__ __launch_bounds__(256) void sampler_kernel(int mode, T *__restrict__ 
   }
 }
 
-hipError_t launch_sampler(int mode, void *x, const void *y, float *v, float *r, float dt,
+hipError_t launch_sampler(int mode, void *x, const void *y, float *v, float *r, double dt,
                           int64_t n, bool f32, hipStream_t s) {
   const int64_t n8 = n / 8;
   dim3 grid((unsigned)((n8 + 255) / 256));
