@@ -83,11 +83,19 @@ enum {
    * its activation quantiser. H3K_F_BF16_GEMM is all three. */
   H3K_F_BF16_QKV = 8u,   /* QKV projection                                            */
   H3K_F_BF16_OUT = 16u,  /* attention output projection                               */
-  H3K_F_BF16_MLP = 32u   /* MLP up and down projections                               */
+  H3K_F_BF16_MLP = 32u,  /* MLP up and down projections                               */
+  /* Attention operand precision. By default the QKV epilogue stores Q, K and V as fp16 and
+   * attention runs on fp16 matrix-core operands (P rounded to fp16), with O stored as fp16
+   * for its int8 quantiser (bf16 when H3K_F_BF16_OUT consumes it). This flag stores Q, K,
+   * V, P and O as bf16 instead (the same instruction rate and bytes, 8 significant bits
+   * instead of 11). Not combinable with H3K_F_FP32_DEBUG. */
+  H3K_F_ATTN_BF16 = 64u,
+  /* h3k_attention only: q carries the base-2 softmax scale (see h3k_attention) */
+  H3K_F_Q_BASE2 = 128u
 };
 
 /* element types */
-enum { H3K_DT_F32 = 0, H3K_DT_BF16 = 1 };
+enum { H3K_DT_F32 = 0, H3K_DT_BF16 = 1, H3K_DT_F16 = 2 };
 
 typedef struct {
   int32_t d;          /* model width = n_heads * head_dim; multiple of 256            */
@@ -127,11 +135,15 @@ typedef struct {
   size_t s_a, s_o, s_a2, s_g;   /* fp32 [L] per-token scales of the four quantisers     */
   size_t qa, qo, qa2;           /* int8 [L, d]                                          */
   size_t qg;                    /* int8 [L, F]                                          */
-  size_t q, k;                  /* T [H, L, Dh] head-major, RoPE applied; in bf16, q is
-                                   stored times log2(e)/sqrt(Dh) (the base-2 softmax
-                                   scale, applied before its one rounding)              */
-  size_t vt;                    /* T [H, Dh, L] head-major, transposed                  */
-  size_t o;                     /* T [L, d] attention output, head e in columns e*Dh .. */
+  size_t q, k;                  /* A [H, L, Dh] head-major, RoPE applied; A is the
+                                   attention operand type: fp16 (bf16 with
+                                   H3K_F_ATTN_BF16, fp32 with H3K_F_FP32_DEBUG). On the
+                                   16-bit paths q is stored times log2(e)/sqrt(Dh) (the
+                                   base-2 softmax scale, applied before its one rounding) */
+  size_t vt;                    /* A [H, Dh, L] head-major, transposed                  */
+  size_t o;                     /* [L, d] attention output, head e in columns e*Dh ..;
+                                   fp16 (bf16 with H3K_F_ATTN_BF16 or H3K_F_BF16_OUT,
+                                   fp32 with H3K_F_FP32_DEBUG)                          */
   size_t x1;                    /* T [L, d] residual stream after the attention half    */
   size_t g;                     /* T [L, F] GELU output                                 */
   size_t h, h2;                 /* bf16 [L, d] modulated activations feeding a bf16 QKV /
@@ -172,16 +184,24 @@ int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
                            int32_t Hg, int32_t Wg, float w_pos_scale, float w_pos_offset,
                            uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
-/* Multi-head softmax attention without mask, bf16 MFMA with fp32 online softmax:
+/* Multi-head softmax attention without mask ("h3-metal: Apple Silicon을 위한 네이티브
+ * MiniMax-H3 추론", section "Metal 4 및 TensorOps": attention over head-major Q/K/V):
  * o[l, e*Dh + j] = sum_k softmax_k(q[e,l,:] . k[e,k,:] * softmax_scale) v[e,k,j].
- * q, k: bf16 [H, L, Dh]; v: bf16 [H, Dh, L] (transposed, as the QKV projection writes
- * it); o: bf16 [L, H*Dh]. All device. head_dim 64 or 128. With H3K_F_FP32_DEBUG in
- * flags every array is fp32 instead, the arithmetic fp64 (no matrix cores) and o is
- * rounded to fp32 once. softmax_scale > 0 (else H3K_EINVAL) is taken as given on the
- * fp64 path; the bf16 path uses softmax_scale * log2(e) rounded to fp32. */
+ * q, k: [H, L, Dh]; v: [H, Dh, L] (transposed, as the QKV projection writes it);
+ * o: [L, H*Dh]; all device, all of element type `dtype`:
+ *   H3K_DT_F16 / H3K_DT_BF16: matrix-core products on 16-bit operands (P rounded to the
+ *     same type), fp32 online softmax with softmax_scale * log2(e) rounded to fp32;
+ *   H3K_DT_F32: fp64 arithmetic without matrix cores (the debug path), softmax_scale
+ *     taken as given, o rounded to fp32 once.
+ * head_dim 64 or 128; L % 8 == 0. flags: H3K_F_SYNC and, for 16-bit dtypes,
+ * H3K_F_Q_BASE2: q already holds q * softmax_scale * log2(e) (the block's QKV epilogue
+ * stores Q that way, so that scores leave the matrix cores as base-2 exponents), and
+ * softmax_scale is not applied again. Errors: H3K_EINVAL (null or misaligned pointers,
+ * n_heads or L < 1, softmax_scale <= 0, unknown dtype or flags, H3K_F_Q_BASE2 with
+ * H3K_DT_F32), H3K_EUNSUPPORTED (head_dim, L % 8, L > 2^24, n_heads > 65535). */
 int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
-                  int64_t L, int32_t head_dim, double softmax_scale, uint32_t flags,
-                  void *stream);
+                  int64_t L, int32_t head_dim, double softmax_scale, int dtype,
+                  uint32_t flags, void *stream);
 
 /* Workspace bytes for h3k_stack_forward (block workspace plus two reduced-token
  * buffers when tr_begin < tr_end). */
@@ -267,8 +287,10 @@ int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift,
                           const float *scale, int64_t rows, int32_t cols, float eps,
                           int8_t *q_out, float *s_out, void *stream);
 
-/* Per-row int8 quantisation of x [rows, cols] (x_dtype) into q_out, s_out.
- * cols % 8 == 0, cols <= 32768. */
+/* Per-row int8 quantisation of x [rows, cols] (x_dtype: fp32, bf16 or fp16) into q_out,
+ * s_out, by the rule of h3k_quantize_weights ("맥북에서 AI 영상 생성 모델 돌리기 - MiniMax
+ * H3 로컬 실행과 30초 애니메이션 만들기", section "int8 이 뭔가요": one F32 scale per
+ * activation row). cols % 8 == 0, cols <= 32768. */
 int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols,
                      int8_t *q_out, float *s_out, void *stream);
 

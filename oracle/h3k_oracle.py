@@ -77,7 +77,7 @@ def quantize_weights(w) -> Tuple[np.ndarray, np.ndarray]:
     return quantize_rows(w)
 
 
-# --------------------------------------------------------------------------- bf16 rounding
+# --------------------------------------------------------------------------- 16-bit rounding
 def round_bf16(v) -> np.ndarray:
     """Round to the nearest bfloat16 value (8 significant bits), ties to even, from the
     exact fp64 value (one rounding). Zero, inf and NaN pass through; values are assumed
@@ -85,6 +85,19 @@ def round_bf16(v) -> np.ndarray:
     v = np.asarray(v, np.float64)
     m, e = np.frexp(v)                   # v = m * 2**e, 0.5 <= |m| < 1
     return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def round_f16(v) -> np.ndarray:
+    """Round to the nearest IEEE binary16 value, ties to even, from the exact fp64 value
+    (one rounding): 11 significant bits for |v| >= 2^-14; below that a fixed step of 2^-24
+    (the subnormals). Magnitudes that round above 65504 become infinite. Written out from
+    the format rather than through a library conversion."""
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)                   # v = m * 2**e, 0.5 <= |m| < 1
+    # quantum of the binade: 2^(e - 11) for normal values, 2^-24 for subnormal ones
+    q = np.ldexp(1.0, np.maximum(e - 11, -24))
+    r = np.rint(v / q) * q               # exact: v / q and the product are powers-of-two scalings
+    return np.where(np.abs(r) > 65504.0, np.copysign(np.inf, v), r)
 
 
 # --------------------------------------------------------------------------- int8 GEMM
@@ -181,14 +194,6 @@ def apply_rope(u, ang) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- attention
-def q_handoff_scale(head_dim: int) -> float:
-    """log2(e) / sqrt(Dh): softmax(Q K^T / sqrt(Dh)) equals a base-2 softmax of
-    (Q * this) K^T, so a path may hand attention Q already multiplied by it and round
-    that product to its storage type once. Pure mathematics (exp(x) = 2^(x log2 e)); the
-    value matters only for where the bf16 rounding of Q happens."""
-    return math.log2(math.e) / math.sqrt(head_dim)
-
-
 def attention(q, k, v, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Multi-head softmax attention, no mask. q, k, v [L, H, Dh] -> O [n, H, Dh] for the
     query rows `rows` (all rows if None). S = q k^T / sqrt(Dh); softmax over keys with
@@ -270,21 +275,19 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     INT8_PROJECTIONS): "w8a8" all, "int8_mlp_qkv" all but the output projection,
     "int8_mlp" the MLP only, "bf16gemm" none (dense, no activation quantisation).
 
-    attn_inputs: "fp64" keeps Q, K, V exact; "bf16" rounds them to bfloat16 (after RoPE)
-    before attention, as on the path whose QKV projection hands the attention bf16
-    tensors (page "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section
-    "Metal 4 및 TensorOps": BF16 QKV projection routed into head-major attention inputs).
-    Q is handed over with the softmax scale in base 2 already applied, so its one
-    rounding is of Q * q_handoff_scale(head_dim); the oracle divides that back out and
-    runs its attention on the exact value of the rounded tensor (see q_handoff_scale).
+    The plain definition is the default: every float exact (fp64), only the quantisers'
+    decisions in fp32. The storage options below round the tensors a path hands from one
+    kernel to the next, each as itself, where it is produced; they serve diagnosis and a
+    path whose storage type is part of its definition (the fp32 debug path).
+    attn_inputs: "fp64" keeps Q, K, V exact; "bf16", "fp16" or "fp32" rounds each of them
+    (after RoPE) to that type before attention (page "h3-metal: Apple Silicon을 위한
+    네이티브 MiniMax-H3 추론", section "Metal 4 및 TensorOps": the QKV projection routed into
+    head-major attention inputs).
     dense_inputs: "fp64" multiplies dense projections by the exact activations; "bf16"
     rounds each dense projection's activation operand to bfloat16 first (see _linear).
     act_store: "fp64" keeps the attention output O, the residual stream x1, the GELU output
-    g and the block output exact; "bf16" rounds each of them to bfloat16 where it is
-    produced, as on a path whose kernels hand each other bf16 activation tensors (the
-    same two passages: bf16 tensors between the int8/bf16 projections and attention).
-    "fp32" (attn_inputs and act_store): the same tensors rounded to fp32 (Q unscaled), as a
-    path that computes in higher precision and stores fp32 tensors hands them over.
+    g and the block output exact; "bf16" or "fp32" rounds each of them to that type where
+    it is produced.
 
     rows: token rows whose output is wanted (all if None). Q, K and V are formed for
     every token (attention needs them); everything after attention is per token and is
@@ -302,13 +305,12 @@ def block_forward(x, cond, w, *, n_heads: int, head_dim: int, grid,
     ang = rope_angles(token_positions(grid, w_scale, w_offset), head_dim, theta)
     q = apply_rope(q, ang)
     k = apply_rope(k, ang)
-    if attn_inputs == "bf16":
-        c = q_handoff_scale(head_dim)
-        q, k, v = round_bf16(q * c) / c, round_bf16(k), round_bf16(v)
-    elif attn_inputs == "fp32":
-        q, k, v = round_f32(q), round_f32(k), round_f32(v)
-    elif attn_inputs != "fp64":
+    rq = {"fp64": None, "bf16": round_bf16, "fp16": round_f16, "fp32": round_f32}
+    if attn_inputs not in rq:
         raise ValueError(attn_inputs)
+    if rq[attn_inputs] is not None:
+        r = rq[attn_inputs]
+        q, k, v = r(q), r(k), r(v)
     sel = np.arange(L) if rows is None else np.asarray(rows)
     if act_store == "bf16":
         store = round_bf16

@@ -24,10 +24,11 @@ the oracle's precision series (W8A8; int8 MLP + QKV; int8 MLP; all bf16) returns
 H3K_EUNSUPPORTED, and so does a stack that is not W8A8 or does not use the default
 LayerNorm eps and RoPE base.
 
-Precision follows the flags: by default the tensors the GPU path stores in bf16 (Q, K,
-V, O, x1, g, the block output, and the operands of bf16 projections) are rounded to
-bf16 where they are produced; with the fp32 debug flag they are rounded to fp32. All
-other arithmetic is the oracle's fp64.
+Precision: by default the oracle's plain definition (every float fp64, the quantisers'
+decisions in fp32); outputs take the type of the caller's array when they are written.
+With the fp32 debug flag the tensors that path stores (Q, K, V, O, x1, g and the block
+output) are rounded to fp32 where they are produced, since fp32 storage is part of that
+path's definition. The attention call rounds its output to its dtype argument.
 """
 import math
 from typing import Optional
@@ -40,7 +41,10 @@ from . import h3k_oracle as O
 OK, EINVAL, EUNSUPPORTED = 0, -1, -2
 F_BF16_GEMM, F_FP32_DEBUG, F_SYNC = 1, 2, 4
 F_BF16_QKV, F_BF16_OUT, F_BF16_MLP = 8, 16, 32
-DT_F32, DT_BF16 = 0, 1
+F_ATTN_BF16 = 64
+F_Q_BASE2 = 128
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
+_KNOWN_FLAGS = F_BF16_GEMM | F_FP32_DEBUG | F_SYNC | F_BF16_QKV | F_BF16_OUT | F_BF16_MLP | F_ATTN_BF16
 
 _DENSE = (F_BF16_QKV, F_BF16_OUT, F_BF16_MLP)
 # (qkv, out, mlp) projections run dense -> the oracle's variant of the precision series
@@ -62,7 +66,7 @@ def _variant(flags: int) -> Optional[str]:
 
 
 def _storage(flags: int) -> str:
-    return "fp32" if flags & F_FP32_DEBUG else "bf16"
+    return "fp32" if flags & F_FP32_DEBUG else "fp64"
 
 
 def _oracle_weights(w, variant: str) -> dict:
@@ -108,6 +112,8 @@ def h3k_ref_block_forward_grid(x_in, x_out, cond, w, dm, T, Hg, Wg, w_pos_scale,
     L = T * Hg * Wg
     if min(T, Hg, Wg) <= 0 or not _dims_ok(_Grid(dm, T, Hg, Wg), L):
         return EINVAL
+    if flags & ~_KNOWN_FLAGS:
+        return EINVAL
     variant = _variant(flags)
     if variant is None:
         return EUNSUPPORTED
@@ -119,7 +125,7 @@ def h3k_ref_block_forward_grid(x_in, x_out, cond, w, dm, T, Hg, Wg, w_pos_scale,
                         n_heads=dm.n_heads, head_dim=dm.head_dim, grid=(T, Hg, Wg),
                         variant=variant, w_scale=w_pos_scale, w_offset=w_pos_offset,
                         eps=float(dm.ln_eps), theta=float(dm.rope_theta), attn_inputs=st,
-                        dense_inputs="bf16" if st == "bf16" else "fp64", act_store=st)
+                        act_store=st)
     _write(x_out, y)
     return OK
 
@@ -133,14 +139,23 @@ def h3k_ref_block_forward(x_in, x_out, cond, w, dm, L, flags, ws=None, ws_bytes=
                                       dm.grid_w, 1.0, 0.0, flags)
 
 
-def h3k_ref_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, flags,
+def h3k_ref_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, dtype, flags,
                       stream=None) -> int:
     """o[l, e*Dh + j] = sum_k softmax_k(q[e,l,:] . k[e,k,:] * softmax_scale) v[e,j,k]
-    with q, k [H, L, Dh], v transposed [H, Dh, L] and o [L, H*Dh]; o is rounded to the
-    storage type of the flags. The oracle's attention scales by 1/sqrt(Dh), so q enters
-    multiplied by softmax_scale * sqrt(Dh)."""
+    with q, k [H, L, Dh], v transposed [H, Dh, L] and o [L, H*Dh], computed from the
+    values q, k, v hold and rounded once to `dtype` (the type the call's o has). With
+    F_Q_BASE2, q holds base-2 logits (q * softmax_scale * log2 e), so the scores are
+    q . k * ln 2. The oracle's attention scales by 1/sqrt(Dh), so q enters multiplied by
+    softmax_scale * sqrt(Dh)."""
     if n_heads <= 0 or L <= 0 or head_dim <= 0 or not softmax_scale > 0:
         return EINVAL
+    if dtype not in (DT_F32, DT_BF16, DT_F16) or flags & ~(F_SYNC | F_Q_BASE2):
+        return EINVAL
+    if flags & F_Q_BASE2:
+        if dtype == DT_F32:
+            return EINVAL
+        # q holds q * scale * log2(e): softmax_2(q . k) = softmax(q . k * ln 2)
+        softmax_scale = math.log(2.0)
     n = n_heads * L * head_dim
     if np.size(q) != n or np.size(k) != n or np.size(v) != n or np.size(o) != n:
         return EINVAL
@@ -148,7 +163,7 @@ def h3k_ref_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, flags,
     kh = _host(k).reshape(n_heads, L, head_dim).transpose(1, 0, 2)
     vh = _host(v).reshape(n_heads, head_dim, L).transpose(2, 0, 1)
     res = O.attention(qh * (softmax_scale * math.sqrt(head_dim)), kh, vh)
-    store = O.round_f32 if flags & F_FP32_DEBUG else O.round_bf16
+    store = {DT_F32: O.round_f32, DT_BF16: O.round_bf16, DT_F16: O.round_f16}[dtype]
     _write(o, store(res.reshape(L, n_heads * head_dim)))
     return OK
 
@@ -160,6 +175,8 @@ def h3k_ref_stack_forward(x_in, x_out, cond, blocks, n_blocks, dm, L, tr_begin, 
     if not _dims_ok(dm, L) or n_blocks <= 0 or len(blocks) < n_blocks:
         return EINVAL
     if not (0 <= tr_begin <= tr_end <= n_blocks) or (tr_begin < tr_end and dm.grid_w % 2):
+        return EINVAL
+    if flags & ~_KNOWN_FLAGS:
         return EINVAL
     variant = _variant(flags)
     # the oracle stack runs W8A8 blocks with the default LayerNorm eps and RoPE base

@@ -24,21 +24,80 @@ def f32_stored_ok(got, ref):
     return (1 - eq) * got.size <= max(1.0, 1e-4 * got.size) and rel < 1e-8, (eq, rel)
 
 
+# unit roundoff (half the spacing above 1) of the 16-bit storage types
+U_F16, U_BF16 = 2.0 ** -11, 2.0 ** -8
+
+
+def q_scale32(Dh: int) -> float:
+    """The factor the QKV epilogue applies to Q on the 16-bit paths: (1 / sqrt(Dh)) * log2(e)
+    evaluated in fp32 as the library's host code does (the stored Q is documented as Q times
+    log2(e) / sqrt(Dh), rounded once)."""
+    f = np.float32
+    return float(f(f(1.0) / np.sqrt(f(Dh))) * f(1.4426950408889634))
+
+
+def rounded_match(got, ref_exact, rnd, ulp_of):
+    """(fraction of elements equal to rnd(ref_exact), largest |got - rnd(ref)| in units of the
+    storage spacing at rnd(ref)): a stage computed in fp32 and stored once in a 16-bit type
+    equals the exact value rounded, apart from values whose fp32 result lies across a rounding
+    boundary from the exact one (one unit off)."""
+    r = rnd(ref_exact)
+    eq = float(np.mean(got == r))
+    units = np.abs(got - r) / ulp_of(r)
+    return eq, float(units.max()) if units.size else 0.0
+
+
+def _spacing(bits, min_normal_exp):
+    """Spacing of the values of a binary format with `bits` significant bits whose smallest
+    normal value is 2^(min_normal_exp - 1), at r (constant below it: the subnormal step)."""
+    def ulp(r):
+        _, e = np.frexp(np.abs(r))
+        return np.ldexp(1.0, np.maximum(e - bits, min_normal_exp - bits))
+    return ulp
+
+
+ULP_F16 = _spacing(11, -13)    # spacing of fp16 values (subnormal step 2^-24)
+ULP_BF16 = _spacing(8, -125)
+
+
 def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     """Teacher-forced per-stage parity on token rows `rows` (W8A8 path) of the block run
     recorded in `r` (inputs, weights, workspace); `grid` and the w-position mapping give
-    the token grid the block ran on (default: the workload's)."""
+    the token grid the block ran on (default: the workload's). Each stage of the oracle gets
+    the GPU's own input to that stage.
+
+    fp32 debug path: every stored tensor equals the oracle's value rounded to fp32 (the path
+    computes in fp64). 16-bit paths: Q, K, V, x1, g and the output each equal the oracle's
+    exact value rounded once to their storage type on >= 99.9% of elements and are never more
+    than one unit off; attention meets a per-row bound; the quantisers' codes are identical."""
     grid = wl.grid if grid is None else grid
     L = grid[0] * grid[1] * grid[2]
     d, F, H, Dh = wl.d, wl.d_ff, wl.n_heads, wl.head_dim
     f32 = bool(r["flags"] & h3k.F_FP32_DEBUG)
+    attn_bf16 = bool(r["flags"] & h3k.F_ATTN_BF16)
     T = torch.float32 if f32 else torch.bfloat16
+    A = torch.float32 if f32 else (torch.bfloat16 if attn_bf16 else torch.float16)  # Q, K, V, O
+    rA, ulpA, uA = (O.round_bf16, ULP_BF16, U_BF16) if attn_bf16 else (O.round_f16, ULP_F16, U_F16)
     ws, lay = r["ws"], r["lay"]
     V = lambda n, dt, shape: h3k.ws_view(ws, lay, n, dt, shape)
     w = oracle_weights(r["bw"])
     rows = np.asarray(rows)
     tq = torch.as_tensor(rows, device="cuda")
     stats = {}
+
+    def exact16(name, got, ref, rnd, ulp_of, arith=None, min_eq=0.999):
+        """got is ref rounded once to its storage type: >= min_eq of the elements identical to
+        rnd(ref), and every element within half a unit of ref plus `arith`, a bound of the fp32
+        arithmetic before the rounding; without `arith`, no element more than one unit from
+        rnd(ref). (Where fp32 arithmetic cancels, as in RoPE's difference of products, a
+        small result can be several of its own units away while within the arithmetic bound.)"""
+        stats[name + "_eq"], units = rounded_match(got, ref, rnd, ulp_of)
+        assert stats[name + "_eq"] >= min_eq, (name, stats[name + "_eq"])
+        if arith is None:
+            assert units <= 1.0, (name, units)
+        else:
+            excess = np.abs(got - ref) - 0.5 * ulp_of(rnd(ref)) - arith
+            assert excess.max() <= 0, (name, float(excess.max()))
 
     m_gpu = np64(V("m", torch.float32, (6 * d,)))
     stats["m"] = rel_l2(m_gpu, O.adaln_modulation(w["w_ada"], np64(r["c"])))
@@ -59,12 +118,11 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     q_ref = O.apply_rope(y[:, :d].reshape(-1, H, Dh), ang)
     k_ref = O.apply_rope(y[:, d:2 * d].reshape(-1, H, Dh), ang)
     v_ref = y[:, 2 * d:].reshape(-1, H, Dh)
-    q_all = V("q", T, (H, L, Dh))
-    k_all = V("k", T, (H, L, Dh))
-    vt_all = V("vt", T, (H, Dh, L))
-    # on the bf16 path Q is stored with the base-2 softmax scale applied
-    qs = 1.0 if f32 else O.q_handoff_scale(Dh)
-    q_ref = q_ref * qs
+    q_all = V("q", A, (H, L, Dh))
+    k_all = V("k", A, (H, L, Dh))
+    vt_all = V("vt", A, (H, Dh, L))
+    # on the 16-bit paths Q is stored with the base-2 softmax scale applied
+    qs = 1.0 if f32 else q_scale32(Dh)
     q_g = np64(q_all[:, tq, :]).transpose(1, 0, 2)
     k_g = np64(k_all[:, tq, :]).transpose(1, 0, 2)
     v_g = np64(vt_all[:, :, tq]).transpose(2, 0, 1)
@@ -73,21 +131,33 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
             ok, (stats[n + "_eq"], stats[n]) = f32_stored_ok(g_, ref)
             assert ok, stats
     else:
-        stats["q"], stats["k"], stats["v"] = rel_l2(q_g, q_ref), rel_l2(k_g, k_ref), rel_l2(v_g, v_ref)
-        assert max(stats["q"], stats["k"], stats["v"]) < 4e-3, stats
+        # fp32 dequant (two roundings), RoPE from an fp32 table (a difference of two rounded
+        # products) and, for Q, the scale: at most 8 fp32 roundings of |y0| + |y1| for a pair
+        # (y0, y1), 3 of |y| for V. The 16-bit rounding is then one of the value computed in
+        # fp32, so a value near a rounding boundary may land one unit from rnd(exact): about
+        # (fp32 error) / (fp16 spacing), more where RoPE's difference cancels, so Q and K allow
+        # 0.5% of elements there; each element stays within half a unit plus that bound.
+        e32 = 2.0 ** -24
+        yp = np.abs(y[:, :2 * d]).reshape(-1, 2 * d // 2, 2).sum(-1).repeat(2, axis=-1)
+        for n, g_, ref, arith, me in (
+                ("q", q_g, q_ref * qs, 8 * e32 * qs * yp[:, :d].reshape(-1, H, Dh), 0.995),
+                ("k", k_g, k_ref, 8 * e32 * yp[:, d:].reshape(-1, H, Dh), 0.995),
+                ("v", v_g, v_ref, 3 * e32 * np.abs(v_ref), 0.999)):
+            exact16(n, g_, ref, rA, ulpA, arith, me)
 
-    # attention rows from the GPU's full Q, K, V (O stored in the activation type)
+    # attention rows from the GPU's full Q, K, V (O stored in the attention's output type)
     qf = np64(q_all).transpose(1, 0, 2) / qs
     kf = np64(k_all).transpose(1, 0, 2)
     vf = np64(vt_all).transpose(2, 0, 1)
-    o_ref = O.attention(qf, kf, vf, rows).reshape(len(rows), d)
-    o_g = np64(V("o", T, (L, d))[tq])
+    o_ref = O.attention(qf, kf, vf, rows)
+    o_g = np64(V("o", A, (L, d))[tq])
     if f32:  # fp64 attention, O rounded once to fp32
-        ok, (stats["o_eq"], stats["o"]) = f32_stored_ok(o_g, o_ref)
+        ok, (stats["o_eq"], stats["o"]) = f32_stored_ok(o_g, o_ref.reshape(len(rows), d))
         assert ok, stats
-    else:
-        stats["o"] = rel_l2(o_g, o_ref)
-        assert stats["o"] < 1e-2, stats
+    else:  # per (query, head) row: P and O each rounded once to the operand type
+        err = np.linalg.norm(o_g.reshape(-1, H, Dh) - o_ref, axis=-1) / np.linalg.norm(o_ref, axis=-1)
+        stats["o_row_max"] = float(err.max())
+        assert stats["o_row_max"] <= 4 * uA, stats
 
     # quantiser of O on the GPU's own tensor: identical codes
     qo, so = O.quantize_rows(o_g)
@@ -101,8 +171,7 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
         ok, (stats["x1_eq"], stats["x1"]) = f32_stored_ok(x1, x1_ref)
         assert ok, stats
     else:
-        stats["x1"] = rel_l2(x1, O.round_bf16(x1_ref))
-        assert stats["x1"] < 1e-4, stats
+        exact16("x1", x1, x1_ref, O.round_bf16, ULP_BF16)
 
     # second LN + quantiser from the GPU's x1
     qa2_ref, sa2_ref = O.quantize_rows(O.modulate(O.layer_norm(x1), mod["shift2"], mod["scale2"]))
@@ -122,10 +191,11 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
         # pointwise: fp64 GELU rounded to fp32, within one ulp (2^-23 relative) of the exact value
         bound = 2.0 ** -23 * np.abs(g_ref) + 1e-45
     else:
-        stats["g"] = rel_l2(g_g, O.round_bf16(g_ref))
-        assert stats["g"] < 1e-4, stats
-        # pointwise: the fp32 dequant and the erf approximation stay within 1e-6 (1 + |u|);
+        # g is the erf GELU evaluated through a polynomial erfc (absolute error ~1e-7 (1 + |u|),
+        # many bf16 units where g is tiny), so g is held to a pointwise bound rather than to
+        # rnd(exact): the fp32 dequant and the erf approximation stay within 1e-6 (1 + |u|);
         # storing g in bf16 (8 significant bits) adds at most 2^-8 of |g|
+        stats["g_eq"], _ = rounded_match(g_g, g_ref, O.round_bf16, ULP_BF16)
         bound = 1e-6 * (1 + np.abs(u_ref)) + 2.0 ** -8 * (np.abs(g_ref) + 1e-6 * (1 + np.abs(u_ref)))
     stats["g_pw"] = float(np.max(np.abs(g_g - g_ref) / bound))
     assert stats["g_pw"] <= 1.0, stats
@@ -140,13 +210,20 @@ def check_stages(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0, label=None):
     if f32:
         ok, (stats["x2_eq"], stats["x2"]) = f32_stored_ok(x2, x2_ref)
     else:
-        stats["x2"] = rel_l2(x2, x2_ref)
+        stats["x2_eq"], units = rounded_match(x2, x2_ref, O.round_bf16, ULP_BF16)
+        ok = stats["x2_eq"] >= 0.999 and units <= 1.0
     print(label or wl.name, {k: (f"{v:.3e}" if isinstance(v, float) else v) for k, v in stats.items()})
-    if f32:
-        assert ok, stats
-    else:
-        assert stats["x2"] < 4e-3, stats
+    assert ok, stats
     return stats
+
+
+# Bound of the code-forced comparison against the plain arithmetic on a 16-bit path. With
+# the codes shared, what remains is the storage of x1 and of the output in bf16 (each at
+# most 2^-8 relative per element, 2^-8 / sqrt(3) in root mean square for a uniformly
+# spread significand) and the per-token scales of the O, x1 and g quantisers, each taken
+# from a stored 16-bit tensor (at most one rounding of its largest element). Four bf16
+# roundings' root-mean-square errors added: 4 * 2^-8 / sqrt(3).
+FORCED_16BIT_TOL = 4 * 2.0 ** -8 / 3 ** 0.5
 
 
 def code_forced_output(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0):
@@ -155,14 +232,14 @@ def code_forced_output(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0):
     int8 products, RoPE, attention, LayerNorm, GELU, residuals) is the oracle's own. Codes may
     legitimately differ at near-ties between fp32 and fp64 inputs; forcing them isolates the
     float arithmetic of the path from the way a flipped code spreads (a flipped code changes a
-    token's Q, K and V, and attention hands that to every query). The tensors the path stores
-    are rounded as it stores them: the modulation to fp32, and Q, K, V, O, x1, g and the output
-    to bf16 (Q times the base-2 softmax scale), or to fp32 on the debug path."""
+    token's Q, K and V, and attention hands that to every query). On the 16-bit paths the
+    arithmetic is the plain definition (no storage rounding modelled); on the fp32 debug path
+    the tensors it stores are rounded to fp32, since that storage is part of its definition."""
     grid = wl.grid if grid is None else grid
     L = grid[0] * grid[1] * grid[2]
     d, F, H, Dh = wl.d, wl.d_ff, wl.n_heads, wl.head_dim
     f32 = bool(r["flags"] & h3k.F_FP32_DEBUG)
-    rb = O.round_f32 if f32 else O.round_bf16
+    rb = O.round_f32 if f32 else (lambda t: t)
     ws, lay = r["ws"], r["lay"]
     V = lambda n, dt, shape: h3k.ws_view(ws, lay, n, dt, shape)
     w = oracle_weights(r["bw"])
@@ -176,14 +253,9 @@ def code_forced_output(wl, r, rows, grid=None, w_scale=1.0, w_offset=0.0):
     qa = V("qa", torch.int8, (L, d)).cpu().numpy()
     y = O.int8_matmul(qa, w["q_qkv"]) * sa.astype(np.float64)[:, None] * w["s_qkv"]
     ang = O.rope_angles(O.token_positions(grid, w_scale, w_offset), Dh)
-    q = O.apply_rope(y[:, :d].reshape(L, H, Dh), ang)
-    k = O.apply_rope(y[:, d:2 * d].reshape(L, H, Dh), ang)
-    v = y[:, 2 * d:].reshape(L, H, Dh)
-    if f32:
-        q, k, v = O.round_f32(q), O.round_f32(k), O.round_f32(v)
-    else:
-        c = O.q_handoff_scale(Dh)
-        q, k, v = O.round_bf16(q * c) / c, O.round_bf16(k), O.round_bf16(v)
+    q = rb(O.apply_rope(y[:, :d].reshape(L, H, Dh), ang))
+    k = rb(O.apply_rope(y[:, d:2 * d].reshape(L, H, Dh), ang))
+    v = rb(y[:, 2 * d:].reshape(L, H, Dh))
     o = rb(O.attention(q, k, v, rows).reshape(len(rows), d))
     _, so = O.quantize_rows(o)
     x1 = rb(x[rows] + mod["gate1"] * (O.int8_matmul(codes("qo", d), w["q_o"]) *

@@ -67,8 +67,8 @@ def test_workspace_monotone_and_layout():
                                    h3k.F_BF16_QKV | h3k.F_BF16_OUT, h3k.F_BF16_GEMM])
 def test_workspace_mixed_precision(flags):
     # each projection's buffers follow its own precision: a bf16 projection has no int8
-    # codes and reads a bf16 tensor (h, O, h2 or g); O, x1 and g are bf16 on every path
-    # but the fp32 debug one
+    # codes and reads a bf16 tensor (h, O, h2 or g); Q, K, V^T, O, x1 and g take two bytes
+    # per element on every path but the fp32 debug one
     L, d, F = 512, 256, 1024
     dm = tiny_dims()
     lay = h3k.workspace_layout(dm, L, flags)
@@ -113,7 +113,8 @@ def _block(dm, L, flags=0, x=FAKE, out=FAKE, cond=FAKE, ws=FAKE, ws_bytes=1 << 4
     (dict(flags=h3k.F_BF16_OUT), h3k.EINVAL),                   # dense out-proj weights missing
     (dict(flags=h3k.F_BF16_MLP), h3k.EINVAL),                   # dense MLP weights missing
     (dict(flags=h3k.F_BF16_MLP | h3k.F_FP32_DEBUG), h3k.EUNSUPPORTED),
-    (dict(flags=64), h3k.EINVAL),
+    (dict(flags=256), h3k.EINVAL),                              # unknown flag bit
+    (dict(flags=h3k.F_ATTN_BF16 | h3k.F_FP32_DEBUG), h3k.EUNSUPPORTED),
 ])
 def test_block_validation(case, code):
     dm = tiny_dims(**case.pop("dm", {}))
@@ -148,9 +149,14 @@ def test_component_validation():
     assert lib.h3k_quantize_weights(None, h3k.DT_BF16, 4, 8, FAKE, FAKE, None) == h3k.EINVAL
     assert lib.h3k_gemm_i8_i32(FAKE, FAKE, FAKE, 16, 100, 128, None) == h3k.EUNSUPPORTED
     assert lib.h3k_gemm_i8_i32(FAKE, FAKE, FAKE, 0, 256, 128, None) == h3k.EINVAL
-    assert lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, 4, 64, 96, 0.1, 0, None) == h3k.EUNSUPPORTED
-    assert lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, 4, 60, 64, 0.1, 0, None) == h3k.EUNSUPPORTED
-    assert lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, 4, 64, 64, -1.0, 0, None) == h3k.EINVAL
+    att = lambda *a: lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, *a, None)  # noqa: E731
+    assert att(4, 64, 96, 0.1, h3k.DT_F16, 0) == h3k.EUNSUPPORTED          # head_dim
+    assert att(4, 60, 64, 0.1, h3k.DT_BF16, 0) == h3k.EUNSUPPORTED         # L % 8
+    assert att(4, 64, 64, -1.0, h3k.DT_F16, 0) == h3k.EINVAL               # scale
+    assert att(4, 64, 64, 0.1, 7, 0) == h3k.EINVAL                         # dtype
+    assert att(4, 64, 64, 0.1, h3k.DT_F16, h3k.F_FP32_DEBUG) == h3k.EINVAL  # not an attention flag
+    assert att(4, 64, 64, 0.1, h3k.DT_F32, h3k.F_Q_BASE2) == h3k.EINVAL    # base-2 q needs 16-bit
+    assert lib.h3k_row_quantize(FAKE, 9, 4, 16, FAKE, FAKE, None) == h3k.EINVAL
     assert lib.h3k_ln_modulate_quant(FAKE, h3k.DT_BF16, FAKE, FAKE, 4, 300, 1e-6, FAKE, FAKE, None) == h3k.EUNSUPPORTED
     assert lib.h3k_row_quantize(FAKE, h3k.DT_BF16, 4, 12, FAKE, FAKE, None) == h3k.EUNSUPPORTED
     assert lib.h3k_adaln_modulation(FAKE, FAKE, FAKE, 10, 12, None) == h3k.EUNSUPPORTED
@@ -192,3 +198,85 @@ def test_denoise_validation():
     rc = lib.h3k_denoise(FAKE, FAKE, arr, 2, C.byref(dm), 512, 4, 1, 1, 2, 0, 0, 0, FAKE, 1024, None)
     assert rc == h3k.ENOSPC
     assert h3k.denoise_workspace_bytes(dm, 512) > h3k.stack_workspace_bytes(dm, 512, 0, 0)
+
+
+# ----------------------------------------------------------------------------- binding checks
+# The binding checks every tensor's dtype and shape against the dims and flags before the
+# library sees a pointer (dtype and shape first, so these run without a GPU), then that it
+# is a contiguous tensor on the current GPU.
+import torch  # noqa: E402
+
+
+def _tiny_weights(dims, dtype_ada=torch.bfloat16):
+    d, F, dc = dims.d, dims.d_ff, dims.d_cond
+    w = h3k.BlockWeights(w_ada=torch.zeros(6 * d, dc, dtype=dtype_ada))
+    for k, shp in {"qkv": (3 * d, d), "o": (d, d), "up": (F, d), "down": (d, F)}.items():
+        setattr(w, "w_" + k, torch.zeros(shp, dtype=torch.int8))
+        setattr(w, "s_" + k, torch.zeros(shp[0], dtype=torch.float32))
+    return w
+
+
+@pytest.mark.parametrize("case,msg", [
+    (dict(x=dict(dtype=torch.float32)), "x must have dtype torch.bfloat16"),
+    (dict(flags=h3k.F_FP32_DEBUG), "x must have dtype torch.float32"),
+    (dict(x=dict(shape=(512, 128))), "x must have shape (512, 256)"),
+    (dict(cond=dict(dtype=torch.bfloat16)), "cond must have dtype torch.float32"),
+    (dict(cond=dict(shape=(255,))), "cond must have shape (256,)"),
+    (dict(out=dict(shape=(511, 256))), "out must have shape (512, 256)"),
+    (dict(w=dict(w_qkv=torch.zeros(768, 128, dtype=torch.int8))), "w_qkv must have shape (768, 256)"),
+    (dict(w=dict(s_up=torch.zeros(1024, dtype=torch.float16))), "s_up must have dtype torch.float32"),
+    (dict(w=dict(w_ada=torch.zeros(1536, 256, dtype=torch.float32))), "w_ada must have dtype torch.bfloat16"),
+    (dict(flags=h3k.F_BF16_MLP), "wb_up is required"),
+    (dict(), "x must be a GPU tensor"),     # right dtypes and shapes, host memory
+])
+def test_binding_block_checks(case, msg):
+    dims = tiny_dims()
+    flags = case.get("flags", 0)
+    xs = dict(dtype=torch.float32 if flags & h3k.F_FP32_DEBUG else torch.bfloat16, shape=(512, 256))
+    xs.update(case.get("x", {}))
+    x = torch.zeros(xs["shape"], dtype=xs["dtype"])
+    if "flags" in case and flags & h3k.F_FP32_DEBUG:  # x right, the default out follows x
+        x = torch.zeros(512, 256, dtype=torch.bfloat16)
+    cs = dict(dtype=torch.float32, shape=(256,))
+    cs.update(case.get("cond", {}))
+    c = torch.zeros(cs["shape"], dtype=cs["dtype"])
+    out = torch.zeros(case["out"]["shape"], dtype=x.dtype) if "out" in case else None
+    w = _tiny_weights(dims)
+    for k, v in case.get("w", {}).items():
+        setattr(w, k, v)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match=re.escape(msg)):
+        h3k.block_forward(x, c, w, dims, flags, ws=ws, out=out)
+
+
+def test_binding_component_checks():
+    bf, f32, f16, i8 = torch.bfloat16, torch.float32, torch.float16, torch.int8
+    with pytest.raises(ValueError, match="k must have dtype torch.float16"):
+        h3k.attention(torch.zeros(2, 64, 64, dtype=f16), torch.zeros(2, 64, 64, dtype=bf),
+                      torch.zeros(2, 64, 64, dtype=f16))
+    with pytest.raises(ValueError, match=re.escape("vt must have shape (2, 64, 64)")):
+        h3k.attention(torch.zeros(2, 64, 64, dtype=bf), torch.zeros(2, 64, 64, dtype=bf),
+                      torch.zeros(2, 32, 64, dtype=bf))
+    with pytest.raises(ValueError, match="q must have dtype"):
+        h3k.attention(torch.zeros(2, 64, 64, dtype=i8), torch.zeros(2, 64, 64, dtype=i8),
+                      torch.zeros(2, 64, 64, dtype=i8))
+    with pytest.raises(ValueError, match=re.escape("b must have shape (256, 128)")):
+        h3k.gemm_i8_i32(torch.zeros(8, 128, dtype=i8), torch.zeros(256, 64, dtype=i8))
+    with pytest.raises(ValueError, match="a must have dtype torch.int8"):
+        h3k.gemm_i8_i32(torch.zeros(8, 128, dtype=f32), torch.zeros(256, 128, dtype=i8))
+    with pytest.raises(ValueError, match="x must have dtype"):
+        h3k.row_quantize(torch.zeros(4, 16, dtype=i8))
+    with pytest.raises(ValueError, match=re.escape("scale must have shape (256,)")):
+        h3k.ln_modulate_quant(torch.zeros(4, 256, dtype=bf), torch.zeros(256, dtype=f32),
+                              torch.zeros(128, dtype=f32))
+    with pytest.raises(ValueError, match="xr_out must have dtype torch.bfloat16"):
+        h3k.token_unpair(torch.zeros(16, 8, dtype=bf), torch.zeros(8, 8, dtype=f32),
+                         torch.zeros(8, 8, dtype=bf), (1, 2, 8))
+    with pytest.raises(ValueError, match=re.escape("x must have shape (16, 8)")):
+        h3k.token_pair(torch.zeros(12, 8, dtype=bf), (1, 2, 8))
+    with pytest.raises(ValueError, match=re.escape("cond must have shape (8,)")):
+        h3k.adaln_modulation(torch.zeros(48, 8, dtype=bf), torch.zeros(9, dtype=f32))
+    with pytest.raises(ValueError, match="w must have dtype"):
+        h3k.quantize_weights(torch.zeros(4, 8, dtype=f16))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        h3k.row_quantize(torch.zeros(4, 16, dtype=f16))

@@ -33,7 +33,7 @@ def test_kernel_work_matches_the_block_totals():
     assert w["attention"][1] == 4.0 * L * L * d  # QK^T and PV, 2 flops per multiply-add
     assert abs(w["attention"][1] - 5.498e12) < 0.001e12
     assert all(w[k][2] == "int8" for k in ("gemm_qkv", "gemm_o", "gemm_up", "gemm_down"))
-    assert w["attention"][2] == "bf16"
+    assert w["attention"][2] == "fp16"
     # bandwidth-bound kernels: bytes read once and written once
     assert w["ln_quant"][1] == L * (2 * d + d + 4)
     assert w["rowquant_g"][1] == L * (2 * F + F + 4)

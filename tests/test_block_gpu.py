@@ -1,12 +1,21 @@
 """Block parity of the HIP path against the CPU oracle on seeded synthetic workloads.
 
-End to end: relative L2 of the block output <= 2e-2 on the bf16 path and <= 1e-3 on the
-fp32 debug path. Stage by stage (teacher-forced: the oracle stage is fed the GPU's own
-input to that stage, read from the workspace): quantiser codes >= 99.99% identical, the
-GEMM+dequant+RoPE outputs and attention within bf16 storage error, and on the fp32 debug
-path (fp64 arithmetic, fp32 storage) every stored tensor identical to the oracle's value
-rounded to fp32 on >= 99.99% of elements. Full-size workloads are
-checked on sampled token rows the oracle computes one by one."""
+End to end against the oracle's plain definition (every float fp64, the quantisers'
+decisions in fp32): relative L2 of the block output <= 2e-2 on the default path (W8A8
+GEMMs, fp16 attention operands, bf16 activations) and on the precision series; the fp32
+debug path, whose definition stores fp32 tensors, <= 1e-3 against the oracle rounding the
+same tensors to fp32. Stage by stage (teacher-forced: the oracle stage is fed the GPU's own
+input to that stage, read from the workspace): quantiser codes >= 99.99% identical, every
+stored 16-bit tensor equal to the exact value rounded once, attention within a per-row
+bound, and on the fp32 debug path every stored tensor identical to the oracle's value
+rounded to fp32. With the quantiser codes shared, the output meets a bound derived from its
+bf16 storage. Full-size workloads are checked on sampled token rows the oracle computes
+one by one.
+
+The bf16-operand attention (F_ATTN_BF16) is held to 3e-2 end to end: on these workloads
+the scores have a standard deviation near 10, the softmax is close to an argmax, and the
+bf16 rounding of Q, K and V alone moves O by about 6.5e-3, which the O, x1 and g
+quantisers spread into code flips (2.2-2.4e-2 measured against the plain oracle)."""
 import numpy as np
 import pytest
 import torch
@@ -28,6 +37,13 @@ def _wl(name, **kw):
 
 
 BF16_ANY = h3k.F_BF16_GEMM | h3k.F_BF16_QKV | h3k.F_BF16_OUT | h3k.F_BF16_MLP
+TOL, TOL_ATTN_BF16, FP32_TOL = 2e-2, 3e-2, 1e-3
+
+
+def tol_of(flags):
+    if flags & h3k.F_FP32_DEBUG:
+        return FP32_TOL
+    return TOL_ATTN_BF16 if flags & h3k.F_ATTN_BF16 else TOL
 # the precision series: oracle variant -> flags that select the bf16 projections
 SERIES = [("w8a8", 0), ("int8_mlp_qkv", h3k.F_BF16_OUT),
           ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT), ("bf16gemm", h3k.F_BF16_GEMM)]
@@ -50,27 +66,32 @@ def run_gpu(wl, flags=0, zero_gates=False, gen_device="cpu"):
                 lay=h3k.workspace_layout(dims, wl.L, flags))
 
 
-def oracle_full(wl, r, variant="w8a8", rows=None, attn_inputs=None):
-    """The oracle block on the run's inputs. On the bf16 path the attention consumes bf16
-    Q, K, V, every bf16 projection bf16 activations, and O, x1, g and the output are stored
-    as bf16, so the oracle rounds them there (attn_inputs = dense_inputs = act_store =
-    "bf16"). The fp32 debug path computes in fp64 and stores the same tensors as fp32, which
-    the oracle rounds likewise (attn_inputs = act_store = "fp32")."""
-    if attn_inputs is None:
-        attn_inputs = "fp32" if r["flags"] & h3k.F_FP32_DEBUG else "bf16"
+def oracle_full(wl, r, variant="w8a8", rows=None):
+    """The oracle block on the run's inputs: the plain definition for the 16-bit paths; for
+    the fp32 debug path, which computes in fp64 and stores its tensors as fp32 by
+    definition, the oracle rounds the same tensors to fp32 (attn_inputs = act_store =
+    "fp32")."""
+    st = "fp32" if r["flags"] & h3k.F_FP32_DEBUG else "fp64"
     w = oracle_weights(r["bw"], r["dense"] if variant != "w8a8" else None)
     return O.block_forward(np64(r["x"]), np64(r["c"]), w, n_heads=wl.n_heads, head_dim=wl.head_dim,
-                           grid=wl.grid, variant=variant, rows=rows, attn_inputs=attn_inputs,
-                           dense_inputs="bf16" if attn_inputs == "bf16" else "fp64",
-                           act_store=attn_inputs)
+                           grid=wl.grid, variant=variant, rows=rows, attn_inputs=st, act_store=st)
+
+
+def check_forced(wl, r, rows, got, label):
+    """End to end with the GPU's quantiser codes shared (the float arithmetic alone)."""
+    forced = rel_l2(got, _stages.code_forced_output(wl, r, rows))
+    bar = FP32_FORCED_TOL if r["flags"] & h3k.F_FP32_DEBUG else _stages.FORCED_16BIT_TOL
+    print(f"{label}: with the GPU's codes {forced:.3e} (bar {bar:.1e})")
+    assert forced <= bar
 
 
 # ----------------------------------------------------------------------------- tiny, full oracle
-@pytest.mark.parametrize("variant,flags,tol", [("w8a8", 0, 2e-2), ("w8a8", h3k.F_FP32_DEBUG, 1e-3),
-                                               ("bf16gemm", h3k.F_BF16_GEMM, 2e-2),
-                                               ("int8_mlp_qkv", h3k.F_BF16_OUT, 2e-2),
-                                               ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT, 2e-2),
-                                               ("bf16gemm", h3k.F_BF16_QKV | h3k.F_BF16_OUT | h3k.F_BF16_MLP, 2e-2)])
+@pytest.mark.parametrize("variant,flags,tol", [("w8a8", 0, TOL), ("w8a8", h3k.F_FP32_DEBUG, FP32_TOL),
+                                               ("w8a8", h3k.F_ATTN_BF16, TOL),
+                                               ("bf16gemm", h3k.F_BF16_GEMM, TOL),
+                                               ("int8_mlp_qkv", h3k.F_BF16_OUT, TOL),
+                                               ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT, TOL),
+                                               ("bf16gemm", h3k.F_BF16_QKV | h3k.F_BF16_OUT | h3k.F_BF16_MLP, TOL)])
 def test_block_tiny(variant, flags, tol):
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl, flags)
@@ -85,14 +106,14 @@ def test_block_tiny(variant, flags, tol):
 @pytest.mark.parametrize("grid,H,Dh", [((3, 5, 8), 4, 64), ((2, 3, 12), 2, 128), ((1, 1, 8), 4, 64)])
 def test_block_ragged(grid, H, Dh):
     wl = _wl("tiny", grid=grid, n_heads=H, head_dim=Dh)
-    for variant, flags, tol in [("w8a8", 0, 2e-2), ("w8a8", h3k.F_FP32_DEBUG, 1e-3)]:
+    for variant, flags, tol in [("w8a8", 0, TOL), ("w8a8", h3k.F_FP32_DEBUG, FP32_TOL)]:
         r = run_gpu(wl, flags)
         err = rel_l2(np64(r["out"]), oracle_full(wl, r, variant))
         assert err <= tol, (grid, flags, err)
 
 
 @pytest.mark.parametrize("flags", [0, h3k.F_FP32_DEBUG, h3k.F_BF16_GEMM, h3k.F_BF16_OUT,
-                                   h3k.F_BF16_QKV | h3k.F_BF16_OUT])
+                                   h3k.F_BF16_QKV | h3k.F_BF16_OUT, h3k.F_ATTN_BF16])
 def test_block_zero_gates_identity(flags):
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl, flags, zero_gates=True)
@@ -109,8 +130,8 @@ def test_block_inplace_and_deterministic():
     assert torch.equal(xin, r["out"])
 
 
-@pytest.mark.parametrize("flags,tol", [(0, 2e-2), (h3k.F_FP32_DEBUG, 1e-3),
-                                       (h3k.F_BF16_QKV | h3k.F_BF16_OUT, 2e-2)])
+@pytest.mark.parametrize("flags,tol", [(0, TOL), (h3k.F_FP32_DEBUG, FP32_TOL),
+                                       (h3k.F_BF16_QKV | h3k.F_BF16_OUT, TOL)])
 def test_block_matches_cpu_twin(flags, tol):
     # one call shape on both sides: h3k.block_forward on the device and the oracle's C-ABI
     # twin h3k_ref_block_forward on host copies of the same buffers, with the binding's own
@@ -135,7 +156,7 @@ def check_stages(wl, r, rows, label=None):
     return _stages.check_stages(wl, r, rows, label=label)
 
 
-@pytest.mark.parametrize("flags", [0, h3k.F_FP32_DEBUG])
+@pytest.mark.parametrize("flags", [0, h3k.F_FP32_DEBUG, h3k.F_ATTN_BF16])
 def test_block_tiny_stages(flags):
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl, flags)
@@ -149,7 +170,7 @@ def _sample_rows(L, n, seed):
     return np.unique(np.concatenate([[0, L - 1], rows]))
 
 
-@pytest.mark.parametrize("variant,flags", SERIES)
+@pytest.mark.parametrize("variant,flags", SERIES + [("w8a8", h3k.F_ATTN_BF16)])
 def test_block_l4096(variant, flags):
     wl = S.WORKLOADS["block_l4096"]
     r = run_gpu(wl, flags, gen_device="cuda")
@@ -158,26 +179,29 @@ def test_block_l4096(variant, flags):
     got = np64(r["out"])[rows]
     x = np64(r["x"])[rows]
     err, upd = rel_l2(got, ref), rel_l2(got - x, ref - x)
-    err64 = rel_l2(got, oracle_full(wl, r, variant, rows=rows, attn_inputs="fp64"))
-    print(f"l4096 {variant}: rel-L2 {err:.3e} update {upd:.3e} (vs fp64-attention-input oracle {err64:.3e})")
-    assert err <= 2e-2
+    print(f"l4096 {variant} flags={flags}: rel-L2 vs plain oracle {err:.3e} update {upd:.3e}")
+    assert err <= tol_of(flags)
     if variant == "w8a8":
         check_stages(wl, r, rows)
+        check_forced(wl, r, rows, got, f"l4096 flags={flags}")
 
 
-def test_block_l16384_sampled():
+@pytest.mark.parametrize("flags", [0, h3k.F_ATTN_BF16])
+def test_block_l16384_sampled(flags):
     wl = S.WORKLOADS["block_l16384"]
-    r = run_gpu(wl, 0, gen_device="cuda")
-    again = h3k.block_forward(r["x"], r["c"], r["bw"], r["dims"], 0, r["ws"])
+    r = run_gpu(wl, flags, gen_device="cuda")
+    again = h3k.block_forward(r["x"], r["c"], r["bw"], r["dims"], flags, r["ws"])
     assert torch.equal(again, r["out"])  # bitwise run-to-run determinism at full size
     rows = _sample_rows(wl.L, 48, 2)
     ref = oracle_full(wl, r, "w8a8", rows=rows)
     got = np64(r["out"])[rows]
     err = rel_l2(got, ref)
     x = np64(r["x"])[rows]
-    print(f"l16384 end-to-end sampled rel-L2 {err:.3e}, update {rel_l2(got - x, ref - x):.3e}")
-    assert err <= 2e-2
+    print(f"l16384 flags={flags}: end-to-end sampled rel-L2 vs plain oracle {err:.3e}, "
+          f"update {rel_l2(got - x, ref - x):.3e}")
+    assert err <= tol_of(flags)
     check_stages(wl, r, rows)
+    check_forced(wl, r, rows, got, f"l16384 flags={flags}")
 
 
 # The fp32 debug path computes every step in fp64 and rounds to fp32 only the tensors it
@@ -185,12 +209,11 @@ def test_block_l16384_sampled():
 # from the rare value whose fp64 results straddle an fp32 rounding boundary (and a quantiser
 # code that such a value might flip). The bar is 1e-3 end to end; with the codes shared,
 # 1e-7.
-FP32_TOL, FP32_FORCED_TOL = 1e-3, 1e-7
+FP32_FORCED_TOL = 1e-7
 
 
-@pytest.mark.parametrize("flags,tol,tol_forced", [(0, 2e-2, 1e-3),
-                                                  (h3k.F_FP32_DEBUG, FP32_TOL, FP32_FORCED_TOL)])
-def test_block_ragged_full_width_sampled(flags, tol, tol_forced):
+@pytest.mark.parametrize("flags,tol", [(0, TOL), (h3k.F_FP32_DEBUG, FP32_TOL)])
+def test_block_ragged_full_width_sampled(flags, tol):
     # d = 5120 with L = 2880 (3 x 24 x 40 grid, 8 outlier channels): the last 256-token tile
     # of every GEMM and the last 256-query block of attention are partial; sampled rows
     # include the tail. Checked stage by stage, end to end against the oracle, and end to end
@@ -203,9 +226,9 @@ def test_block_ragged_full_width_sampled(flags, tol, tol_forced):
     check_stages(wl, r, rows, label=f"l2880 flags={flags}")
     got = np64(r["out"])[rows]
     err = rel_l2(got, oracle_full(wl, r, "w8a8", rows=rows))
-    forced = rel_l2(got, _stages.code_forced_output(wl, r, rows))
-    print(f"l2880 ragged flags={flags}: rel-L2 {err:.3e}, with the GPU's codes {forced:.3e}")
-    assert err <= tol and forced <= tol_forced
+    print(f"l2880 ragged flags={flags}: rel-L2 {err:.3e}")
+    assert err <= tol
+    check_forced(wl, r, rows, got, f"l2880 ragged flags={flags}")
 
 
 @pytest.mark.parametrize("name,n_rows", [("block_l4096", 32), ("block_l16384", 24), ("block_l65536", 8)])
@@ -218,9 +241,9 @@ def test_block_fp32_sampled(name, n_rows):
     check_stages(wl, r, rows, label=f"{name} fp32")
     got = np64(r["out"])[rows]
     err = rel_l2(got, oracle_full(wl, r, "w8a8", rows=rows))
-    forced = rel_l2(got, _stages.code_forced_output(wl, r, rows))
-    print(f"{name} fp32 end-to-end sampled rel-L2 {err:.3e}, with the GPU's codes {forced:.3e}")
-    assert err <= FP32_TOL and forced <= FP32_FORCED_TOL
+    print(f"{name} fp32 end-to-end sampled rel-L2 {err:.3e}")
+    assert err <= FP32_TOL
+    check_forced(wl, r, rows, got, f"{name} fp32")
 
 
 def test_block_l65536_sampled():
@@ -233,6 +256,7 @@ def test_block_l65536_sampled():
     got = np64(r["out"])[rows]
     err = rel_l2(got, ref)
     x = np64(r["x"])[rows]
-    print(f"l65536 end-to-end sampled rel-L2 {err:.3e}, update {rel_l2(got - x, ref - x):.3e}")
-    assert err <= 2e-2
+    print(f"l65536 end-to-end sampled rel-L2 vs plain oracle {err:.3e}, update {rel_l2(got - x, ref - x):.3e}")
+    assert err <= TOL
     check_stages(wl, r, rows)
+    check_forced(wl, r, rows, got, "l65536")

@@ -1,6 +1,8 @@
 """Per-kernel parity of the HIP path against the CPU oracle on identical seeded inputs.
 Quantisers: codes identical on >= 99.99% of elements (off by at most one step), scales
-within 1e-6 relative. int32 GEMM accumulators: bit-exact. Attention: relative L2."""
+within 1e-6 relative. int32 GEMM accumulators: bit-exact. Attention: a bound on the
+relative error of every (query, head) row, derived from the rounding of P and O to the
+16-bit type; the fp32 path equals the oracle's value rounded to fp32."""
 import math
 
 import numpy as np
@@ -77,7 +79,8 @@ def test_ln_modulate_quant(rows, cols, dtype):
 
 # ----------------------------------------------------------------------------- row quant
 @pytest.mark.parametrize("rows,cols,dtype", [(129, 5120, torch.bfloat16), (33, 20480, torch.bfloat16),
-                                             (50, 1024, torch.float32), (5, 32768, torch.bfloat16)])
+                                             (50, 1024, torch.float32), (5, 32768, torch.bfloat16),
+                                             (129, 5120, torch.float16), (7, 20480, torch.float16)])
 def test_row_quantize(rows, cols, dtype):
     x = randn((rows, cols), 8, 3.0, dtype)
     x[2] = 0
@@ -113,81 +116,128 @@ def test_gemm_i8_extremes():
 
 
 # ----------------------------------------------------------------------------- attention
+# unit roundoff (half the spacing above 1) of the 16-bit types
+U16 = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+
+
+def _oracle_attn(q, k, vt, scale_mult=1.0):
+    """Oracle attention on the exact values of q, k [H, L, Dh] and vt [H, Dh, L] ->
+    [L, H, Dh]; scale_mult multiplies the 1/sqrt(Dh) softmax scale."""
+    return O.attention(np64(q).transpose(1, 0, 2) * scale_mult, np64(k).transpose(1, 0, 2),
+                       np64(vt).transpose(2, 0, 1))
+
+
+def row_errors(o, ref):
+    """Relative L2 error of every (query, head) row of o against ref, both [L, H, Dh]."""
+    num = np.linalg.norm(o - ref, axis=-1)
+    return num / np.maximum(np.linalg.norm(ref, axis=-1), 1e-300)
+
+
+def check_rows(o, ref, dtype, label):
+    """Per-row bound of a 16-bit attention output: P is rounded to the operand type (relative
+    error <= u per weight, the same rounded weights in the numerator and the row sum) and O
+    once more where it is stored (<= u per element), so a row's relative error stays below
+    a few u; the bar is 4u (u = 2^-11 fp16, 2^-8 bf16)."""
+    err = row_errors(o, ref)
+    worst = float(err.max())
+    print(f"{label}: worst row rel-L2 {worst:.3e} ({worst / U16[dtype]:.2f} u), mean {err.mean():.3e}")
+    assert worst <= 4 * U16[dtype], (label, worst, np.unravel_index(err.argmax(), err.shape))
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 56, 128), (1, 72, 128), (2, 200, 128), (3, 1000, 64),
                                     (1, 4096, 128)])
-def test_attention_bf16(H, L, Dh):
-    q = randn((H, L, Dh), 21, 1.0)
-    k = randn((H, L, Dh), 22, 1.0)
-    v = randn((H, L, Dh), 23, 1.0)
-    vt = v.transpose(1, 2).contiguous()
-    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).float().cpu().numpy()
-    ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
-                      np64(v).transpose(1, 0, 2)).reshape(L, H * Dh)
-    err = rel_l2(o, ref)
-    assert err < 1e-2, err
+def test_attention_16bit(H, L, Dh, dtype):
+    q = randn((H, L, Dh), 21, 1.0, dtype)
+    k = randn((H, L, Dh), 22, 1.0, dtype)
+    vt = randn((H, Dh, L), 23, 1.0, dtype)
+    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda())
+    assert o.dtype == dtype
+    check_rows(np64(o).reshape(L, H, Dh), _oracle_attn(q, k, vt), dtype, f"attention {dtype} H={H} L={L} Dh={Dh}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("Dh", [64, 128])
-def test_attention_running_max_per_query_tile(Dh):
+@pytest.mark.parametrize("base2", [False, True])
+def test_attention_running_max_per_query_tile(Dh, base2, dtype):
     # Some queries' scores climb to ~460 (in log2 units) over the keys, the others' fall: the
     # running maximum of the climbing rows must move many times, tile by tile, and a maximum
     # taken from the wrong query (another 16-query tile, or another column of one) would
     # overflow exp2 (inf / NaN). Query l climbs iff (l % 32 < 16) differs from (l % 16 < 8),
-    # so neighbouring tiles and the two halves of a tile have opposite signs.
+    # so neighbouring tiles and the two halves of a tile have opposite signs. base2: the
+    # block's own variant, q handed over as base-2 logits (q * log2(e) / sqrt(Dh)), whose
+    # score tiles start from -m and whose pending tile is shifted when m moves.
     L = 1024
     q = torch.zeros((1, L, Dh))
     k = torch.zeros((1, L, Dh))
     l = torch.arange(L)
     sign = torch.where(((l % 32) < 16) != ((l % 16) < 8), 1.0, -1.0)
-    q[0, :, 0] = 60.0 * sign
+    c = math.log2(math.e) / math.sqrt(Dh)
+    q[0, :, 0] = 60.0 * sign * (c if base2 else 1.0)
     k[0, :, 0] = 60.0 * torch.arange(L) / L
-    v = randn((1, L, Dh), 27, 1.0)
-    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
-    vt = v.transpose(1, 2).contiguous()
-    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).float().cpu().numpy()
+    q, k = q.to(dtype), k.to(dtype)
+    vt = randn((1, Dh, L), 27, 1.0, dtype)
+    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda(), flags=h3k.F_Q_BASE2 if base2 else 0)
+    o = np64(o).reshape(L, 1, Dh)
     assert np.all(np.isfinite(o))
-    ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
-                      np64(v).transpose(1, 0, 2)).reshape(L, Dh)
-    assert rel_l2(o, ref) < 1e-2
+    ref = _oracle_attn(q, k, vt, 1.0 / c if base2 else 1.0)
+    check_rows(o, ref, dtype, f"ramped scores {dtype} Dh={Dh} base2={base2}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_attention_base2_random(dtype):
+    # the pre-scaled variant on random data with large scores (std ~10 in natural-log
+    # units, like the block's), against the oracle at the equivalent scale
+    H, L, Dh = 2, 2056, 128
+    c = math.log2(math.e) / math.sqrt(Dh)
+    q = (torch.randn(H, L, Dh, generator=_gen(61)) * 3.2 * c).to(dtype)
+    k = (torch.randn(H, L, Dh, generator=_gen(62)) * 3.2).to(dtype)
+    vt = randn((H, Dh, L), 63, 1.0, dtype)
+    o = np64(h3k.attention(q.cuda(), k.cuda(), vt.cuda(), flags=h3k.F_Q_BASE2)).reshape(L, H, Dh)
+    check_rows(o, _oracle_attn(q, k, vt, 1.0 / c), dtype, f"base-2 q {dtype}")
 
 
 @pytest.mark.parametrize("H,L,Dh", [(2, 8, 64), (2, 264, 128)])
 def test_attention_fp32(H, L, Dh):
     q = randn((H, L, Dh), 31, 1.0, torch.float32)
     k = randn((H, L, Dh), 32, 1.0, torch.float32)
-    v = randn((H, L, Dh), 33, 1.0, torch.float32)
-    o = h3k.attention(q.cuda(), k.cuda(), v.transpose(1, 2).contiguous().cuda(),
-                      flags=h3k.F_FP32_DEBUG).cpu().numpy()
-    ref = O.attention(np64(q).transpose(1, 0, 2), np64(k).transpose(1, 0, 2),
-                      np64(v).transpose(1, 0, 2)).reshape(L, H * Dh)
+    vt = randn((H, Dh, L), 33, 1.0, torch.float32)
+    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).cpu().numpy()
+    ref = _oracle_attn(q, k, vt).reshape(L, H * Dh)
     # fp64 arithmetic, O rounded once to fp32: the oracle's value rounded to fp32
     ok, (eq, rel) = _stages.f32_stored_ok(o.astype(np.float64), ref)
     print(f"fp32 attention H={H} L={L} Dh={Dh}: identical {eq:.6f}, rel-L2 {rel:.3e}")
     assert ok
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("L,Dh", [(16384, 128), (4104, 64)])
-def test_attention_deterministic(L, Dh):
+def test_attention_deterministic(L, Dh, dtype):
     """Two runs are bitwise identical at full size (LDS races and uninitialised reads
     show up here)."""
     H = 8
-    q = torch.randn(H, L, Dh, device="cuda").to(torch.bfloat16)
-    k = torch.randn(H, L, Dh, device="cuda").to(torch.bfloat16)
-    vt = torch.randn(H, Dh, L, device="cuda").to(torch.bfloat16)
+    q = torch.randn(H, L, Dh, device="cuda").to(dtype)
+    k = torch.randn(H, L, Dh, device="cuda").to(dtype)
+    vt = torch.randn(H, Dh, L, device="cuda").to(dtype)
     o1 = h3k.attention(q, k, vt)
     for _ in range(3):
         assert torch.equal(h3k.attention(q, k, vt), o1)
 
 
-def test_attention_constant_v():
-    H, L, Dh = 2, 136, 64
-    q = randn((H, L, Dh), 41, 2.0)
-    k = randn((H, L, Dh), 42, 2.0)
-    row = randn((H, 1, Dh), 43, 1.0)
-    vt = row.expand(H, L, Dh).transpose(1, 2).contiguous()
-    o = h3k.attention(q.cuda(), k.cuda(), vt.cuda()).float().cpu().numpy().reshape(L, H, Dh)
-    want = np64(row)[:, 0, :]
-    assert np.allclose(o, np.broadcast_to(want, o.shape), rtol=1e-2, atol=1e-2)
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("Dh", [64, 128])
+def test_attention_constant_v(Dh, dtype):
+    # every key carries the same value row, so each output row is that row: the weights cancel
+    # exactly (the row sum is the sum of the same rounded P), leaving the fp32 accumulation and
+    # the one rounding of O (within one unit in the last place of the 16-bit type)
+    H, L = 2, 136
+    q = randn((H, L, Dh), 41, 2.0, dtype)
+    k = randn((H, L, Dh), 42, 2.0, dtype)
+    row = randn((H, Dh, 1), 43, 1.0, dtype)
+    vt = row.expand(H, Dh, L).contiguous()
+    o = np64(h3k.attention(q.cuda(), k.cuda(), vt.cuda())).reshape(L, H, Dh)
+    want = np.broadcast_to(np64(row)[:, :, 0], o.shape)
+    assert np.all(np.abs(o - want) <= 2 * U16[dtype] * np.abs(want) + 1e-30)
 
 
 # ----------------------------------------------------------------------------- token pairing
@@ -213,3 +263,28 @@ def test_token_pair_unpair(dtype):
     h3k.token_unpair(xp, xo, xr, grid)
     ref = O.token_unpair(np64(x), np64(xo), np64(xr), grid)
     assert rel_l2(xp.float().cpu().numpy(), ref) < (4e-3 if dtype == torch.bfloat16 else 1e-7)
+
+
+def test_token_pair_unpair_full_width():
+    # the long-clip canvas at full width: d = 5120 on the 4 x 64 x 64 grid (16384 tokens ->
+    # 8192 pairs). Pairing adds two bf16 values in fp32 (exact) and halves them (exact), so
+    # the stored mean is the exact mean rounded once to bf16; unpairing likewise rounds
+    # x_pre + (xr_out - xr_in), computed in fp32, once.
+    grid, d = (4, 64, 64), 5120
+    g = torch.Generator(device="cuda")
+    g.manual_seed(71)
+    x = torch.randn(16384, d, generator=g, device="cuda").to(torch.bfloat16)
+    xr, xr2 = h3k.token_pair(x, grid)
+    assert torch.equal(xr, xr2)
+    xn = np64(x)
+    want = O.round_bf16(O.token_pair(xn, grid))
+    got = np64(xr)
+    assert np.mean(got == want) >= 0.9999
+    assert np.allclose(got, want, rtol=2.0 ** -7, atol=0)
+    xo = (xr.float() + 0.1 * torch.randn(xr.shape, generator=g, device="cuda")).to(torch.bfloat16)
+    xp = x.clone()
+    h3k.token_unpair(xp, xo, xr, grid)
+    ref = O.token_unpair(xn, np64(xo), got, grid)
+    out = np64(xp)
+    assert np.mean(out == O.round_bf16(ref)) >= 0.9999
+    assert np.max(np.abs(out - ref) / np.maximum(np.abs(ref), 1e-30)) <= 2.0 ** -7

@@ -71,6 +71,26 @@ def test_round_bf16_vs_torch_and_ties():
     assert O.round_bf16(0.0) == 0.0
 
 
+def test_round_f16_vs_library_and_ties():
+    # normal, subnormal and overflowing magnitudes against numpy's binary16 conversion
+    v = rng.standard_normal(40000) * np.exp(rng.uniform(-26 * math.log(2), 17 * math.log(2), 40000))
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).astype(np.float64)
+    assert np.array_equal(O.round_f16(v), want)
+    ulp = 2.0 ** -10  # fp16 spacing just above 1
+    assert O.round_f16(1 + ulp / 2) == 1.0                  # tie -> even
+    assert O.round_f16(1 + 3 * ulp / 2) == 1 + 2 * ulp      # tie -> even
+    assert O.round_f16(-(1 + ulp / 2 + 1e-12)) == -(1 + ulp)
+    sub = 2.0 ** -24  # smallest subnormal
+    assert O.round_f16(sub / 2) == 0.0                      # tie -> even (0)
+    assert O.round_f16(3 * sub / 2) == 2 * sub              # tie -> even
+    assert O.round_f16(2.0 ** -14 + sub / 2) == 2.0 ** -14  # the normal range starts at 2^-14
+    assert O.round_f16(65504.0) == 65504.0
+    assert O.round_f16(65519.9) == 65504.0
+    assert O.round_f16(65520.0) == np.inf                   # tie -> even: 2^16, out of range
+    assert O.round_f16(-70000.0) == -np.inf and O.round_f16(0.0) == 0.0
+
+
 # ----------------------------------------------------------------------------- int8 GEMM
 def test_int8_matmul_bruteforce():
     a = rng.integers(-127, 128, size=(5, 11)).astype(np.int8)
@@ -225,24 +245,26 @@ def test_normal_tail_fixture_matches_asymptotic_series():
 
 # ----------------------------------------------------------------------------- block (brute force)
 def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_dense=False,
-              round_qkv=False, round_store=False, f32=False):
+              qkv_type=None, store_type=None):
     """Independent scalar-loop implementation of the block on tiny shapes. round_dense:
-    dense projections take bf16-rounded activations; round_qkv: Q, K (after RoPE) and V are
-    rounded to bf16 before attention; round_store: the attention output, the residual after
-    the attention half, the GELU output and the block output are rounded to bf16 where they
-    are produced. Every rounding is torch's RNE conversion; f32: round_qkv and round_store
-    round to fp32 instead (Q without the softmax scale)."""
+    dense projections take bf16-rounded activations; qkv_type ("bf16", "fp16", "fp32"):
+    Q, K (after RoPE) and V are each rounded to that type before attention; store_type
+    ("bf16", "fp32"): the attention output, the residual after the attention half, the GELU
+    output and the block output are rounded to that type where they are produced. The
+    roundings are library conversions (torch's to bf16, numpy's to fp16 and fp32)."""
 
-    def rb(vals):
-        if f32:
-            return [float(np.float32(t)) for t in vals]
+    def rnd(vals, t):
+        if t == "fp32":
+            return [float(np.float32(v)) for v in vals]
+        if t == "fp16":
+            return np.asarray(vals, np.float64).astype(np.float16).astype(np.float64).tolist()
         return torch.tensor(vals, dtype=torch.float64).to(torch.bfloat16).double().tolist()
 
     def rq(vals):
-        return rb(vals) if round_qkv else vals
+        return rnd(vals, qkv_type) if qkv_type else vals
 
     def rs(vals):
-        return rb(vals) if round_store else vals
+        return rnd(vals, store_type) if store_type else vals
     L, d = len(x), len(x[0])
     F = len(w["w_up"])
     # the modulation is stored as fp32 (nearest, ties to even)
@@ -301,15 +323,7 @@ def _bf_block(x, c, w, H, Dh, grid, variant, w_scale=1.0, w_offset=0.0, round_de
         return out
 
     qkv = [lin(ln_mod(x[l], sh1, sc1), "_qkv") for l in range(L)]
-    # Q is rounded as handed to a base-2 softmax: times 1 / (sqrt(Dh) ln 2), then back
-    cq = 1.0 / (math.sqrt(Dh) * math.log(2.0))
-
-    def rqs(vals):
-        if f32:
-            return rq(vals)
-        return [t / cq for t in rb([t * cq for t in vals])] if round_qkv else vals
-
-    Q = [[rqs(rope(qkv[l][e * Dh:(e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
+    Q = [[rq(rope(qkv[l][e * Dh:(e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
     K = [[rq(rope(qkv[l][d + e * Dh:d + (e + 1) * Dh], l)) for e in range(H)] for l in range(L)]
     V = [[rq(qkv[l][2 * d + e * Dh:2 * d + (e + 1) * Dh]) for e in range(H)] for l in range(L)]
     out = []
@@ -381,8 +395,8 @@ def test_block_bruteforce_dense_bf16_inputs(variant):
 
 @pytest.mark.parametrize("variant", ["w8a8", "bf16gemm"])
 @pytest.mark.parametrize("attn_inputs,act_store", [("bf16", "fp64"), ("fp64", "bf16"), ("bf16", "bf16"),
-                                                   ("fp32", "fp32")])
-def test_block_bruteforce_bf16_handoffs(variant, attn_inputs, act_store):
+                                                   ("fp16", "fp64"), ("fp32", "fp32")])
+def test_block_bruteforce_storage_options(variant, attn_inputs, act_store):
     d, H, Dh, F, dc, grid = 12, 2, 6, 24, 5, (2, 2, 2)
     w = _tiny_weights(d, F, dc, 13)
     r = np.random.default_rng(14)
@@ -390,34 +404,22 @@ def test_block_bruteforce_bf16_handoffs(variant, attn_inputs, act_store):
     c = r.standard_normal(dc)
     got = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
                           attn_inputs=attn_inputs, act_store=act_store)
-    f32 = attn_inputs == "fp32"
     ref = _bf_block(x.tolist(), c.tolist(), {k: (v.tolist() if hasattr(v, "tolist") else v) for k, v in w.items()},
-                    H, Dh, grid, variant, round_qkv=attn_inputs != "fp64", round_store=act_store != "fp64",
-                    f32=f32)
+                    H, Dh, grid, variant, qkv_type=None if attn_inputs == "fp64" else attn_inputs,
+                    store_type=None if act_store == "fp64" else act_store)
     assert np.allclose(got, ref, rtol=1e-9, atol=1e-9)
     plain = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant)
     assert not np.allclose(got, plain, rtol=1e-9, atol=1e-9)
     rnd = O.round_f32 if act_store == "fp32" else O.round_bf16
     if act_store != "fp64":
         assert np.array_equal(got, rnd(got))
-    # the stored intermediates are bf16 values and x2 is built from them
+    # the stored intermediates are values of the storage type and x2 is built from them
     x2, parts = O.block_forward(x, c, w, n_heads=H, head_dim=Dh, grid=grid, variant=variant,
                                 attn_inputs=attn_inputs, act_store=act_store, return_parts=True)
     assert np.array_equal(x2, got)
     if act_store != "fp64":
         for name in ("o", "x1", "g"):
             assert np.array_equal(parts[name], rnd(parts[name])), name
-
-
-def test_q_handoff_scale_base2_softmax():
-    # a base-2 softmax of (Q * c) K^T is the softmax of Q K^T / sqrt(Dh)
-    r = np.random.default_rng(21)
-    for dh in (64, 128):
-        q, k = r.standard_normal(dh), r.standard_normal((40, dh))
-        e = np.exp(k @ q / math.sqrt(dh))
-        b = 2.0 ** (k @ (q * O.q_handoff_scale(dh)))
-        assert np.allclose(e / e.sum(), b / b.sum(), rtol=1e-12, atol=0)
-    assert O.q_handoff_scale(128) == pytest.approx(0.12752, abs=1e-5)
 
 
 def test_block_zero_gates_identity():

@@ -61,21 +61,25 @@ def test_quantize_weights_twin():
 
 
 @pytest.mark.parametrize("flags,variant,store", [
-    (0, "w8a8", "bf16"), (R.F_FP32_DEBUG, "w8a8", "fp32"), (R.F_BF16_OUT, "int8_mlp_qkv", "bf16"),
-    (R.F_BF16_QKV | R.F_BF16_OUT, "int8_mlp", "bf16"), (R.F_BF16_GEMM, "bf16gemm", "bf16"),
-    (R.F_BF16_QKV | R.F_BF16_OUT | R.F_BF16_MLP, "bf16gemm", "bf16")])
+    (0, "w8a8", "fp64"), (R.F_ATTN_BF16, "w8a8", "fp64"), (R.F_FP32_DEBUG, "w8a8", "fp32"),
+    (R.F_BF16_OUT, "int8_mlp_qkv", "fp64"), (R.F_BF16_QKV | R.F_BF16_OUT, "int8_mlp", "fp64"),
+    (R.F_BF16_GEMM, "bf16gemm", "fp64"), (R.F_BF16_QKV | R.F_BF16_OUT | R.F_BF16_MLP, "bf16gemm", "fp64")])
 def test_block_twin_maps_flags_to_the_precision_series(flags, variant, store):
+    # the 16-bit paths' twin is the plain definition; the fp32 debug path's stores fp32
     w = _weights(1)
     x, c = _inputs()
-    out = np.zeros((L, D), np.float32)
+    out = np.zeros((L, D), np.float64)
     assert R.h3k_ref_block_forward(x, out, c, w, _dims(), L, flags) == R.OK
     ref = O.block_forward(x, c, _oracle_w(w, variant != "w8a8"), n_heads=H, head_dim=DH, grid=GRID,
                           variant=variant, eps=float(np.float32(O.LN_EPS)), attn_inputs=store,
-                          dense_inputs="bf16" if store == "bf16" else "fp64", act_store=store)
-    assert np.array_equal(out, ref.astype(np.float32))
-    # the output holds values of the storage type
-    rounded = O.round_bf16(out) if store == "bf16" else O.round_f32(out)
-    assert np.array_equal(out, rounded)
+                          act_store=store)
+    assert np.array_equal(out, ref)
+    if store == "fp32":  # the output holds fp32 values
+        assert np.array_equal(out, O.round_f32(out))
+    # an fp32 output array receives the values rounded to fp32 once
+    out32 = np.zeros((L, D), np.float32)
+    assert R.h3k_ref_block_forward(x, out32, c, w, _dims(), L, flags) == R.OK
+    assert np.array_equal(out32, ref.astype(np.float32))
 
 
 def test_block_grid_twin_positions():
@@ -88,20 +92,19 @@ def test_block_grid_twin_positions():
     out = np.zeros((n, D))
     assert R.h3k_ref_block_forward_grid(x, out, c, w, _dims(), *g2, 2.0, 0.5, 0) == R.OK
     ref = O.block_forward(x, c, _oracle_w(w, False), n_heads=H, head_dim=DH, grid=g2, w_scale=2.0,
-                          w_offset=0.5, eps=float(np.float32(O.LN_EPS)), attn_inputs="bf16",
-                          dense_inputs="bf16", act_store="bf16")
+                          w_offset=0.5, eps=float(np.float32(O.LN_EPS)))
     assert np.array_equal(out, ref)
 
 
-@pytest.mark.parametrize("flags", [0, R.F_FP32_DEBUG])
-def test_attention_twin_layouts_bruteforce(flags):
+@pytest.mark.parametrize("dtype", [R.DT_BF16, R.DT_F16, R.DT_F32])
+def test_attention_twin_layouts_bruteforce(dtype):
     # explicit loops over the C ABI's layouts: q, k [H, L, Dh], v [H, Dh, L], o [L, H*Dh];
     # a softmax scale other than 1/sqrt(Dh)
     rng = np.random.default_rng(5)
     h, n, dh, scale = 3, 6, 4, 0.37
     q, k, v = rng.standard_normal((h, n, dh)), rng.standard_normal((h, n, dh)), rng.standard_normal((h, dh, n))
     o = np.zeros((n, h * dh))
-    assert R.h3k_ref_attention(q, k, v, o, h, n, dh, scale, flags) == R.OK
+    assert R.h3k_ref_attention(q, k, v, o, h, n, dh, scale, dtype, 0) == R.OK
     ref = np.zeros((n, h * dh))
     for e in range(h):
         for i in range(n):
@@ -111,12 +114,16 @@ def test_attention_twin_layouts_bruteforce(flags):
             z = sum(p)
             for t in range(dh):
                 ref[i, e * dh + t] = sum(p[j] * v[e, t, j] for j in range(n)) / z
-    store = O.round_f32 if flags else O.round_bf16
-    # rounding of a value within an ulp of a storage boundary may go either way
-    assert np.max(np.abs(o - store(ref)) / np.abs(ref)) <= (2.0 ** -23 if flags else 2.0 ** -7)
-    assert np.allclose(o, ref, rtol=2.0 ** -8, atol=0)
-    assert R.h3k_ref_attention(q, k, v, o, h, n, dh, 0.0, flags) == R.EINVAL
-    assert R.h3k_ref_attention(q, k, v, o, h, n + 1, dh, scale, flags) == R.EINVAL
+    # o holds values of the dtype, each within half a unit in the last place of the loop's
+    # value (a value within rounding error of a boundary may go either way: one ulp)
+    store, ulp = {R.DT_F32: (O.round_f32, 2.0 ** -23), R.DT_F16: (O.round_f16, 2.0 ** -10),
+                  R.DT_BF16: (O.round_bf16, 2.0 ** -7)}[dtype]
+    assert np.array_equal(o, store(o))
+    assert np.max(np.abs(o - store(ref)) / np.abs(ref)) <= ulp
+    assert np.allclose(o, ref, rtol=ulp / 2 * 1.0001, atol=0)
+    assert R.h3k_ref_attention(q, k, v, o, h, n, dh, 0.0, dtype, 0) == R.EINVAL
+    assert R.h3k_ref_attention(q, k, v, o, h, n + 1, dh, scale, dtype, 0) == R.EINVAL
+    assert R.h3k_ref_attention(q, k, v, o, h, n, dh, scale, 9, 0) == R.EINVAL
 
 
 def test_stack_twin_matches_the_oracle_stack():
@@ -126,8 +133,7 @@ def test_stack_twin_matches_the_oracle_stack():
     for tr in [(0, 0), (1, 2), (0, 3)]:
         assert R.h3k_ref_stack_forward(x, out, c, blocks, 3, _dims(), L, *tr, 0) == R.OK
         ref = O.stack_forward(x, c, [_oracle_w(b, False) for b in blocks], n_heads=H, head_dim=DH,
-                              grid=GRID, tr_begin=tr[0], tr_end=tr[1], attn_inputs="bf16",
-                              act_store="bf16")
+                              grid=GRID, tr_begin=tr[0], tr_end=tr[1])
         assert np.array_equal(out, ref), tr
 
 
@@ -142,6 +148,7 @@ def test_return_codes():
     assert ok(x, out, c, w, _dims(ln_eps=0.0), L, 0) == R.EINVAL
     assert ok(x[:-1], out, c, w, _dims(), L, 0) == R.EINVAL               # wrong buffer size
     assert ok(x, out, c, w, _dims(), L, R.F_BF16_MLP) == R.EUNSUPPORTED  # not in the series
+    assert ok(x, out, c, w, _dims(), L, 1 << 12) == R.EINVAL              # unknown flag bit
     st = R.h3k_ref_stack_forward
     blocks = [w, w]
     assert st(x, out, c, blocks, 2, _dims(), L, 2, 1, 0) == R.EINVAL       # tr_begin > tr_end

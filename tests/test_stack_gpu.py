@@ -42,10 +42,11 @@ def test_stack_tiny(tr, flags):
     c = S.conditioning(wl).cuda()
     out = h3k.stack_forward(x, c, blocks, h3k.dims_of(wl), tr[0], tr[1], flags)
     torch.cuda.synchronize()
+    # plain oracle stack on the 16-bit path; the fp32 debug path stores fp32 by definition
+    st = "fp32" if flags else "fp64"
     ref = O.stack_forward(np64(x), np64(c), [oracle_weights(b) for b in blocks],
                           n_heads=wl.n_heads, head_dim=wl.head_dim, grid=wl.grid,
-                          tr_begin=tr[0], tr_end=tr[1], attn_inputs="fp32" if flags else "bf16",
-                          act_store="fp32" if flags else "bf16")
+                          tr_begin=tr[0], tr_end=tr[1], attn_inputs=st, act_store=st)
     err = rel_l2(np64(out), ref)
     print(f"tiny stack tr={tr} flags={flags}: rel-L2 {err:.3e}")
     assert err <= (1e-3 if flags else 2e-2)
@@ -169,7 +170,9 @@ def test_stack50_l16384_token_reduction():
 ])
 def test_denoise_tiny(steps, reuse, core_reuse, layers, tr, flags):
     """The denoising loop against the oracle's sampler around the oracle stack of the first
-    `layers` blocks (bf16 path: y and x stored in bf16 on both sides)."""
+    `layers` blocks. The loop's state x and the stack output y are tensors of the
+    activation type (bf16 on the default path), so the sampler rounds them there; the stack
+    itself is the plain oracle (fp32 storage on the debug path)."""
     wl = dataclasses.replace(S.WORKLOADS["tiny"], n_blocks=2)
     blocks = _blocks(wl, 2)
     xdt = torch.float32 if flags else torch.bfloat16
@@ -182,8 +185,8 @@ def test_denoise_tiny(steps, reuse, core_reuse, layers, tr, flags):
     ow = [oracle_weights(b) for b in blocks[:layers]]
     core = lambda xs: O.stack_forward(xs, np64(c), ow, n_heads=wl.n_heads, head_dim=wl.head_dim,  # noqa: E731
                                       grid=wl.grid, tr_begin=tr[0], tr_end=tr[1],
-                                      attn_inputs="fp32" if flags else "bf16",
-                                      act_store="fp32" if flags else "bf16")
+                                      attn_inputs="fp32" if flags else "fp64",
+                                      act_store="fp32" if flags else "fp64")
     ref = O.denoise(x0, core, steps=steps, reuse=reuse, core_reuse=core_reuse, store_bf16=not flags,
                     store_f32=bool(flags))
     err = rel_l2(np64(got), ref)

@@ -191,12 +191,33 @@ int check_weights(const char *fn, const h3k_block_weights *w, uint32_t flags) {
 
 int check_flags(const char *fn, uint32_t flags) {
   if (flags & ~(uint32_t)(H3K_F_BF16_GEMM | H3K_F_FP32_DEBUG | H3K_F_SYNC | H3K_F_BF16_QKV |
-                          H3K_F_BF16_OUT | H3K_F_BF16_MLP))
+                          H3K_F_BF16_OUT | H3K_F_BF16_MLP | H3K_F_ATTN_BF16))
     return fail(H3K_EINVAL, "%s: unknown flag bits 0x%x", fn, flags);
   if (Prec(flags).any() && (flags & H3K_F_FP32_DEBUG))
     return fail(H3K_EUNSUPPORTED, "%s: bf16 projections with H3K_F_FP32_DEBUG are unsupported", fn);
+  if ((flags & H3K_F_ATTN_BF16) && (flags & H3K_F_FP32_DEBUG))
+    return fail(H3K_EUNSUPPORTED, "%s: H3K_F_ATTN_BF16 with H3K_F_FP32_DEBUG is unsupported", fn);
   return H3K_OK;
 }
+
+// Element types of the attention tensors in a block: fp32 on the debug path; otherwise
+// Q, K, V^T (and P) fp16, or bf16 under H3K_F_ATTN_BF16, and O fp16 when the int8
+// out-projection's quantiser reads it, bf16 when a bf16 projection consumes it or the
+// attention runs on bf16.
+struct AttnTypes {
+  AttnType in, out;
+  explicit AttnTypes(uint32_t f) {
+    if (f & H3K_F_FP32_DEBUG) {
+      in = out = AT_F32;
+    } else if (f & H3K_F_ATTN_BF16) {
+      in = out = AT_BF16;
+    } else {
+      in = AT_F16;
+      out = Prec(f).out ? AT_BF16 : AT_F16;
+    }
+  }
+  int o_row_type() const { return out == AT_F32 ? ROW_F32 : (out == AT_F16 ? ROW_F16 : ROW_BF16); }
+};
 
 // One block on grid (T, Hg, Wg) with w positions w * w_scale + w_offset. Arguments are
 // already validated.
@@ -206,7 +227,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   const int64_t L = (int64_t)T * Hg * Wg;
   const int d = dm->d, F = dm->d_ff, H = dm->n_heads, Dh = dm->head_dim;
   const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
+  const int act = f32 ? ROW_F32 : ROW_BF16;  // x, x1 (and g) element type
   const Prec p(flags);
+  const AttnTypes at_(flags);
   h3k_ws_layout lay;
   plan(dm, L, flags, &lay);
   float *m = at<float>(ws, lay.m);
@@ -228,9 +251,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // LN + modulate (+ quant)
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
-    hipError_t e = p.qkv ? launch_rows(1, x_in, false, shift1, scale1, L, d, dm->ln_eps, nullptr, nullptr,
-                                       at<uint16_t>(ws, lay.h), s)
-                      : launch_rows(0, x_in, f32, shift1, scale1, L, d, dm->ln_eps,
+    hipError_t e = p.qkv ? launch_rows(1, x_in, ROW_BF16, shift1, scale1, L, d, dm->ln_eps, nullptr,
+                                       nullptr, at<uint16_t>(ws, lay.h), s)
+                      : launch_rows(0, x_in, act, shift1, scale1, L, d, dm->ln_eps,
                                     at<int8_t>(ws, lay.qa), at<float>(ws, lay.s_a), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant"))) return rc;
   }
@@ -255,9 +278,11 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.Dh = Dh;
     a.rope = rope;
     a.rg = rg;
-    // bf16 path: Q leaves the epilogue multiplied by log2(e) / sqrt(Dh), so that attention
-    // exponentiates its scores without a scaling step (one rounding of Q either way)
+    // 16-bit path: Q leaves the epilogue multiplied by log2(e) / sqrt(Dh), so that attention
+    // exponentiates its scores without a scaling step (one rounding of Q either way); Q, K
+    // and V^T are stored in the attention's operand type
     if (!f32) a.q_scale = (1.0f / sqrtf((float)Dh)) * 1.4426950408889634f;
+    a.qkv_f16 = at_.in == AT_F16;
     Launch l(H3K_K_GEMM_QKV, s, flags);
     if ((rc = l.done(launch_gemm(EPI_QKV, a, s), fn, "gemm_qkv"))) return rc;
   }
@@ -265,13 +290,14 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   {
     Launch l(H3K_K_ATTENTION, s, flags);
     hipError_t e = launch_attention(at<void>(ws, lay.q), at<void>(ws, lay.k), at<void>(ws, lay.vt),
-                                    at<void>(ws, lay.o), H, L, Dh, 1.0 / sqrt((double)Dh), f32, !f32, s);
+                                    at<void>(ws, lay.o), H, L, Dh, 1.0 / sqrt((double)Dh), at_.in,
+                                    at_.out, !f32, s);
     if ((rc = l.done(e, fn, "attention"))) return rc;
   }
   // quantise O
   if (!p.out) {
     Launch l(H3K_K_ROWQUANT_O, s, flags);
-    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), f32, nullptr, nullptr, L, d, 0.f,
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.o), at_.o_row_type(), nullptr, nullptr, L, d, 0.f,
                                  at<int8_t>(ws, lay.qo), at<float>(ws, lay.s_o), nullptr, s),
                      fn, "rowquant_o")))
       return rc;
@@ -298,9 +324,9 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // LN + modulate (+ quant) of x1
   {
     Launch l(H3K_K_LN_QUANT, s, flags);
-    hipError_t e = p.mlp ? launch_rows(1, x1, f32, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
+    hipError_t e = p.mlp ? launch_rows(1, x1, act, shift2, scale2, L, d, dm->ln_eps, nullptr, nullptr,
                                        at<uint16_t>(ws, lay.h2), s)
-                      : launch_rows(0, x1, f32, shift2, scale2, L, d, dm->ln_eps,
+                      : launch_rows(0, x1, act, shift2, scale2, L, d, dm->ln_eps,
                                     at<int8_t>(ws, lay.qa2), at<float>(ws, lay.s_a2), nullptr, s);
     if ((rc = l.done(e, fn, "ln_modulate_quant_2"))) return rc;
   }
@@ -322,7 +348,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   // quantise g
   if (!p.mlp) {
     Launch l(H3K_K_ROWQUANT_G, s, flags);
-    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), f32, nullptr, nullptr, L, F, 0.f,
+    if ((rc = l.done(launch_rows(2, at<void>(ws, lay.g), act, nullptr, nullptr, L, F, 0.f,
                                  at<int8_t>(ws, lay.qg), at<float>(ws, lay.s_g), nullptr, s),
                      fn, "rowquant_g")))
       return rc;
@@ -365,7 +391,8 @@ int h3k_quantize_weights(const void *w, int w_dtype, int64_t n_out, int64_t k_in
   if (k_in % 8) return fail(H3K_EUNSUPPORTED, "%s: k_in must be a multiple of 8", fn);
   if (k_in > 32768) return fail(H3K_EUNSUPPORTED, "%s: k_in > 32768 unsupported", fn);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_rows(2, w, w_dtype == H3K_DT_F32, nullptr, nullptr, n_out, (int)k_in, 0.f,
+  hipError_t e = launch_rows(2, w, w_dtype == H3K_DT_F32 ? ROW_F32 : ROW_BF16, nullptr, nullptr,
+                             n_out, (int)k_in, 0.f,
                              q_out, scale_out, nullptr, s);
   if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return H3K_OK;
@@ -440,14 +467,19 @@ int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
 }
 
 int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
-                  int64_t L, int32_t head_dim, double softmax_scale, uint32_t flags,
+                  int64_t L, int32_t head_dim, double softmax_scale, int dtype, uint32_t flags,
                   void *stream) {
   const char *fn = "h3k_attention";
   H3K_CHECK_PTR(q);
   H3K_CHECK_PTR(k);
   H3K_CHECK_PTR(v);
   H3K_CHECK_PTR(o);
-  if (flags & ~(uint32_t)(H3K_F_FP32_DEBUG | H3K_F_SYNC)) return fail(H3K_EINVAL, "%s: bad flags", fn);
+  if (flags & ~(uint32_t)(H3K_F_SYNC | H3K_F_Q_BASE2)) return fail(H3K_EINVAL, "%s: bad flags", fn);
+  if (dtype != H3K_DT_F32 && dtype != H3K_DT_BF16 && dtype != H3K_DT_F16)
+    return fail(H3K_EINVAL, "%s: bad dtype %d", fn, dtype);
+  const bool base2 = (flags & H3K_F_Q_BASE2) != 0;
+  if (base2 && dtype == H3K_DT_F32)
+    return fail(H3K_EINVAL, "%s: H3K_F_Q_BASE2 needs a 16-bit dtype", fn);
   if (n_heads <= 0 || L <= 0) return fail(H3K_EINVAL, "%s: n_heads and L must be positive", fn);
   if (head_dim != 64 && head_dim != 128) return fail(H3K_EUNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
   if (L % 8) return fail(H3K_EUNSUPPORTED, "%s: L must be a multiple of 8", fn);
@@ -455,8 +487,8 @@ int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t 
   if (!(softmax_scale > 0.0)) return fail(H3K_EINVAL, "%s: softmax_scale must be positive", fn);
   hipStream_t s = (hipStream_t)stream;
   Launch l(H3K_K_ATTENTION, s, flags);
-  const bool f32 = (flags & H3K_F_FP32_DEBUG) != 0;
-  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, f32, false, s),
+  const AttnType t = dtype == H3K_DT_F32 ? AT_F32 : (dtype == H3K_DT_F16 ? AT_F16 : AT_BF16);
+  return l.done(launch_attention(q, k, v, o, n_heads, L, head_dim, softmax_scale, t, t, base2, s),
                 fn, "attention");
 }
 
@@ -678,7 +710,8 @@ int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift, const 
   if (rows <= 0 || cols <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
   if (cols % 256 || cols > 8192) return fail(H3K_EUNSUPPORTED, "%s: cols must be a multiple of 256, <= 8192", fn);
   if (!(eps > 0.f)) return fail(H3K_EINVAL, "%s: eps must be positive", fn);
-  hipError_t e = launch_rows(0, x, x_dtype == H3K_DT_F32, shift, scale, rows, cols, eps, q_out, s_out,
+  hipError_t e = launch_rows(0, x, x_dtype == H3K_DT_F32 ? ROW_F32 : ROW_BF16, shift, scale, rows,
+                             cols, eps, q_out, s_out,
                              nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return H3K_OK;
@@ -690,10 +723,12 @@ int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols, int
   H3K_CHECK_PTR(x);
   H3K_CHECK_PTR(q_out);
   H3K_CHECK_PTR(s_out);
-  if (x_dtype != H3K_DT_F32 && x_dtype != H3K_DT_BF16) return fail(H3K_EINVAL, "%s: bad x_dtype", fn);
+  if (x_dtype != H3K_DT_F32 && x_dtype != H3K_DT_BF16 && x_dtype != H3K_DT_F16)
+    return fail(H3K_EINVAL, "%s: bad x_dtype", fn);
   if (rows <= 0 || cols <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
   if (cols % 8 || cols > 32768) return fail(H3K_EUNSUPPORTED, "%s: cols must be a multiple of 8, <= 32768", fn);
-  hipError_t e = launch_rows(2, x, x_dtype == H3K_DT_F32, nullptr, nullptr, rows, cols, 0.f, q_out, s_out,
+  const int rt = x_dtype == H3K_DT_F32 ? ROW_F32 : (x_dtype == H3K_DT_F16 ? ROW_F16 : ROW_BF16);
+  hipError_t e = launch_rows(2, x, rt, nullptr, nullptr, rows, cols, 0.f, q_out, s_out,
                              nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return H3K_OK;

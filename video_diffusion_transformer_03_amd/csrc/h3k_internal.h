@@ -38,6 +38,65 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// fp16 (IEEE binary16) counterparts: two fp32 -> packed fp16 pair (v_cvt_pk_f16_f32) and
+// one fp32 -> fp16, round to nearest even; magnitudes above 65504 become infinite
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  v2h h = __builtin_convertvector((v2f){a, b}, v2h);
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+// the low / high half of a packed pair widened to fp32 (exact)
+__device__ __forceinline__ float h2f_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float h2f_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+// 16-bit matrix-core operands: bf16, or fp16 when F16. Both element types use the same
+// 8-element (16-byte) fragments, so kernels carry them as v8bf bit patterns.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  if constexpr (F16)
+    return pack_h2(a, b);
+  else
+    return pack_bf2(a, b);
+}
+template <bool F16>
+__device__ __forceinline__ v4f mma16(v8bf a, v8bf b, v4f c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
+                                                  __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// a fragment of eight 1.0 values in the operand type
+template <bool F16>
+__device__ __forceinline__ v8bf ones16() {
+  if constexpr (F16) {
+    const _Float16 one = (_Float16)1.0f;
+    return __builtin_bit_cast(v8bf, v8h{one, one, one, one, one, one, one, one});
+  } else {
+    const __bf16 one = (__bf16)1.0f;
+    return v8bf{one, one, one, one, one, one, one, one};
+  }
+}
+// acc + the two halves of a packed pair (v_dot2 against (1, 1): exact products, fp32 sum)
+template <bool F16>
+__device__ __forceinline__ float add_pair16(uint32_t u, float acc) {
+  if constexpr (F16) {
+    const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, u), ones, acc, false);
+  } else {
+    const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u), ones, acc, false);
+  }
+}
+
 // max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the 16-lane rows of the wave) with
 // gfx950 row swaps in registers; a shuffle (__shfl_xor) would go through LDS
 // (ds_bpermute) and wait for every outstanding LDS read.
@@ -99,8 +158,10 @@ size_t rope_table_entries(const RopeGeom &g);
 hipError_t launch_rope_table(void *tbl, const RopeGeom &g, float theta, bool f64, hipStream_t s);
 hipError_t launch_adaln(const uint16_t *w, const float *c, float *m, int64_t n_out, int dc,
                         bool f64, hipStream_t s);
-// mode: 0 = LN + modulate + int8 quant, 1 = LN + modulate -> bf16, 2 = int8 quant only
-hipError_t launch_rows(int mode, const void *x, bool x_f32, const float *shift,
+// mode: 0 = LN + modulate + int8 quant, 1 = LN + modulate -> bf16, 2 = int8 quant only.
+// x_type: ROW_BF16, ROW_F32, or ROW_F16 (mode 2 only)
+enum RowType { ROW_BF16 = 0, ROW_F32 = 1, ROW_F16 = 2 };
+hipError_t launch_rows(int mode, const void *x, int x_type, const float *shift,
                        const float *scale, int64_t rows, int cols, float eps, int8_t *q,
                        float *sc, uint16_t *hout, hipStream_t s);
 hipError_t launch_token_pair(const void *x, void *xr, void *xr2, bool f32, int T, int Hg,
@@ -134,6 +195,7 @@ struct GemmArgs {
   const void *rope;    // (cos, sin) table: float2, or double2 with fp32 outputs
   RopeGeom rg;
   float q_scale = 1.0f;  // EPI_QKV: factor applied to Q after RoPE, before it is rounded
+  bool qkv_f16 = false;  // EPI_QKV, 16-bit outputs: Q, K, V^T stored as fp16 (else bf16)
   // EPI_GELU: out [M, N]; EPI_RESID: out[m,n] = res[m,n] + gate[n] * y
   void *out;
   const void *res;
@@ -156,12 +218,15 @@ inline hipError_t ensure_dynamic_lds(const void *kern, int bytes, std::atomic<ui
   return hipSuccess;
 }
 
-// attention: q, k [H, L, Dh], vt [H, Dh, L], o [L, H*Dh]. f32: fp32 inputs and output,
-// fp64 arithmetic (plain FMA kernel); otherwise bf16 inputs and output on the matrix cores.
-// q_prescaled (bf16 only): q already carries scale * log2(e), the factor of the base-2
+// element types of the attention tensors
+enum AttnType { AT_BF16 = 0, AT_F16 = 1, AT_F32 = 2 };
+// attention: q, k [H, L, Dh], vt [H, Dh, L] of type `in`, o [L, H*Dh] of type `out`.
+// AT_F32 (in and out): fp64 arithmetic in a plain FMA kernel. AT_BF16 / AT_F16: 16-bit
+// operands on the matrix cores (fp32 accumulation and softmax), o in bf16 or fp16.
+// q_prescaled (16-bit only): q already carries scale * log2(e), the factor of the base-2
 // softmax.
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, double scale, bool f32, bool q_prescaled,
-                            hipStream_t s);
+                            int64_t L, int Dh, double scale, AttnType in, AttnType out,
+                            bool q_prescaled, hipStream_t s);
 
 }  // namespace h3k

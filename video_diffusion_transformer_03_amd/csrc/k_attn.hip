@@ -7,14 +7,20 @@
 // head-major attention inputs). Layouts: Q, K [H, L, Dh]; V transposed [H, Dh, L];
 // O [L, H*Dh] (token-major, head e in columns e*Dh .. e*Dh + Dh - 1).
 //
-// bf16 kernel: both products run on v_mfma_f32_16x16x32_bf16 in transposed form so that a
-// lane always owns one query column:
+// 16-bit kernels: Q, K, V and P are fp16 (v_mfma_f32_16x16x32_f16) or bf16
+// (v_mfma_f32_16x16x32_bf16); the two instructions have the same shape and rate. The
+// block's default is fp16: 11 significant bits instead of 8 for the same bytes. Its
+// scores are large (a standard deviation near 10 on the synthetic workloads), so the
+// softmax is close to an argmax, and bf16 rounding of Q, K and V moves O by about 6e-3;
+// the quantiser of O and those after it turn that into code flips. Both products run in
+// transposed form so that a lane always owns one query column:
 //   S^T = K Q^T   (A = K rows from LDS, B = Q held in registers)
 //   O^T = V^T P^T (A = V^T rows from LDS, B = P^T taken straight from the S^T registers)
 // The 8 key slots of the P^T operand are the lane's own S^T values, and V^T is read
 // with the same key order, so no cross-lane data movement is needed between the two
 // products; the softmax statistics live in the same lane as the output columns they
-// scale. P is rounded to bf16 for the second product; max, exp and sums are fp32.
+// scale. P is rounded to the operand type for the second product (at most 2^8 with the
+// lazy maximum below, inside the fp16 range); max, exp and sums are fp32.
 #include "h3k_internal.h"
 
 namespace h3k {
@@ -76,7 +82,7 @@ struct AttnState {
 };
 
 // one K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-template <int DH, bool MASK>
+template <bool F16, int DH, bool MASK>
 __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH / 32],
                                           const uint16_t *cK, const uint16_t *cV, int lane,
                                           int64_t k0, int64_t L, float sl2) {
@@ -91,8 +97,8 @@ __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH 
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       v8bf kf = __builtin_bit_cast(v8bf, ld16(cK + (t4 * 16 + c16) * KP + kk * 32 + g * 8));
-      s[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], s[t4][0], 0, 0, 0);
-      s[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], s[t4][1], 0, 0, 0);
+      s[t4][0] = mma16<F16>(kf, qf[0][kk], s[t4][0]);
+      s[t4][1] = mma16<F16>(kf, qf[1][kk], s[t4][1]);
     }
   }
   // lane holds S^T for query c16 and keys k0 + (t4/2)*32 + kperm(t4&1, 4g + r)
@@ -134,38 +140,38 @@ __device__ __forceinline__ void attn_tile(AttnState &st, const v8bf (&qf)[2][DH 
         s[t4][qt][r] = __builtin_amdgcn_exp2f(fmaf(s[t4][qt][r], sl2, mneg));
   }
   // O^T += V^T P^T over two 32-key steps; slots of lane group g = keys 8g .. 8g+7. The
-  // row sum l accumulates the same bf16-rounded P the matrix cores consume (one dot2 per
-  // packed pair against (1, 1)), so O = sum(p v) / sum(p) is normalised consistently.
-  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // row sum l accumulates the same rounded P the matrix cores consume (one dot2 per packed
+  // pair against (1, 1)), so O = sum(p v) / sum(p) is normalised consistently.
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     v8bf pb[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       uint4 u;
-      u.x = pack_bf2(s[2 * ks][qt][0], s[2 * ks][qt][1]);
-      u.y = pack_bf2(s[2 * ks][qt][2], s[2 * ks][qt][3]);
-      u.z = pack_bf2(s[2 * ks + 1][qt][0], s[2 * ks + 1][qt][1]);
-      u.w = pack_bf2(s[2 * ks + 1][qt][2], s[2 * ks + 1][qt][3]);
+      u.x = pack16<F16>(s[2 * ks][qt][0], s[2 * ks][qt][1]);
+      u.y = pack16<F16>(s[2 * ks][qt][2], s[2 * ks][qt][3]);
+      u.z = pack16<F16>(s[2 * ks + 1][qt][0], s[2 * ks + 1][qt][1]);
+      u.w = pack16<F16>(s[2 * ks + 1][qt][2], s[2 * ks + 1][qt][3]);
       float l = st.l[qt];
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.x), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.y), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.z), ones, l, false);
-      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, u.w), ones, l, false);
+      l = add_pair16<F16>(u.x, l);
+      l = add_pair16<F16>(u.y, l);
+      l = add_pair16<F16>(u.z, l);
+      l = add_pair16<F16>(u.w, l);
       st.l[qt] = l;
       pb[qt] = __builtin_bit_cast(v8bf, u);
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       v8bf vf = __builtin_bit_cast(v8bf, ld16(cV + (dt * 16 + c16) * VP + ks * 32 + g * 8));
-      st.o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0], st.o[dt][0], 0, 0, 0);
-      st.o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1], st.o[dt][1], 0, 0, 0);
+      st.o[dt][0] = mma16<F16>(vf, pb[0], st.o[dt][0]);
+      st.o[dt][1] = mma16<F16>(vf, pb[1], st.o[dt][1]);
     }
   }
 }
 
-template <int DH>
-__global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
+// F16: fp16 operands (else bf16); OF16: O stored as fp16 (else bf16)
+template <bool F16, bool OF16, int DH>
+__global__ __launch_bounds__(256, kAttnOcc) void attn_h_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ Vt, void *__restrict__ Ov, int H, int64_t L, float sl2) {
   using C = AttnCfg<DH>;
@@ -239,19 +245,19 @@ __global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
   for (int kt = 0; kt + 1 < nkt; ++kt) {
     const int cur = kt & 1;
     H3K_ATTN_GLOAD(kt + 1);
-    attn_tile<DH, false>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
-                         (int64_t)kt * BK, L, sl2);
+    attn_tile<F16, DH, false>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
+                              (int64_t)kt * BK, L, sl2);
     H3K_ATTN_LSTORE(cur ^ 1);
     __syncthreads();
   }
   {
     const int cur = (nkt - 1) & 1;
     if (tail)
-      attn_tile<DH, true>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
-                          (int64_t)(nkt - 1) * BK, L, sl2);
+      attn_tile<F16, DH, true>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
+                               (int64_t)(nkt - 1) * BK, L, sl2);
     else
-      attn_tile<DH, false>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
-                           (int64_t)(nkt - 1) * BK, L, sl2);
+      attn_tile<F16, DH, false>(st, qf, sK + cur * C::K_ELEMS, sV + cur * C::V_ELEMS, lane,
+                                (int64_t)(nkt - 1) * BK, L, sl2);
   }
 #undef H3K_ATTN_GLOAD
 #undef H3K_ATTN_LSTORE
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(256, kAttnOcc) void attn_bf16_kernel(
       for (int dt = 0; dt < NDT; ++dt) {
         v4f v = st.o[dt][qt];
         *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
-            make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
+            make_uint2(pack16<OF16>(v[0] * inv, v[1] * inv), pack16<OF16>(v[2] * inv, v[3] * inv));
       }
     }
   }
@@ -309,6 +315,7 @@ __device__ __forceinline__ int kof(int R) {  // key (within the tile) held by K 
 }
 
 // S^T = K Q^T for one K tile: lane holds keys (t4/2)*32 + 8g + 4(t4%2) + r, query c16
+template <bool F16>
 __device__ __forceinline__ void s_tile(v4f (&s)[4][2], const v8bf (&qf)[2][4],
                                        const uint8_t *kb, int koff) {
 #pragma unroll
@@ -318,15 +325,15 @@ __device__ __forceinline__ void s_tile(v4f (&s)[4][2], const v8bf (&qf)[2][4],
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const v8bf kf = *(const v8bf *)(kb + t4 * 4096 + (koff ^ (kk * 64)));
-      s[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][kk], s[t4][0], 0, 0, 0);
-      s[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][kk], s[t4][1], 0, 0, 0);
+      s[t4][0] = mma16<F16>(kf, qf[0][kk], s[t4][0]);
+      s[t4][1] = mma16<F16>(kf, qf[1][kk], s[t4][1]);
     }
   }
 }
 
-// P = exp2(S sl2 - m) rounded to bf16 (the P^T operand, keys 8g .. 8g+7 of each 32-key
-// step). QPRE: S already holds the exponent (scaled scores minus m), P = exp2(S).
-template <bool QPRE>
+// P = exp2(S sl2 - m) rounded to the operand type (the P^T operand, keys 8g .. 8g+7 of
+// each 32-key step). QPRE: S already holds the exponent (scaled scores minus m), P = exp2(S).
+template <bool F16, bool QPRE>
 __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
                                          const float (&m)[2], float sl2) {
 #pragma unroll
@@ -346,10 +353,10 @@ __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
         }
       }
       uint4 u;
-      u.x = pack_bf2(p[0], p[1]);
-      u.y = pack_bf2(p[2], p[3]);
-      u.z = pack_bf2(p[4], p[5]);
-      u.w = pack_bf2(p[6], p[7]);
+      u.x = pack16<F16>(p[0], p[1]);
+      u.y = pack16<F16>(p[2], p[3]);
+      u.z = pack16<F16>(p[4], p[5]);
+      u.w = pack16<F16>(p[6], p[7]);
       pb[ks][qt] = __builtin_bit_cast(v8bf, u);
     }
   }
@@ -358,24 +365,21 @@ __device__ __forceinline__ void exp_tile(const v4f (&s)[4][2], v8bf (&pb)[2][2],
 // Accumulator block NO = 8 of O^T holds the row sum: its V^T operand is all ones, so every
 // row of the block is the sum over keys of the rounded P the other blocks consume
 constexpr int NO = 9;
-__device__ __forceinline__ v8bf ones_frag() {
-  const __bf16 one = (__bf16)1.0f;
-  return v8bf{one, one, one, one, one, one, one, one};
-}
 
 // O^T += V^T P^T for one V^T tile (and the row-sum block)
+template <bool F16>
 __device__ __forceinline__ void pv_tile(v4f (&o)[NO][2], const v8bf (&pb)[2][2],
                                         const uint8_t *vb, int voff) {
-  const v8bf ones = ones_frag();
+  const v8bf ones = ones16<F16>();
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
-    o[8][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][0], o[8][0], 0, 0, 0);
-    o[8][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][1], o[8][1], 0, 0, 0);
+    o[8][0] = mma16<F16>(ones, pb[ks][0], o[8][0]);
+    o[8][1] = mma16<F16>(ones, pb[ks][1], o[8][1]);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const v8bf vf = *(const v8bf *)(vb + dt * 2048 + (voff ^ (ks * 64)));
-      o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ks][0], o[dt][0], 0, 0, 0);
-      o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[ks][1], o[dt][1], 0, 0, 0);
+      o[dt][0] = mma16<F16>(vf, pb[ks][0], o[dt][0]);
+      o[dt][1] = mma16<F16>(vf, pb[ks][1], o[dt][1]);
     }
   }
 }
@@ -465,9 +469,9 @@ __device__ __forceinline__ void shift_tile(v4f (&s)[4][2], const float (&shift)[
 constexpr int PD = 3;  // LDS fragment reads issued this many MFMA pairs ahead
 
 // One slice of the softmax of a score tile: the pair of scores PART of query tile QT in
-// 32-key step KS -> two exp2 and one bf16 pair packed into u[PART] (pb[KS][QT] once the four
-// parts are done). The row sum comes from the matrix cores (accumulator block 8).
-template <bool QPRE, int QT, int KS, int PART>
+// 32-key step KS -> two exp2 and one 16-bit pair packed into u[PART] (pb[KS][QT] once the
+// four parts are done). The row sum comes from the matrix cores (accumulator block 8).
+template <bool F16, bool QPRE, int QT, int KS, int PART>
 __device__ __forceinline__ void softmax_slice(const v4f (&cur)[4][2], uint32_t (&u)[4],
                                               v8bf (&pb)[2][2], const float (&mneg)[2],
                                               float sl2) {
@@ -476,7 +480,7 @@ __device__ __forceinline__ void softmax_slice(const v4f (&cur)[4][2], uint32_t (
                         : __builtin_amdgcn_exp2f(fmaf(cur[tt][QT][r0], sl2, mneg[QT]));
   const float p1 = QPRE ? __builtin_amdgcn_exp2f(cur[tt][QT][r0 + 1])
                         : __builtin_amdgcn_exp2f(fmaf(cur[tt][QT][r0 + 1], sl2, mneg[QT]));
-  u[PART] = pack_bf2(p0, p1);
+  u[PART] = pack16<F16>(p0, p1);
   if constexpr (PART == 3) pb[KS][QT] = __builtin_bit_cast(v8bf, make_uint4(u[0], u[1], u[2], u[3]));
 }
 
@@ -493,7 +497,7 @@ __device__ __forceinline__ void softmax_slice(const v4f (&cur)[4][2], uint32_t (
 // the waves' issue.
 // QPRE: Q carries the base-2 softmax scale, each S tile starts from cq = -m (the MFMA's C
 // operand), so it comes out as the exponents themselves and exp2 reads it directly.
-template <bool QPRE, typename CopyF>
+template <bool F16, bool QPRE, typename CopyF>
 __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4][2],
                                             v8bf (&pb)[2][2], const v8bf (&qf)[2][4],
                                             const uint8_t *kb, int koff, const float (&m)[2],
@@ -513,13 +517,13 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
     constexpr int t4 = i % 4, kk = i / 4;
     const v8bf k = kf[i % (PD + 1)];
     const v4f z = {0.f, 0.f, 0.f, 0.f};
-    nxt[t4][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[0][kk],
-                                                         kk ? nxt[t4][0] : (QPRE ? cq[0] : z), 0, 0, 0);
-    nxt[t4][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qf[1][kk],
-                                                         kk ? nxt[t4][1] : (QPRE ? cq[1] : z), 0, 0, 0);
+    nxt[t4][0] = mma16<F16>(k, qf[0][kk],
+                                                         kk ? nxt[t4][0] : (QPRE ? cq[0] : z));
+    nxt[t4][1] = mma16<F16>(k, qf[1][kk],
+                                                         kk ? nxt[t4][1] : (QPRE ? cq[1] : z));
     if constexpr (i % 2 == 1) {
       constexpr int sl = i / 2;
-      softmax_slice<QPRE, sl / 4, 0, sl % 4>(cur, u, pb, mneg, sl2);
+      softmax_slice<F16, QPRE, sl / 4, 0, sl % 4>(cur, u, pb, mneg, sl2);
     }
     __builtin_amdgcn_sched_barrier(0);
   });
@@ -530,12 +534,12 @@ __device__ __forceinline__ void phase_s_exp(v4f (&nxt)[4][2], const v4f (&cur)[4
 // row maximum of nxt (query tile i / 8, two scores per step). Steps
 // 0 .. 7 also do the softmax slices of cur's last 32 keys (pb[1]), which the MFMAs of steps
 // 8 .. 15 consume.
-template <bool QPRE>
+template <bool F16, bool QPRE>
 __device__ __forceinline__ bool phase_pv_max(v4f (&o)[NO][2], v8bf (&pb)[2][2],
                                              const v4f (&nxt)[4][2], const v4f (&cur)[4][2],
                                              const uint8_t *vb, int voff, const float (&m)[2],
                                              float (&mnew)[2], float sl2) {
-  const v8bf ones = ones_frag();
+  const v8bf ones = ones16<F16>();
   v8bf vf[PD + 1];
   static_for<PD>([&](auto I) {
     vf[I] = *(const v8bf *)(vb + (I % 8) * 2048 + (voff ^ ((I / 8) * 64)));
@@ -551,12 +555,12 @@ __device__ __forceinline__ bool phase_pv_max(v4f (&o)[NO][2], v8bf (&pb)[2][2],
           *(const v8bf *)(vb + ((i + PD) % 8) * 2048 + (voff ^ (((i + PD) / 8) * 64)));
     constexpr int dt = i % 8, ks = i / 8;
     const v8bf v = vf[i % (PD + 1)];
-    o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][0], o[dt][0], 0, 0, 0);
-    o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pb[ks][1], o[dt][1], 0, 0, 0);
-    if constexpr (i < 8) softmax_slice<QPRE, i / 4, 1, i % 4>(cur, u, pb, mneg, sl2);
+    o[dt][0] = mma16<F16>(v, pb[ks][0], o[dt][0]);
+    o[dt][1] = mma16<F16>(v, pb[ks][1], o[dt][1]);
+    if constexpr (i < 8) softmax_slice<F16, QPRE, i / 4, 1, i % 4>(cur, u, pb, mneg, sl2);
     if constexpr (dt == 7) {  // row sums of this key step's P
-      o[8][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][0], o[8][0], 0, 0, 0);
-      o[8][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[ks][1], o[8][1], 0, 0, 0);
+      o[8][0] = mma16<F16>(ones, pb[ks][0], o[8][0]);
+      o[8][1] = mma16<F16>(ones, pb[ks][1], o[8][1]);
     }
     constexpr int qt = i / 8, st = i % 8;  // scores 2 st, 2 st + 1 of query tile qt
     const float a0 = nxt[st >> 1][qt][(st & 1) * 2], a1 = nxt[st >> 1][qt][(st & 1) * 2 + 1];
@@ -597,8 +601,9 @@ __device__ __forceinline__ void rescale(v4f (&o)[NO][2], const float (&alpha)[2]
 }
 }  // namespace v2
 
-// QPRE: Q arrives multiplied by log2(e) / sqrt(Dh) (sl2 is then unused)
-template <bool QPRE>
+// F16: fp16 operands (else bf16); OF16: O stored as fp16 (else bf16); QPRE: Q arrives
+// multiplied by log2(e) / sqrt(Dh) (sl2 is then unused)
+template <bool F16, bool OF16, bool QPRE>
 __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict__ Q,
                                                       const uint16_t *__restrict__ K,
                                                       const uint16_t *__restrict__ Vt,
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   static_for<DIST>([&](auto J) { H3K_V2_COPY(J); });
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 1)));
   H3K_PP_SYNC();
-  s_tile(sa, qf, smem, koff);
+  s_tile<F16>(sa, qf, smem, koff);
   float mnew[2];
   bool pend = max_vals<true, QPRE>(sa, m, mnew, sl2, g, (int)min((int64_t)BK, L));
   if constexpr (QPRE) {
@@ -746,11 +751,11 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
           cq[qt] = v4f{-m[qt], -m[qt], -m[qt], -m[qt]};                                        \
       }                                                                                        \
     }                                                                                          \
-    phase_s_exp<QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, sl2, [&](int pc) {                   \
+    phase_s_exp<F16, QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, sl2, [&](int pc) {                   \
       if (jj + DIST <= nkt) copy_piece(jj + DIST, pc);                                         \
     });                                                                                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
-    const bool grow_ = phase_pv_max<QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, sl2);           \
+    const bool grow_ = phase_pv_max<F16, QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, sl2);           \
     pend = rescale_decision<QPRE, true>(grow_, mnew, m, alpha, shift, sl2);                    \
     if (jj + DIST <= nkt)                                                                      \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
@@ -765,8 +770,8 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
       rescale(o, alpha);                                                                       \
       if constexpr (QPRE) shift_tile(CUR, shift);                                              \
     }                                                                                          \
-    exp_tile<QPRE>(CUR, pb, m, sl2);                                                           \
-    pv_tile(o, pb, sb_, voff);                                                                 \
+    exp_tile<F16, QPRE>(CUR, pb, m, sl2);                                                      \
+    pv_tile<F16>(o, pb, sb_, voff);                                                                 \
   }
   // nkt - 1 iterations in pairs (the score tiles swap roles); only the last iteration, whose
   // S tile is the last key tile, can need the key mask. An odd count runs one iteration
@@ -804,7 +809,7 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
       for (int dt = 0; dt < 8; ++dt) {
         const v4f v = o[dt][qt];
         *(uint2 *)((uint16_t *)Ov + obase + dt * 16) =
-            make_uint2(pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv));
+            make_uint2(pack16<OF16>(v[0] * inv, v[1] * inv), pack16<OF16>(v[2] * inv, v[3] * inv));
       }
     }
   }
@@ -881,10 +886,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
   }
 }
 
-template <bool QPRE>
+template <bool F16, bool OF16, bool QPRE>
 static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o, int H,
                           int64_t L, float sl2, hipStream_t s) {
-  auto kern = attn_v2_kernel<QPRE>;
+  auto kern = attn_v2_kernel<F16, OF16, QPRE>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)v2::LDS, lds_set);
       e != hipSuccess)
@@ -897,11 +902,11 @@ static hipError_t attn_v2(const void *q, const void *k, const void *vt, void *o,
   return hipGetLastError();
 }
 
-template <int DH>
-static hipError_t attn_bf16(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, float sl2, hipStream_t s) {
+template <bool F16, bool OF16, int DH>
+static hipError_t attn_h(const void *q, const void *k, const void *vt, void *o, int H,
+                         int64_t L, float sl2, hipStream_t s) {
   using C = AttnCfg<DH>;
-  auto kern = attn_bf16_kernel<DH>;
+  auto kern = attn_h_kernel<F16, OF16, DH>;
   static std::atomic<uint64_t> lds_set{0};
   if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)C::LDS, lds_set);
       e != hipSuccess)
@@ -922,19 +927,34 @@ static hipError_t attn_f32(const void *q, const void *k, const void *vt, void *o
 }
 
 hipError_t launch_attention(const void *q, const void *k, const void *vt, void *o, int H,
-                            int64_t L, int Dh, double scale, bool f32, bool q_prescaled,
-                            hipStream_t s) {
+                            int64_t L, int Dh, double scale, AttnType in, AttnType out,
+                            bool q_prescaled, hipStream_t s) {
   const double sl2d = scale * 1.44269504088896340736;  // exp(x) = exp2(x * log2(e))
   const float sl2 = (float)sl2d;
   if (Dh != 64 && Dh != 128) return hipErrorInvalidValue;
-  if (f32) {
-    if (q_prescaled) return hipErrorInvalidValue;
+  if (in == AT_F32 || out == AT_F32) {
+    if (in != out || q_prescaled) return hipErrorInvalidValue;
     return Dh == 128 ? attn_f32<128>(q, k, vt, o, H, L, sl2d, s)
                      : attn_f32<64>(q, k, vt, o, H, L, sl2d, s);
   }
-  if (Dh == 64) return attn_bf16<64>(q, k, vt, o, H, L, q_prescaled ? 1.0f : sl2, s);
-  return q_prescaled ? attn_v2<true>(q, k, vt, o, H, L, sl2, s)
-                     : attn_v2<false>(q, k, vt, o, H, L, sl2, s);
+  // operand / output type pairs: fp16 -> fp16, fp16 -> bf16 (O feeding a bf16 projection),
+  // bf16 -> bf16
+  const bool f16 = in == AT_F16, of16 = out == AT_F16;
+  if (!f16 && of16) return hipErrorInvalidValue;
+  if (Dh == 64) {
+    const float sl = q_prescaled ? 1.0f : sl2;
+    if (f16) return of16 ? attn_h<true, true, 64>(q, k, vt, o, H, L, sl, s)
+                         : attn_h<true, false, 64>(q, k, vt, o, H, L, sl, s);
+    return attn_h<false, false, 64>(q, k, vt, o, H, L, sl, s);
+  }
+  if (q_prescaled) {
+    if (f16) return of16 ? attn_v2<true, true, true>(q, k, vt, o, H, L, sl2, s)
+                         : attn_v2<true, false, true>(q, k, vt, o, H, L, sl2, s);
+    return attn_v2<false, false, true>(q, k, vt, o, H, L, sl2, s);
+  }
+  if (f16 != of16) return hipErrorInvalidValue;
+  return f16 ? attn_v2<true, true, false>(q, k, vt, o, H, L, sl2, s)
+             : attn_v2<false, false, false>(q, k, vt, o, H, L, sl2, s);
 }
 
 }  // namespace h3k

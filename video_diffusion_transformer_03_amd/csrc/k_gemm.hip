@@ -16,7 +16,8 @@
 // head-major Q/K scatter stores 4 consecutive head dims per lane. Epilogues:
 //   RAW_I32  int32 accumulators (exactness check of the main loop)
 //   QKV      dequant, 3D RoPE on Q and K, scatter to head-major Q, K [H, L, Dh] and
-//            transposed V [H, Dh, L] (the layout attention consumes)
+//            transposed V [H, Dh, L] (the layout attention consumes), in fp16 (the
+//            attention's operand type; bf16 when attention runs on bf16 operands)
 //   GELU     dequant + exact erf GELU (MLP up)
 //   RESID    dequant + gated residual out = res + gate[n] * y (out-proj, MLP down)
 #include "h3k_internal.h"
@@ -149,7 +150,7 @@ constexpr int kStageBytes = 64 * kStagePitch;
 // with m = token m_base + 16 j + (lane & 15) and n = channel n_base + 16 i + 4 (lane >> 4) + r.
 // Loads use token rows clamped to M - 1; only the stores test m < M.
 //
-// bf16 outputs go through `stage`, 8 KB of LDS private to the wave, 64 channels (four
+// 16-bit outputs go through `stage`, 8 KB of LDS private to the wave, 64 channels (four
 // column blocks) at a time: the values are written there in the output's row order and read
 // back 16 bytes per lane, so that every store instruction writes whole 128-byte lines (a
 // token's 64 channels of Q, K or a row-major output; 64 tokens of one V^T row). Written
@@ -157,7 +158,7 @@ constexpr int kStageBytes = 64 * kStagePitch;
 // instruction), and V^T 2 bytes. The staged V^T path needs M % 8 == 0 (the block's token
 // counts are). A staged 64-channel slice is stored after all its residual loads have
 // completed and only the wave touches it, so an output aliasing the residual stays correct.
-template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, typename AccT>
+template <int TN, int TM, bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN][TM],
                                               int n_base, int64_t m_base, int lane,
                                               uint8_t *stage) {
@@ -225,15 +226,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
       *(v4i *)(stage + (k * 8 + (lane >> 3)) * kStagePitch + (lane & 7) * 16) = rl[k];
     });
   };
-  // bf16 values of column block i, token tile j (channels 4 (lane >> 4) .. + 3 of the block)
+  // 16-bit values (bf16, or fp16 when OH) of column block i, token tile j (channels
+  // 4 (lane >> 4) .. + 3 of the block)
   auto stage_vals = [&](int i, int j, const float (&v)[4]) {
     const int t = j * 16 + (lane & 15);           // token within the wave's 64
     const int cb = (i & 3) * 16 + (lane >> 4) * 4;  // channel within the 64 being staged
     if (vsec) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) stage_put2(cb + r, t * 2, f2bf(v[r]));
+      for (int r = 0; r < 4; ++r) stage_put2(cb + r, t * 2, OH ? f2h(v[r]) : f2bf(v[r]));
     } else {
-      stage_put8(t, cb * 2, make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])));
+      stage_put8(t, cb * 2, make_uint2(pack16<OH>(v[0], v[1]), pack16<OH>(v[2], v[3])));
     }
   };
   int64_t mrow[TM];
@@ -438,7 +440,8 @@ constexpr int waitcnt_vm_lgkm0(int vm) {
     __builtin_amdgcn_sched_barrier(0);                  \
   }
 
-template <bool BF16, int EPI, bool OUTF32, bool RESF32>
+// OH: 16-bit outputs stored as fp16 instead of bf16 (the QKV epilogue's attention inputs)
+template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
   constexpr int TN = 8, TM = 4;
   using AccT = typename std::conditional<BF16, v4f, v4i>::type;
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
     }
     // LDS from buffer 1 on is free until the next tile's first loop iteration (its stage 0
     // goes to buffer 0): each wave stages there
-    gemm_epilogue<TN, TM, BF16, EPI, OUTF32, RESF32>(a, acc, n0 + grp * TN * 16,
+    gemm_epilogue<TN, TM, BF16, EPI, OUTF32, RESF32, OH>(a, acc, n0 + grp * TN * 16,
                                                    m0 + wq * TM * 16, lane,
                                                    smem + PP_STAGE + wave * kStageBytes);
     if (!more) break;
@@ -594,9 +597,9 @@ static hipError_t compute_units(int *n) {
   return hipSuccess;
 }
 
-template <bool BF16, int EPI, bool OUTF32, bool RESF32>
+template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH>
 static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
-  auto kern = gemm_pp_kernel<BF16, EPI, OUTF32, RESF32>;
+  auto kern = gemm_pp_kernel<BF16, EPI, OUTF32, RESF32, OH>;
   constexpr size_t lds = (size_t)PP_STAGE + 8 * kStageBytes;  // > 2 stages
   static_assert(lds >= (size_t)2 * PP_STAGE && lds <= 160 * 1024, "LDS budget");
   static std::atomic<uint64_t> lds_set{0};
@@ -614,13 +617,13 @@ static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool BF16, int EPI, bool OUTF32, bool RESF32>
+template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH = false>
 static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
-  return run_gemm_pp<BF16, EPI, OUTF32, RESF32>(a, s);
+  return run_gemm_pp<BF16, EPI, OUTF32, RESF32, OH>(a, s);
 }
 
 // instantiated type combinations (operands -> outputs):
-//   QKV    int8 -> bf16 | int8 -> fp32 | bf16 -> bf16
+//   QKV    int8 -> fp16 | int8 -> bf16 | int8 -> fp32 | bf16 -> fp16 | bf16 -> bf16
 //   GELU   int8 -> bf16 | int8 -> fp32 | bf16 -> bf16
 //   RESID  residual and output bf16 (int8 or bf16 operands) | fp32 (int8 operands)
 static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) {
@@ -628,9 +631,15 @@ static hipError_t gemm_dispatch(EpiKind kind, const GemmArgs &a, hipStream_t s) 
   if (kind == EPI_QKV && !OF && a.M % 8) return hipErrorInvalidValue;  // staged V^T rows
   switch (kind) {
     case EPI_QKV:
-      if (B) return OF ? hipErrorInvalidValue : gemm_tiles<true, EPI_QKV, false, false>(a, s);
-      return OF ? gemm_tiles<false, EPI_QKV, true, false>(a, s)
-                : gemm_tiles<false, EPI_QKV, false, false>(a, s);
+      if (OF && a.qkv_f16) return hipErrorInvalidValue;
+      if (B) {
+        if (OF) return hipErrorInvalidValue;
+        return a.qkv_f16 ? gemm_tiles<true, EPI_QKV, false, false, true>(a, s)
+                         : gemm_tiles<true, EPI_QKV, false, false, false>(a, s);
+      }
+      if (OF) return gemm_tiles<false, EPI_QKV, true, false>(a, s);
+      return a.qkv_f16 ? gemm_tiles<false, EPI_QKV, false, false, true>(a, s)
+                       : gemm_tiles<false, EPI_QKV, false, false, false>(a, s);
     case EPI_GELU:
       if (B) return OF ? hipErrorInvalidValue : gemm_tiles<true, EPI_GELU, false, false>(a, s);
       return OF ? gemm_tiles<false, EPI_GELU, true, false>(a, s)

@@ -238,10 +238,13 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
   // that lane c's 16-byte reads of a plane are consecutive (no bank conflicts)
   constexpr int LP = LDSP ? MAXV * 64 : 1;
   __shared__ float4 lss[4 * LP];
-  // bf16 rows stay packed in registers (half the registers of an fp32 copy): a LayerNorm
-  // row through its mean and variance passes (the modulated fp32 values then replace it),
-  // a quantiser row throughout (absmax on the bit patterns, unpacked again for the codes)
-  constexpr bool PACKED = std::is_same<Tin, uint16_t>::value;
+  // 16-bit rows stay packed in registers (half the registers of an fp32 copy): a bf16
+  // LayerNorm row through its mean and variance passes (the modulated fp32 values then
+  // replace it), a bf16 or fp16 quantiser row throughout (absmax on the bit patterns,
+  // unpacked again for the codes). Tin = _Float16 (fp16 rows) occurs only in RM_Q.
+  constexpr bool HALF = std::is_same<Tin, _Float16>::value;
+  static_assert(!HALF || MODE == RM_Q, "fp16 rows are quantised only");
+  constexpr bool PACKED = std::is_same<Tin, uint16_t>::value || HALF;
   constexpr int NT = WPR * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
@@ -416,8 +419,8 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
     constexpr bool RAWQ = PACKED && MODE == RM_Q;
     float a = 0.f;
     if constexpr (RAWQ) {
-      // |bf16| orders like its 15 magnitude bits read as an integer: the row's largest
-      // magnitude is an integer maximum over the halves, then widened to fp32 once
+      // |bf16| and |fp16| order like their 15 magnitude bits read as an integer: the row's
+      // largest magnitude is an integer maximum over the halves, then widened to fp32 once
       uint32_t mi = 0;
 #pragma unroll
       for (int i = 0; i < MAXV; ++i) {
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
 #pragma unroll
         for (int t = 0; t < 4; ++t) mi = max(mi, max(w[t] & 0x7fffu, (w[t] >> 16) & 0x7fffu));
       }
-      a = __uint_as_float(mi << 16);
+      a = HALF ? h2f_lo(mi) : __uint_as_float(mi << 16);
     } else {
 #pragma unroll
       for (int i = 0; i < MAXV; ++i)
@@ -447,8 +450,8 @@ __global__ __launch_bounds__(256) void row_kernel(const Tin *__restrict__ x,
             const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              e[2 * t] = __uint_as_float(w[t] << 16);
-              e[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+              e[2 * t] = HALF ? h2f_lo(w[t]) : __uint_as_float(w[t] << 16);
+              e[2 * t + 1] = HALF ? h2f_hi(w[t]) : __uint_as_float(w[t] & 0xffff0000u);
             }
           }
           uint32_t lo = 0, hi = 0;
@@ -494,10 +497,15 @@ static hipError_t rows_wpr(const Tin *x, const float *shift, const float *scale,
   return rows_dispatch<MODE, Tin, 4>(x, shift, scale, rows, cols, eps, q, sc, hout, s);
 }
 
-hipError_t launch_rows(int mode, const void *x, bool x_f32, const float *shift,
+hipError_t launch_rows(int mode, const void *x, int x_type, const float *shift,
                        const float *scale, int64_t rows, int cols, float eps, int8_t *q,
                        float *sc, uint16_t *hout, hipStream_t s) {
-  if (x_f32) {
+  if (x_type == ROW_F16) {
+    if (mode != RM_Q) return hipErrorInvalidValue;
+    return rows_wpr<RM_Q, _Float16>((const _Float16 *)x, shift, scale, rows, cols, eps, q, sc,
+                                    hout, s);
+  }
+  if (x_type == ROW_F32) {
     const float *xf = (const float *)x;
     if (mode == RM_LNQ) return rows_wpr<RM_LNQ, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);
     if (mode == RM_Q) return rows_wpr<RM_Q, float>(xf, shift, scale, rows, cols, eps, q, sc, hout, s);

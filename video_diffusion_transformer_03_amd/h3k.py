@@ -2,7 +2,9 @@
 
 Every step of the block runs in the library's HIP kernels; torch provides device memory
 and the current stream. There is no fallback: if the library is missing, or a tensor is
-not on the GPU, the call raises.
+not on the GPU, the call raises. Before each call the binding checks every tensor's
+dtype, shape, contiguity and device against the dims and flags it passes (ValueError),
+since the C library sees only pointers and sizes.
 """
 from __future__ import annotations
 
@@ -20,7 +22,11 @@ OK, EINVAL, EUNSUPPORTED, ENOSPC, EHIP = 0, -1, -2, -3, -4
 F_BF16_GEMM, F_FP32_DEBUG, F_SYNC = 1, 2, 4
 # per-projection bf16 GEMMs (the precision series); F_BF16_GEMM is all three
 F_BF16_QKV, F_BF16_OUT, F_BF16_MLP = 8, 16, 32
-DT_F32, DT_BF16 = 0, 1
+# attention on bf16 operands (default: fp16 Q, K, V, P and O)
+F_ATTN_BF16 = 64
+# h3k_attention: q already carries softmax_scale * log2(e)
+F_Q_BASE2 = 128
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
 KERNELS = ["adaln", "rope_table", "ln_quant", "gemm_qkv", "attention", "rowquant_o",
            "gemm_o", "gemm_up", "rowquant_g", "gemm_down", "token_pair", "token_unpair"]
 
@@ -70,7 +76,7 @@ def lib() -> C.CDLL:
                                             i64, u32, vp, sz, vp]),
             "h3k_block_forward_grid": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), C.POINTER(Dims),
                                                  i32, i32, i32, f32, f32, u32, vp, sz, vp]),
-            "h3k_attention": (C.c_int, [vp, vp, vp, vp, i32, i64, i32, C.c_double, u32, vp]),
+            "h3k_attention": (C.c_int, [vp, vp, vp, vp, i32, i64, i32, C.c_double, C.c_int, u32, vp]),
             "h3k_stack_workspace_bytes": (sz, [C.POINTER(Dims), i64, i32, i32, u32]),
             "h3k_stack_forward": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), i32,
                                             C.POINTER(Dims), i64, i32, i32, u32, vp, sz, vp]),
@@ -114,14 +120,43 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
-def _dev(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+def _meta(t: Optional[torch.Tensor], name: str, dtype=None, shape=None) -> None:
+    """Checks t's dtype (one dtype or a tuple of allowed ones) and shape (None: no tensor)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name} must have dtype {' or '.join(map(str, allowed))}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None) -> Optional[int]:
+    """Device pointer of t after checking it: dtype and shape (_meta), then contiguity and
+    that t lives on the current device, where the library launches its kernels."""
     if t is None:
         return None
+    _meta(t, name, dtype, shape)
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     return t.data_ptr()
+
+
+def _ptrs(*specs) -> List[Optional[int]]:
+    """Pointers of several (tensor, name, dtype, shape) specs: every dtype and shape is
+    checked before any device check, so a wrong dtype or shape is reported as such even for
+    host tensors."""
+    for sp in specs:
+        _meta(*sp)
+    return [_dev(*sp) for sp in specs]
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -129,7 +164,20 @@ def _dt(t: torch.Tensor) -> int:
         return DT_BF16
     if t.dtype == torch.float32:
         return DT_F32
+    if t.dtype == torch.float16:
+        return DT_F16
     raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def act_dtype(flags: int):
+    """Activation dtype of the block, stack and denoise calls under `flags`."""
+    return torch.float32 if flags & F_FP32_DEBUG else torch.bfloat16
+
+
+def _ws(ws: torch.Tensor, name: str = "ws") -> int:
+    if ws.dim() != 1:
+        raise ValueError(f"{name} must be a 1-D byte tensor")
+    return _dev(ws, name, torch.uint8)
 
 
 def make_dims(d, n_heads, head_dim, d_ff, d_cond, grid, rope_theta=10000.0, ln_eps=1e-6) -> Dims:
@@ -158,18 +206,48 @@ class BlockWeights:
     wb_up: Optional[torch.Tensor] = None
     wb_down: Optional[torch.Tensor] = None
 
-    def c_struct(self) -> BlockWeightsC:
-        return BlockWeightsC(*[_dev(getattr(self, f), f) for f, _ in BlockWeightsC._fields_])
+    def specs(self, dims: "Dims", flags: int = 0) -> list:
+        """(tensor, name, dtype, shape) of every field: the tensors the flags' path reads are
+        required: w_ada bf16 [6d, d_cond]; int8 codes [N, K] with fp32 scales [N] for the W8A8
+        projections; bf16 [N, K] originals for the bf16 ones. The others are checked if set."""
+        d, F = dims.d, dims.d_ff
+        shapes = {"qkv": (3 * d, d), "o": (d, d), "up": (F, d), "down": (d, F)}
+        bf16_proj = {"qkv": bool(flags & (F_BF16_GEMM | F_BF16_QKV)),
+                     "o": bool(flags & (F_BF16_GEMM | F_BF16_OUT)),
+                     "up": bool(flags & (F_BF16_GEMM | F_BF16_MLP)),
+                     "down": bool(flags & (F_BF16_GEMM | F_BF16_MLP))}
+        sp = {"w_ada": (self._req("w_ada"), "w_ada", torch.bfloat16, (6 * d, dims.d_cond))}
+        for k, shp in shapes.items():
+            get_q = self.__dict__.get if bf16_proj[k] else (lambda f: self._req(f))
+            get_b = (lambda f: self._req(f)) if bf16_proj[k] else self.__dict__.get
+            sp["w_" + k] = (get_q("w_" + k), "w_" + k, torch.int8, shp)
+            sp["s_" + k] = (get_q("s_" + k), "s_" + k, torch.float32, shp[:1])
+            sp["wb_" + k] = (get_b("wb_" + k), "wb_" + k, torch.bfloat16, shp)
+        return [sp[f] for f, _ in BlockWeightsC._fields_]
+
+    def c_struct(self, dims: Optional["Dims"] = None, flags: int = 0) -> BlockWeightsC:
+        """The C struct of device pointers; with dims, every tensor is checked (specs)."""
+        if dims is None:
+            return BlockWeightsC(*[_dev(getattr(self, f), f) for f, _ in BlockWeightsC._fields_])
+        return BlockWeightsC(*_ptrs(*self.specs(dims, flags)))
+
+    def _req(self, f: str) -> torch.Tensor:
+        t = getattr(self, f)
+        if t is None:
+            raise ValueError(f"block weights: {f} is required by these flags")
+        return t
 
 
 # ------------------------------------------------------------------------ entry points
 def quantize_weights(w: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-output-channel int8 quantisation of w [N, K] (bf16 or fp32, on the GPU)."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [n_out, k_in]")
     n, k = w.shape
+    pw = _dev(w, "w", (torch.bfloat16, torch.float32))
     q = torch.empty((n, k), dtype=torch.int8, device=w.device)
     s = torch.empty((n,), dtype=torch.float32, device=w.device)
-    _check(lib().h3k_quantize_weights(_dev(w, "w"), _dt(w), n, k, q.data_ptr(), s.data_ptr(),
-                                      _stream(stream)))
+    _check(lib().h3k_quantize_weights(pw, _dt(w), n, k, q.data_ptr(), s.data_ptr(), _stream(stream)))
     return q, s
 
 
@@ -202,18 +280,33 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty((nbytes,), dtype=torch.uint8, device=device)
 
 
+def _act_io(x, out, cond, dims: Dims, flags: int, L: int, blocks=()):
+    """Pointers of the activation input/output [L, d] (the flags' activation dtype), of the
+    conditioning vector fp32 [d_cond] and of each block's weights (C structs), all checked
+    (every dtype and shape before any device check)."""
+    dt = act_dtype(flags)
+    io = [(x, "x", dt, (L, dims.d)), (out, "out", dt, (L, dims.d)),
+          (cond, "cond", torch.float32, (dims.d_cond,))]
+    wsp = [b.specs(dims, flags) for b in blocks]
+    for sp in io + [e for w in wsp for e in w]:
+        _meta(*sp)
+    px, po, pc = [_dev(*sp) for sp in io]
+    structs = [BlockWeightsC(*[_dev(*e) for e in w]) for w in wsp]
+    return px, po, pc, structs
+
+
 def block_forward(x: torch.Tensor, cond: torch.Tensor, w: BlockWeights, dims: Dims,
                   flags: int = 0, ws: Optional[torch.Tensor] = None,
                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One block: x [L, d] (bf16; fp32 under F_FP32_DEBUG) -> out (may be x itself)."""
     L = x.shape[0]
     if ws is None:
         ws = alloc_workspace(workspace_bytes(dims, L, flags), x.device)
     if out is None:
         out = torch.empty_like(x)
-    wc = w.c_struct()
-    _check(lib().h3k_block_forward(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), C.byref(wc),
-                                   C.byref(dims), L, flags, _dev(ws, "ws"), ws.numel(),
-                                   _stream(stream)))
+    px, po, pc, (wc,) = _act_io(x, out, cond, dims, flags, L, [w])
+    _check(lib().h3k_block_forward(px, po, pc, C.byref(wc), C.byref(dims), L, flags, _ws(ws),
+                                   ws.numel(), _stream(stream)))
     return out
 
 
@@ -224,16 +317,18 @@ def block_forward_grid(x: torch.Tensor, cond: torch.Tensor, w: BlockWeights, dim
     """One block on the token grid `grid` with w positions w * scale + offset."""
     T, Hg, Wg = grid
     L = x.shape[0]
+    if L != T * Hg * Wg:
+        raise ValueError(f"x has {L} tokens, grid {tuple(grid)} has {T * Hg * Wg}")
     if ws is None:
         g = Dims.from_buffer_copy(dims)
         g.grid_t, g.grid_h, g.grid_w = T, Hg, Wg
         ws = alloc_workspace(workspace_bytes(g, L, flags), x.device)
     if out is None:
         out = torch.empty_like(x)
-    wc = w.c_struct()
-    _check(lib().h3k_block_forward_grid(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), C.byref(wc),
-                                        C.byref(dims), T, Hg, Wg, float(w_pos_scale), float(w_pos_offset),
-                                        flags, _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    px, po, pc, (wc,) = _act_io(x, out, cond, dims, flags, L, [w])
+    _check(lib().h3k_block_forward_grid(px, po, pc, C.byref(wc), C.byref(dims), T, Hg, Wg,
+                                        float(w_pos_scale), float(w_pos_offset), flags, _ws(ws),
+                                        ws.numel(), _stream(stream)))
     return out
 
 
@@ -244,19 +339,28 @@ def ws_view(ws: torch.Tensor, layout: Dict[str, int], name: str, dtype, shape) -
         n *= s
     nbytes = n * torch.empty((), dtype=dtype).element_size()
     off = layout[name]
+    if off + nbytes > ws.numel():
+        raise ValueError(f"{name} {tuple(shape)} {dtype} does not fit the workspace")
     return ws[off:off + nbytes].view(dtype).view(*shape)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, softmax_scale: Optional[float] = None,
               flags: int = 0, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """q, k [H, L, Dh]; vt [H, Dh, L] -> o [L, H*Dh]."""
+    """q, k [H, L, Dh]; vt [H, Dh, L] -> o [L, H*Dh], all of one dtype: fp16 or bf16
+    (matrix cores) or fp32 (fp64 arithmetic)."""
+    if q.dim() != 3:
+        raise ValueError("q must be 3-D [H, L, Dh]")
     H, L, Dh = q.shape
+    dts = (torch.float16, torch.bfloat16, torch.float32)
+    _meta(q, "q", dts)
     if softmax_scale is None:
         softmax_scale = Dh ** -0.5
     if out is None:
         out = torch.empty((L, H * Dh), dtype=q.dtype, device=q.device)
-    _check(lib().h3k_attention(_dev(q, "q"), _dev(k, "k"), _dev(vt, "vt"), _dev(out, "out"), H, L, Dh,
-                               float(softmax_scale), flags, _stream(stream)))
+    pq, pk, pv, po = _ptrs((q, "q", dts, None), (k, "k", q.dtype, (H, L, Dh)),
+                           (vt, "vt", q.dtype, (H, Dh, L)), (out, "out", q.dtype, (L, H * Dh)))
+    _check(lib().h3k_attention(pq, pk, pv, po, H, L, Dh, float(softmax_scale), _dt(q), flags,
+                               _stream(stream)))
     return out
 
 
@@ -276,10 +380,10 @@ def stack_forward(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWei
         ws = alloc_workspace(stack_workspace_bytes(dims, L, tr_begin, tr_end, flags), x.device)
     if out is None:
         out = torch.empty_like(x)
-    arr = (BlockWeightsC * len(blocks))(*[b.c_struct() for b in blocks])
-    _check(lib().h3k_stack_forward(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), arr, len(blocks),
-                                   C.byref(dims), L, tr_begin, tr_end, flags, _dev(ws, "ws"),
-                                   ws.numel(), _stream(stream)))
+    px, po, pc, structs = _act_io(x, out, cond, dims, flags, L, blocks)
+    arr = (BlockWeightsC * len(structs))(*structs)
+    _check(lib().h3k_stack_forward(px, po, pc, arr, len(blocks), C.byref(dims), L, tr_begin, tr_end,
+                                   flags, _ws(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -296,10 +400,10 @@ def denoise(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWeights],
     layers = len(blocks) if layers is None else layers
     if ws is None:
         ws = alloc_workspace(denoise_workspace_bytes(dims, L, tr_begin, tr_end, flags), x.device)
-    arr = (BlockWeightsC * len(blocks))(*[b.c_struct() for b in blocks])
-    _check(lib().h3k_denoise(_dev(x, "x"), _dev(cond, "cond"), arr, len(blocks), C.byref(dims), L,
-                             steps, reuse, core_reuse, layers, tr_begin, tr_end, flags,
-                             _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    px, _, pc, structs = _act_io(x, x, cond, dims, flags, L, blocks)
+    arr = (BlockWeightsC * len(structs))(*structs)
+    _check(lib().h3k_denoise(px, pc, arr, len(blocks), C.byref(dims), L, steps, reuse, core_reuse,
+                             layers, tr_begin, tr_end, flags, _ws(ws), ws.numel(), _stream(stream)))
     return x
 
 
@@ -311,11 +415,12 @@ class StackGraph:
     def __init__(self, x, cond, blocks, dims, tr_begin, tr_end, flags, ws, out, capture_stream):
         self._keep = (x, cond, list(blocks), ws, out)
         self.out = out
-        arr = (BlockWeightsC * len(blocks))(*[b.c_struct() for b in blocks])
+        L = x.shape[0]
+        px, po, pc, structs = _act_io(x, out, cond, dims, flags, L, blocks)
+        arr = (BlockWeightsC * len(structs))(*structs)
         h = C.c_void_p()
-        _check(lib().h3k_stack_graph_create(_dev(x, "x"), _dev(out, "out"), _dev(cond, "cond"), arr,
-                                            len(blocks), C.byref(dims), x.shape[0], tr_begin, tr_end,
-                                            flags, _dev(ws, "ws"), ws.numel(),
+        _check(lib().h3k_stack_graph_create(px, po, pc, arr, len(blocks), C.byref(dims), L, tr_begin,
+                                            tr_end, flags, _ws(ws), ws.numel(),
                                             C.c_void_p(capture_stream.cuda_stream), C.byref(h)))
         self._h = h
 
@@ -345,46 +450,60 @@ def stack_graph(x: torch.Tensor, cond: torch.Tensor, blocks: Sequence[BlockWeigh
 
 
 def adaln_modulation(w_ada: torch.Tensor, cond: torch.Tensor, stream=None) -> torch.Tensor:
+    if w_ada.dim() != 2:
+        raise ValueError("w_ada must be 2-D [n_out, d_cond]")
     n, dc = w_ada.shape
+    pw, pc = _ptrs((w_ada, "w_ada", torch.bfloat16, None), (cond, "cond", torch.float32, (dc,)))
     m = torch.empty((n,), dtype=torch.float32, device=w_ada.device)
-    _check(lib().h3k_adaln_modulation(_dev(w_ada, "w_ada"), _dev(cond, "cond"), m.data_ptr(), n, dc,
-                                      _stream(stream)))
+    _check(lib().h3k_adaln_modulation(pw, pc, m.data_ptr(), n, dc, _stream(stream)))
     return m
 
 
 def ln_modulate_quant(x: torch.Tensor, shift: torch.Tensor, scale: torch.Tensor, eps: float = 1e-6,
                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
     rows, cols = x.shape
+    px, ps, pk = _ptrs((x, "x", (torch.bfloat16, torch.float32), None),
+                       (shift, "shift", torch.float32, (cols,)), (scale, "scale", torch.float32, (cols,)))
     q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
     s = torch.empty((rows,), dtype=torch.float32, device=x.device)
-    _check(lib().h3k_ln_modulate_quant(_dev(x, "x"), _dt(x), _dev(shift, "shift"), _dev(scale, "scale"),
-                                       rows, cols, eps, q.data_ptr(), s.data_ptr(), _stream(stream)))
+    _check(lib().h3k_ln_modulate_quant(px, _dt(x), ps, pk, rows, cols, eps, q.data_ptr(), s.data_ptr(),
+                                       _stream(stream)))
     return q, s
 
 
 def row_quantize(x: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
     rows, cols = x.shape
+    px = _dev(x, "x", (torch.bfloat16, torch.float32, torch.float16))
     q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
     s = torch.empty((rows,), dtype=torch.float32, device=x.device)
-    _check(lib().h3k_row_quantize(_dev(x, "x"), _dt(x), rows, cols, q.data_ptr(), s.data_ptr(),
-                                  _stream(stream)))
+    _check(lib().h3k_row_quantize(px, _dt(x), rows, cols, q.data_ptr(), s.data_ptr(), _stream(stream)))
     return q, s
 
 
 def gemm_i8_i32(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
+    pa, pb = _ptrs((a, "a", torch.int8, None), (b, "b", torch.int8, (N, K)))
     c = torch.empty((M, N), dtype=torch.int32, device=a.device)
-    _check(lib().h3k_gemm_i8_i32(_dev(a, "a"), _dev(b, "b"), c.data_ptr(), M, N, K, _stream(stream)))
+    _check(lib().h3k_gemm_i8_i32(pa, pb, c.data_ptr(), M, N, K, _stream(stream)))
     return c
 
 
 def token_pair(x: torch.Tensor, grid, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     T, Hg, Wg = grid
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [T*Hg*Wg, d]")
     d = x.shape[1]
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), (T * Hg * Wg, d))
     xr = torch.empty((T * Hg * (Wg // 2), d), dtype=x.dtype, device=x.device)
     xr2 = torch.empty_like(xr)
-    _check(lib().h3k_token_pair(_dev(x, "x"), xr.data_ptr(), xr2.data_ptr(), _dt(x), T, Hg, Wg, d,
+    _check(lib().h3k_token_pair(px, xr.data_ptr(), xr2.data_ptr(), _dt(x), T, Hg, Wg, d,
                                 _stream(stream)))
     return xr, xr2
 
@@ -393,8 +512,14 @@ def token_unpair(x_pre: torch.Tensor, xr_out: torch.Tensor, xr_in: torch.Tensor,
                  stream=None) -> torch.Tensor:
     """In place on x_pre; returns it."""
     T, Hg, Wg = grid
-    _check(lib().h3k_token_unpair(_dev(x_pre, "x_pre"), _dev(xr_out, "xr_out"), _dev(xr_in, "xr_in"),
-                                  _dt(x_pre), T, Hg, Wg, x_pre.shape[1], _stream(stream)))
+    if x_pre.dim() != 2:
+        raise ValueError("x_pre must be 2-D [T*Hg*Wg, d]")
+    d = x_pre.shape[1]
+    _meta(x_pre, "x_pre", (torch.bfloat16, torch.float32))
+    pp, po, pi = _ptrs((x_pre, "x_pre", x_pre.dtype, (T * Hg * Wg, d)),
+                       (xr_out, "xr_out", x_pre.dtype, (T * Hg * (Wg // 2), d)),
+                       (xr_in, "xr_in", x_pre.dtype, (T * Hg * (Wg // 2), d)))
+    _check(lib().h3k_token_unpair(pp, po, pi, _dt(x_pre), T, Hg, Wg, d, _stream(stream)))
     return x_pre
 
 
