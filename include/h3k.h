@@ -174,6 +174,21 @@ int h3k_block_forward(const void *x_in, void *x_out, const float *cond,
                       const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
                       uint32_t flags, void *ws, size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): h3k_block_forward with its workspace in
+ * a library-owned scratch array of H3K_NOALLOC_MAX_BYTES per GPU (allocated when the
+ * library is loaded, held until the process ends) instead of a caller workspace. The call
+ * itself allocates nothing and records no profiling events. Arguments, layouts and errors
+ * as h3k_block_forward; H3K_ENOSPC when h3k_workspace_bytes(dm, L, flags) exceeds
+ * H3K_NOALLOC_MAX_BYTES (e.g. d = 256 up to L ~ 10000; d = 5120 up to L ~ 500). Every call
+ * on one GPU shares that GPU's array and leaves its intermediates there (nothing in it
+ * needs clearing between calls: each is written before it is read), so calls that overlap
+ * on one GPU (several streams or threads) race; serialise them. */
+#define H3K_NOALLOC_MAX_BYTES (64u << 20)
+int h3k_block_forward_noalloc(const void *x_in, void *x_out, const float *cond,
+                              const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
+                              uint32_t flags, void *stream);
+
 /* One block on an explicit token grid (T, Hg, Wg) whose w positions are
  * w * w_pos_scale + w_pos_offset in RoPE; dm's own grid fields are ignored and
  * L = T*Hg*Wg. This is the call the stack makes for its horizontally paired middle

@@ -280,3 +280,24 @@ def test_binding_component_checks():
         h3k.quantize_weights(torch.zeros(4, 8, dtype=f16))
     with pytest.raises(ValueError, match="must be a GPU tensor"):
         h3k.row_quantize(torch.zeros(4, 16, dtype=f16))
+
+
+def test_noalloc_validation():
+    """The allocation-free block call checks its arguments like h3k_block_forward and
+    refuses, before touching the device, a call whose workspace exceeds its scratch array."""
+    lib = h3k.lib()
+    w = h3k.BlockWeightsC(*([FAKE] * 9 + [None] * 4))
+    dm = tiny_dims()
+    call = lambda *a: lib.h3k_block_forward_noalloc(*a, None)  # noqa: E731
+    assert call(None, FAKE, FAKE, C.byref(w), C.byref(dm), 512, 0) == h3k.EINVAL
+    assert call(FAKE, FAKE, FAKE, None, C.byref(dm), 512, 0) == h3k.EINVAL
+    assert call(FAKE, FAKE, FAKE, C.byref(w), C.byref(dm), 500, 0) == h3k.EINVAL
+    assert call(FAKE, FAKE, FAKE, C.byref(w), C.byref(dm), 512, 256) == h3k.EINVAL
+    big = h3k.make_dims(5120, 40, 128, 20480, 5120, (4, 32, 32))
+    assert h3k.workspace_bytes(big, 4096, 0) > h3k.NOALLOC_MAX_BYTES
+    assert call(FAKE, FAKE, FAKE, C.byref(w), C.byref(big), 4096, 0) == h3k.ENOSPC
+    assert "scratch" in h3k.last_error()
+    # the binding's constant is the header's
+    src = open(HEADER).read()
+    assert re.search(r"#define H3K_NOALLOC_MAX_BYTES \(64u << 20\)", src)
+    assert h3k.NOALLOC_MAX_BYTES == 64 << 20

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -374,11 +375,65 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
   return H3K_OK;
 }
 
+// ------------------------------------------------------------------ allocation-free block
+// Workspace of h3k_block_forward_noalloc: one array per GPU, held from the library's load
+// until the process ends. The name `scratch` is a host-side handle only; host code uses the
+// device address hipGetSymbolAddress returns for the current device (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[H3K_NOALLOC_MAX_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};  // per device id, filled on the first call on that device
+
+int scratch_ptr(const char *fn, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(H3K_EUNSUPPORTED, "%s: device id %d >= 64", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(H3K_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return H3K_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char *h3k_last_error(void) { return g_err.c_str(); }
+
+int h3k_block_forward_noalloc(const void *x_in, void *x_out, const float *cond,
+                              const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
+                              uint32_t flags, void *stream) {
+  const char *fn = "h3k_block_forward_noalloc";
+  int rc;
+  if ((rc = check_flags(fn, flags))) return rc;
+  if ((rc = check_dims(fn, dm, L))) return rc;
+  H3K_CHECK_PTR(x_in);
+  H3K_CHECK_PTR(x_out);
+  H3K_CHECK_PTR(cond);
+  if ((rc = check_weights(fn, w, flags))) return rc;
+  h3k_ws_layout lay;
+  plan(dm, L, flags, &lay);
+  if (lay.total > (size_t)H3K_NOALLOC_MAX_BYTES)
+    return fail(H3K_ENOSPC, "%s: this call needs %zu bytes of workspace, more than the %zu of the "
+                "allocation-free scratch; use h3k_block_forward with a caller workspace",
+                fn, lay.total, (size_t)H3K_NOALLOC_MAX_BYTES);
+  void *ws = nullptr;
+  if ((rc = scratch_ptr(fn, &ws))) return rc;
+  // no profiling events either (creating one allocates)
+  const bool prof = g_prof_on;
+  g_prof_on = false;
+  rc = block_impl(fn, x_in, x_out, cond, w, dm, dm->grid_t, dm->grid_h, dm->grid_w, 1.f, 0.f, flags,
+                  ws, (hipStream_t)stream);
+  g_prof_on = prof;
+  return rc;
+}
 
 int h3k_quantize_weights(const void *w, int w_dtype, int64_t n_out, int64_t k_in,
                          int8_t *q_out, float *scale_out, void *stream) {

@@ -74,6 +74,8 @@ def lib() -> C.CDLL:
             "h3k_workspace_layout": (C.c_int, [C.POINTER(Dims), i64, u32, C.POINTER(WsLayout)]),
             "h3k_block_forward": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), C.POINTER(Dims),
                                             i64, u32, vp, sz, vp]),
+            "h3k_block_forward_noalloc": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC),
+                                                    C.POINTER(Dims), i64, u32, vp]),
             "h3k_block_forward_grid": (C.c_int, [vp, vp, vp, C.POINTER(BlockWeightsC), C.POINTER(Dims),
                                                  i32, i32, i32, f32, f32, u32, vp, sz, vp]),
             "h3k_attention": (C.c_int, [vp, vp, vp, vp, i32, i64, i32, C.c_double, C.c_int, u32, vp]),
@@ -307,6 +309,24 @@ def block_forward(x: torch.Tensor, cond: torch.Tensor, w: BlockWeights, dims: Di
     px, po, pc, (wc,) = _act_io(x, out, cond, dims, flags, L, [w])
     _check(lib().h3k_block_forward(px, po, pc, C.byref(wc), C.byref(dims), L, flags, _ws(ws),
                                    ws.numel(), _stream(stream)))
+    return out
+
+
+# workspace bytes of the library's own scratch array (h3k_block_forward_noalloc)
+NOALLOC_MAX_BYTES = 64 << 20
+
+
+def block_forward_noalloc(x: torch.Tensor, cond: torch.Tensor, w: BlockWeights, dims: Dims,
+                          flags: int = 0, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """h3k_block_forward_noalloc: one block with the library's scratch array as workspace
+    (no device allocation in the call; `out` must be given by callers that cannot allocate).
+    Calls that overlap on one GPU race on that array."""
+    L = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    px, po, pc, (wc,) = _act_io(x, out, cond, dims, flags, L, [w])
+    _check(lib().h3k_block_forward_noalloc(px, po, pc, C.byref(wc), C.byref(dims), L, flags,
+                                           _stream(stream)))
     return out
 
 
