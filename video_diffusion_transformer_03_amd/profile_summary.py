@@ -47,12 +47,40 @@ def source_hash(fname: str) -> str:
     return hashlib.sha256(data).hexdigest()[:16]
 
 
+# template arguments in mangled names the profiler leaves undemangled (it does not know
+# _Float16, "DF16_"): integer literals, bool literals and the types used here
+_MANGLED_ARGS = [(r"Li(-?\d+)E", r"\1"), (r"Lb0E", "false"), (r"Lb1E", "true"),
+                 (r"DF16_", "_Float16"), (r"^t", "unsigned short"), (r"^f", "float")]
+
+
+def _demangle_args(args: str) -> str:
+    out = []
+    while args:
+        for pat, rep in _MANGLED_ARGS:
+            m = re.match(pat if pat.startswith("^") else "^" + pat, args)
+            if m:
+                out.append(m.expand(rep))
+                args = args[m.end():]
+                break
+        else:
+            out.append(args)
+            break
+    return ", ".join(out)
+
+
 def short_name(name: str) -> str:
     m = re.search(r"h3k::(\w+)<([^>]*)>", name)
     if m:
         return f"{m.group(1)}<{m.group(2)}>"
+    m = re.match(r"_ZN3h3k\d+(\w+?)I(.*?)EEEv", name)
+    if m:  # a mangled h3k kernel
+        return f"{m.group(1)}<{_demangle_args(m.group(2) + 'E')}>"
     m = re.search(r"h3k::(\w+)", name)
     return m.group(1) if m else name[:60]
+
+
+def is_ours(name: str) -> bool:
+    return "h3k::" in name or name.startswith("_ZN3h3k")
 
 
 def _one(pattern: str) -> str:
@@ -129,7 +157,7 @@ def main():
                "sources": {f: source_hash(f) for f, _ in KINDS.values()}, "kernels": {}}
     rows = []
     for name, (calls, avg_ns, tot_ns) in stats.items():
-        if "h3k::" not in name:
+        if not is_ours(name):
             continue
         f_kib = [v for (k, _), v in fetch.items() if k == name]
         w_kib = [v for (k, _), v in write.items() if k == name]
@@ -163,7 +191,7 @@ def sq_summary(a):
              f"{'kernel':58s} {'MFMA busy':>10s} {'wait/wave':>10s} {'LDS confl/inst':>15s} {'LDS active':>11s}"]
     rows = []
     for name, cs in acc.items():
-        if "h3k::" not in name:
+        if not is_ours(name):
             continue
         d = {c: sum(v) / len(v) for c, v in cs.items()}
         cyc = d.get("GRBM_GUI_ACTIVE", 0) / 8
