@@ -71,11 +71,7 @@ def cpu_baseline(wl, x, c, bw, n_rows: int):
     prefix = t1 - t0
     rest = max((t2 - t1) - prefix, 1e-9)
     per_token = prefix / wl.L + rest / n_rows
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = _cores()
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -87,7 +83,157 @@ def cpu_baseline(wl, x, c, bw, n_rows: int):
             "sample": (f"{wl.name}: LN+quant+QKV+RoPE for all {wl.L} tokens ({prefix:.1f} s), then "
                        f"attention, out-proj and MLP for {n_rows} evenly spaced tokens "
                        f"({rest:.1f} s); tokens/s = 1 / (prefix/{wl.L} + rest/{n_rows})"),
-            "seconds": t2 - t0}
+            "seconds": t2 - t0, "prefix_per_token_s": prefix / wl.L, "rest_per_token_s": rest / n_rows}
+
+
+def log(msg: str) -> None:
+    """Progress on stderr (stdout carries only the result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _oracle_w(bw):
+    import numpy as np
+    w = {"w_ada": bw.w_ada.detach().float().cpu().numpy().astype(np.float64)}
+    for k in ("qkv", "o", "up", "down"):
+        w["q_" + k] = getattr(bw, "w_" + k).cpu().numpy()
+        w["s_" + k] = getattr(bw, "s_" + k).cpu().numpy()
+    return w
+
+
+def attention_row_seconds(L, H, Dh, rows=8, seed=5):
+    """Host seconds the oracle's attention takes per query row at L keys (random values:
+    its cost depends on the shapes only)."""
+    import numpy as np
+
+    import oracle as O
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((L, H, Dh))
+    k = g.standard_normal((L, H, Dh))
+    v = g.standard_normal((L, H, Dh))
+    t0 = time.perf_counter()
+    O.attention(q, k, v, np.arange(rows))
+    return (time.perf_counter() - t0) / rows
+
+
+def cpu_baselines(S, h3k, torch, head_cpu, bw_head):
+    """The oracle on the host for the other workloads, each bounded to a few seconds:
+      - tiny (2 blocks, d = 256, L = 512): the whole stack, median of 3, on all the threads
+        and on one (the per-core figure);
+      - block_l4096: the headline's sampling on its own activations (8 outlier channels);
+        the d = 5120 weights are the headline's (the oracle's cost depends on the shapes);
+      - block_l65536 and the 50-block stack at L = 16384 (with and without pairing in blocks
+        [10, 40)): extrapolated from the headline sample's per-token costs and the oracle's
+        attention timed per query row at each key count (attention per row grows with L;
+        the rest is per token)."""
+    import numpy as np
+
+    import oracle as O
+    out = {}
+    cores = _cores()
+    # tiny: full stack
+    wl = S.WORKLOADS["tiny"]
+    blocks = [h3k.quantize_block({k: v.cuda() for k, v in S.block_weights_bf16(wl, b).items()})
+              for b in range(wl.n_blocks)]
+    ow = [_oracle_w(b) for b in blocks]
+    x = S.activations(wl).float().numpy().astype(np.float64)
+    c = S.conditioning(wl).numpy().astype(np.float64)
+    kw = dict(n_heads=wl.n_heads, head_dim=wl.head_dim, grid=wl.grid)
+
+    def run_tiny():
+        t0 = time.perf_counter()
+        O.stack_forward(x, c, ow, **kw)
+        return time.perf_counter() - t0
+    ts = sorted(run_tiny() for _ in range(3))
+    ent = {"value": round(wl.L / ts[1], 1), "unit": "tokens/s (2-block stack)", "cores": cores,
+           "kind": "oracle", "sample": "whole 2-block stack, median of 3"}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = sorted(run_tiny() for _ in range(3))[1]
+        ent["one_thread"] = {"value": round(wl.L / t1, 1), "cores": 1}
+    except Exception:
+        pass
+    out["tiny"] = ent
+    # block_l4096 on its own activations
+    wl4 = S.WORKLOADS["block_l4096"]
+    x4 = S.activations(wl4, device="cuda")
+    c4 = S.conditioning(wl4, device="cuda")
+    r4 = cpu_baseline(wl4, x4, c4, bw_head, 512)
+    out["block_l4096"] = {k: r4[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    # extrapolations from the headline sample
+    wl2 = S.WORKLOADS["block_l16384"]
+    pre, rest = head_cpu["prefix_per_token_s"], head_cpu["rest_per_token_s"]
+    a16 = attention_row_seconds(wl2.L, wl2.n_heads, wl2.head_dim)
+    a8 = attention_row_seconds(wl2.L // 2, wl2.n_heads, wl2.head_dim)
+    a64 = attention_row_seconds(4 * wl2.L, wl2.n_heads, wl2.head_dim, rows=4)
+    rest_na = max(rest - a16, 0.0)  # per-token work other than attention
+
+    def block_s(L, a_row):
+        return L * (pre + rest_na + a_row)
+    out["block_l65536"] = {"value": round(65536 / block_s(65536, a64), 2), "unit": "tokens/s",
+                           "cores": cores, "kind": "oracle (extrapolated)",
+                           "sample": ("per-token costs of the block_l16384 sample with the attention per "
+                                      f"row timed at 65536 keys ({a64:.3f} s per row)")}
+    full = 50 * block_s(wl2.L, a16)
+    paired = 20 * block_s(wl2.L, a16) + 30 * block_s(wl2.L // 2, a8)
+    out["stack50_l16384"] = {"value": round(full, 1), "unit": "s per denoising step (50 blocks)",
+                             "token_reduction_value": round(paired, 1), "cores": cores,
+                             "kind": "oracle (extrapolated)",
+                             "sample": ("50 x the block_l16384 per-token costs; with pairing, 30 blocks at "
+                                        f"8192 tokens (attention per row {a8:.4f} s at 8192 keys, "
+                                        f"{a16:.4f} s at 16384)")}
+    return out
+
+
+def weight_bytes(wl):
+    """Bytes of one block's weights in each variant of the precision series (the pages
+    report the model's DiT weights going from 36.4 GiB in BF16 to 19.8 GiB with int8): the
+    AdaLN linear layer stays bf16; a W8A8 projection holds int8 codes and fp32 scales, a
+    bf16 one its bf16 matrix."""
+    d, F, dc = wl.d, wl.d_ff, wl.d_cond
+    proj = {"qkv": (3 * d, d), "o": (d, d), "up": (F, d), "down": (d, F)}
+    int8_of = {"bf16": (), "int8_mlp": ("up", "down"), "int8_mlp_qkv": ("qkv", "up", "down"),
+               "w8a8": ("qkv", "o", "up", "down")}
+    out = {}
+    for name, i8 in int8_of.items():
+        b = 6 * d * dc * 2
+        for k, (n, kk) in proj.items():
+            b += n * kk + 4 * n if k in i8 else 2 * n * kk
+        out[name] = {"per_block_GiB": round(b / 2**30, 4), "per_50_blocks_GiB": round(50 * b / 2**30, 2)}
+    return out
+
+
+def clock_under_load(torch, fn, n=40):
+    """Median engine clock (MHz) sampled while n calls of fn run, or None if unreadable."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                samples.append(float(torch.cuda.clock_rate()))
+            except Exception:
+                return
+            time.sleep(0.01)
+    th = threading.Thread(target=sample)
+    for _ in range(n):
+        fn()
+    th.start()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    samples = sorted(v for v in samples if v > 0)
+    return samples[len(samples) // 2] if samples else None
 
 
 def main():
@@ -101,6 +247,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the 50-block stack and L=65536 measurements")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the engine clock under load (profiled runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB on the device twice (counter calibration) and exit")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -148,6 +296,7 @@ def main():
     out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
 
+    log(f"{wl.name} {args.variant}: {args.warmup} warm-up and {args.steps} timed steps")
     for _ in range(args.warmup):
         h3k.block_forward(x, c, bw, dims, flags, ws, out)
     torch.cuda.synchronize()
@@ -168,6 +317,8 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = L * args.steps / (t1 - t0)
+    sclk = None if args.no_clock else clock_under_load(
+        torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, out))
 
     work = kernel_work(wl, L)
     copy_gbps = device_copy_gbps(torch)
@@ -188,7 +339,7 @@ def main():
             else:
                 rate = wk[1] / (avg * 1e-3) / 1e9
                 ent.update(achieved=round(rate, 1), peak=HBM_GBS, unit="GB/s",
-                           frac=round(rate / HBM_GBS, 4), frac_of_copy=round(rate / copy_gbps, 4))
+                           frac=round(rate / HBM_GBS, 4), vs_torch_copy=round(rate / copy_gbps, 4))
         kernels[name] = ent
 
     label = {"w8a8": "W8A8", "w8a8_attn_bf16": "W8A8, bf16 attention", "bf16gemm": "BF16",
@@ -224,15 +375,38 @@ def main():
     props = torch.cuda.get_device_properties(0)
     result["device"] = {"name": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
-                        "hbm_gib": round(props.total_memory / 2**30, 1)}
-    result["device_copy_GBps"] = round(copy_gbps, 1)
+                        "hbm_gib": round(props.total_memory / 2**30, 1),
+                        "max_clock_mhz": round(getattr(props, "clock_rate", 0) / 1000.0, 1) or None,
+                        "clock_under_load_mhz": sclk}
+    if int8 and sclk:
+        # the dense peaks recomputed at the clock observed under this load: CUs x clock x
+        # 8192 int8 ops (4096 16-bit flops) per clock per CU
+        cu = props.multi_processor_count
+        pk8 = cu * sclk * 1e6 * 8192 / 1e12
+        pk16 = cu * sclk * 1e6 * 4096 / 1e12
+        gemm_ops = sum(work[k][1] for k in ("gemm_qkv", "gemm_o", "gemm_up", "gemm_down"))
+        gemm_ms = sum(kernels[k]["ms_per_step"] for k in ("gemm_qkv", "gemm_o", "gemm_up", "gemm_down"))
+        result["at_observed_clock"] = {
+            "clock_mhz": sclk, "peak_int8_TOPs": round(pk8, 1), "peak_16bit_TFLOPs": round(pk16, 1),
+            "gemm_int8_frac": round(gemm_ops / (gemm_ms * 1e-3) / 1e12 / pk8, 4),
+            "attention_frac": round(work["attention"][1] / (kernels["attention"]["ms_per_step"] * 1e-3) / 1e12 / pk16, 4)}
+    # a plain torch device copy, for comparison (not a ceiling: the row kernels beat it)
+    result["torch_copy_GBps"] = round(copy_gbps, 1)
     result["kernels"] = kernels
     if not args.no_extras and args.variant == "w8a8" and args.workload == "block_l16384":
         del ws, out
         torch.cuda.empty_cache()
+        log("extras: 50-block stack, precision series, sequence scaling")
         result["extras"] = extras(S, h3k, torch)
+    result["weight_bytes"] = weight_bytes(wl)
     if not args.no_cpu_baseline and args.variant == "w8a8":
-        result["cpu_baseline"] = cpu_baseline(wl, x, c, bw, args.cpu_rows)
+        log("oracle on the host (cpu_baseline)")
+        cb = cpu_baseline(wl, x, c, bw, args.cpu_rows)
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                     "cpu_model", "seconds")}
+        if args.workload == "block_l16384" and not args.no_extras:
+            log("oracle on the host: other workloads")
+            result["cpu_baselines_other_workloads"] = cpu_baselines(S, h3k, torch, cb, bw)
     print(json.dumps(result))
 
 
@@ -291,6 +465,21 @@ def _time_steps(torch, fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def _median_time(torch, fn, n, warmup=1):
+    """Median over n separately synchronised calls (seconds)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
 def extras(S, h3k, torch):
     """Measurements beside the headline line:
       - the 50-block stack at L=16384: ms per denoising step without and with horizontal
@@ -314,14 +503,30 @@ def extras(S, h3k, torch):
     dims = h3k.dims_of(wl)
     res, sweep, ref = {}, {}, None
     for tr in [(0, 0), wl.tr_range, (5, 45), (15, 35), (20, 30), (0, 50)]:
+        log(f"stack step, pairing {tr}")
         ws = h3k.alloc_workspace(h3k.stack_workspace_bytes(dims, wl.L, *tr))
         y = torch.empty_like(x)
-        t = _time_steps(torch, lambda: h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y), 2, 1)
+        nmed = 5 if tr in ((0, 0), tuple(wl.tr_range)) else 3
+        t = _median_time(torch, lambda: h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y), nmed)
         if tr in ((0, 0), tuple(wl.tr_range)):
             g = h3k.stack_graph(x, c, blocks, dims, tr[0], tr[1], 0, ws, y)
-            tg = _time_steps(torch, g.launch, 2, 1)
+            tg = _median_time(torch, g.launch, 5)
             res["graph_" + ("token_reduction" if tr[1] > tr[0] else "full")] = round(tg * 1e3, 2)
             del g
+        if tr == tuple(wl.tr_range):
+            # one profiled step: per-kernel time of the whole step, and token pairing's bandwidth
+            h3k.profile_enable(True)
+            h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y)
+            torch.cuda.synchronize()
+            prof = h3k.profile_read()
+            h3k.profile_enable(False)
+            step = {k: {"launches": n, "ms": round(tt, 3)} for k, (n, tt) in prof.items() if n}
+            npair = wl.L // 2  # paired tokens
+            for k, rd, wr in (("token_pair", 4 * wl.d, 4 * wl.d), ("token_unpair", 8 * wl.d, 4 * wl.d)):
+                if k in step:
+                    gbs = npair * (rd + wr) / (step[k]["ms"] * 1e-3) / 1e9
+                    step[k].update(bytes=npair * (rd + wr), GBps=round(gbs, 1), frac_of_8TBps=round(gbs / HBM_GBS, 4))
+            out["stack50_l16384_token_reduction_kernels"] = step
         if tr == (0, 0):
             ref = y.float().clone()
             res["full"] = round(t * 1e3, 2)
@@ -354,6 +559,7 @@ def extras(S, h3k, torch):
     del blocks, ref
     torch.cuda.empty_cache()
 
+    log("precision series")
     # precision series (one block, L=16384)
     wl = S.WORKLOADS["block_l16384"]
     bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"), keep_bf16=True)
@@ -362,10 +568,10 @@ def extras(S, h3k, torch):
     dims = h3k.dims_of(wl)
     series = {}
     for name, flags in [("bf16", h3k.F_BF16_GEMM), ("int8_mlp", h3k.F_BF16_QKV | h3k.F_BF16_OUT),
-                        ("int8_mlp_qkv", h3k.F_BF16_OUT), ("w8a8", 0)]:
+                        ("int8_mlp_qkv", h3k.F_BF16_OUT), ("w8a8", 0), ("w8a8_attn_bf16", h3k.F_ATTN_BF16)]:
         ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, wl.L, flags))
         y = torch.empty_like(x)
-        t = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, y), 5, 2)
+        t = _median_time(torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, y), 5, 2)
         series[name] = round(t * 1e3, 3)
         del ws, y
     out["precision_series_l16384_ms"] = series
@@ -378,6 +584,7 @@ def extras(S, h3k, torch):
              65536: (16, 64, 64)}
     scaling, l65536 = {}, None
     for L, grid in grids.items():
+        log(f"sequence scaling L={L}")
         wl = dataclasses.replace(base, name=f"block_l{L}", grid=grid)
         bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"))
         x = S.activations(wl, device="cuda")
@@ -385,18 +592,19 @@ def extras(S, h3k, torch):
         dims = h3k.dims_of(wl)
         ws = h3k.alloc_workspace(h3k.workspace_bytes(dims, L, 0))
         y = torch.empty_like(x)
+        t = _median_time(torch, lambda: h3k.block_forward(x, c, bw, dims, 0, ws, y), 3, 1)
         h3k.profile_enable(True)
-        t = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, 0, ws, y), 3, 1)
+        _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, 0, ws, y), 2, 0)
         prof = h3k.profile_read()
         h3k.profile_enable(False)
         n, tot = prof["attention"]
         attn_ms = tot / n
-        frac = 4.0 * L * L * wl.d / (attn_ms * 1e-3) / 1e12 / PEAK["bf16"]
+        frac = 4.0 * L * L * wl.d / (attn_ms * 1e-3) / 1e12 / PEAK["fp16"]
         scaling[str(L)] = {"ms": round(t * 1e3, 3), "attention_ms": round(attn_ms, 3),
-                           "attention_bf16_frac": round(frac, 4)}
+                           "attention_frac": round(frac, 4)}
         if L == 65536:
             l65536 = {"ms_per_step": round(t * 1e3, 3), "tokens_per_s": round(L / t, 1),
-                      "attention_ms": round(attn_ms, 3), "attention_bf16_frac": round(frac, 4)}
+                      "attention_ms": round(attn_ms, 3), "attention_frac": round(frac, 4)}
         del bw, x, ws, y
         torch.cuda.empty_cache()
     Ls = [float(k) for k in scaling]

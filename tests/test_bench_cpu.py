@@ -69,3 +69,18 @@ def test_committed_traffic_summary_is_well_formed(path):
     att = [k for k in tr["kernels"] if k.startswith("attn_v2_kernel")]
     assert att and tr["kernels"][att[0]]["read_bytes"] > 0
     assert set(tr["copy_factor"]) == {"fetch", "write"}
+
+
+def test_weight_bytes_per_variant():
+    # AdaLN bf16 in every variant; a W8A8 projection: one byte per weight plus a 4-byte
+    # scale per output channel; a bf16 projection: two bytes per weight
+    wl = S.WORKLOADS["block_l16384"]
+    d, F, dc = wl.d, wl.d_ff, wl.d_cond
+    wb = bench.weight_bytes(wl)
+    ada = 6 * d * dc * 2
+    w8 = ada + (3 * d * d + d * d + F * d + d * F) + 4 * (3 * d + d + F + d)
+    b16 = ada + 2 * (3 * d * d + d * d + F * d + d * F)
+    assert wb["w8a8"]["per_block_GiB"] == round(w8 / 2**30, 4)
+    assert wb["bf16"]["per_block_GiB"] == round(b16 / 2**30, 4)
+    assert wb["w8a8"]["per_block_GiB"] < wb["int8_mlp_qkv"]["per_block_GiB"] < \
+        wb["int8_mlp"]["per_block_GiB"] < wb["bf16"]["per_block_GiB"]
