@@ -45,6 +45,11 @@
  *     its 16-bit pattern (uint16); fp32 as IEEE float.
  *   - Calls on different streams are independent only if their outputs and workspaces
  *     are disjoint.
+ *   - Token counts: L (and L / 2 where tokens are paired) must be a multiple of 8, else
+ *     H3K_EUNSUPPORTED: the transposed V rows and the attention's key tiles move 8 tokens
+ *     per 16-byte access. A grid whose product is not a multiple of 8 is padded by the
+ *     caller. Any L that is a multiple of 8 is supported: partial 256-token GEMM tiles and
+ *     partial 64-key attention tiles are masked.
  */
 #ifndef H3K_H
 #define H3K_H
@@ -151,21 +156,31 @@ typedef struct {
   size_t total;                 /* bytes needed (= h3k_workspace_bytes)                */
 } h3k_ws_layout;
 
-/* Per-output-channel int8 weight quantisation of w [n_out, k_in] (device; bf16 or
- * fp32 per w_dtype): scale_out[n] = max_k |w[n,k]| / 127, q_out[n,k] =
+/* Per-output-channel int8 weight quantisation ("맥북에서 AI 영상 생성 모델 돌리기 - MiniMax H3 로컬 실행과 30초 애니메이션 만들기", section "int8 이 뭔가요": one F32
+ * scale per weight output channel; "h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "Int8 양자화": per-output-channel
+ * weight scales) of w [n_out, k_in] (device; bf16 or fp32 per w_dtype):
+ * scale_out[n] = max_k |w[n,k]| / 127, q_out[n,k] =
  * clamp(rint(w[n,k] * (127 / max_k |w[n,k]|)), -127, 127), decisions in fp32.
  * q_out int8 [n_out, k_in], scale_out fp32 [n_out] (device). k_in % 8 == 0. */
 int h3k_quantize_weights(const void *w, int w_dtype, int64_t n_out, int64_t k_in,
                          int8_t *q_out, float *scale_out, void *stream);
 
-/* Workspace bytes one h3k_block_forward call needs for L tokens under `flags`
- * (0 on invalid dims). */
+/* Workspace bytes one h3k_block_forward call needs for L tokens under `flags`: room for
+ * the intermediates of the block the pages describe (see h3k_block_forward). 0 on invalid
+ * dims (the message of h3k_last_error is left as it was). */
 size_t h3k_workspace_bytes(const h3k_dims *dm, int64_t L, uint32_t flags);
 
-/* Fills *out with the workspace layout for (dm, L, flags). Returns H3K_OK or an error. */
+/* Fills *out with the workspace layout for (dm, L, flags) (the intermediates of the block,
+ * see h3k_block_forward). Returns H3K_OK, or H3K_EINVAL / H3K_EUNSUPPORTED for the dims
+ * and flags h3k_block_forward would refuse. */
 int h3k_workspace_layout(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *out);
 
-/* One DiT block forward. x_in, x_out: [L, d] bf16 (fp32 under H3K_F_FP32_DEBUG),
+/* One DiT block forward: the equations at the top of this file, i.e. the gated AdaLN with
+ * the activation quantisers folded in, W8A8 QKV with per-output-channel weight scales and
+ * RoPE routed into head-major attention inputs, attention, and the W8A8 out-projection and
+ * MLP with gated residuals ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", sections "Int8 양자화" and "Metal 4 및 TensorOps";
+ * "MiniMax-H3在Apple Silicon上的兩種推理實現工程取舍", section 性能上限).
+ * x_in, x_out: [L, d] bf16 (fp32 under H3K_F_FP32_DEBUG),
  * device; x_out may alias x_in. cond: fp32 [d_cond] device. w: host pointer to a struct
  * of device pointers. L == grid_t*grid_h*grid_w. ws: device workspace of at least
  * h3k_workspace_bytes(dm, L, flags) bytes; after the call it holds the intermediates at
@@ -189,7 +204,8 @@ int h3k_block_forward_noalloc(const void *x_in, void *x_out, const float *cond,
                               const h3k_block_weights *w, const h3k_dims *dm, int64_t L,
                               uint32_t flags, void *stream);
 
-/* One block on an explicit token grid (T, Hg, Wg) whose w positions are
+/* One block on an explicit token grid ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", the "속도 및 품질 트레이드오프" table: token
+ * reduction pairs horizontal tokens in the middle blocks) (T, Hg, Wg) whose w positions are
  * w * w_pos_scale + w_pos_offset in RoPE; dm's own grid fields are ignored and
  * L = T*Hg*Wg. This is the call the stack makes for its horizontally paired middle
  * blocks (T, Hg, Wg/2 with scale 2 and offset 0.5); h3k_block_forward is the case
@@ -219,11 +235,13 @@ int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t 
                   uint32_t flags, void *stream);
 
 /* Workspace bytes for h3k_stack_forward (block workspace plus two reduced-token
- * buffers when tr_begin < tr_end). */
+ * buffers when tr_begin < tr_end). 0 on invalid dims. */
 size_t h3k_stack_workspace_bytes(const h3k_dims *dm, int64_t L, int32_t tr_begin,
                                  int32_t tr_end, uint32_t flags);
 
-/* A stack of n_blocks blocks sharing cond; blocks: host array of n_blocks weight structs.
+/* A stack of n_blocks blocks sharing cond ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론": the DiT runs 50 blocks per denoising
+ * step, section "고성능 추론 프리셋"; token reduction pairs horizontal tokens in the middle
+ * blocks, the "속도 및 품질 트레이드오프" table); blocks: host array of n_blocks weight structs.
  * Blocks [tr_begin, tr_end) run on horizontally paired tokens: before tr_begin,
  * xr[t,h,j] = (x[t,h,2j] + x[t,h,2j+1]) / 2 on the (T, Hg, Wg/2) grid with w positions
  * 2j + 0.5; after tr_end - 1, x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out - xr_in)[t,h,j].
@@ -290,12 +308,15 @@ void h3k_graph_destroy(h3k_graph *graph);
 
 /* ---- single steps of the block (the same kernels the block call launches) ---- */
 
-/* m[i] = sum_j w_ada[i, j] * cond[j], fp32 accumulation. w_ada bf16 [n_out, d_cond],
+/* The gated AdaLN's modulation ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "Int8 양자화"; "MiniMax-H3在Apple Silicon上的
+ * 兩種推理實現工程取舍", section 性能上限: AdaLN gating):
+ * m[i] = sum_j w_ada[i, j] * cond[j], fp32 accumulation. w_ada bf16 [n_out, d_cond],
  * cond fp32 [d_cond], m fp32 [n_out]; device. d_cond % 8 == 0, d_cond <= 8192. */
 int h3k_adaln_modulation(const uint16_t *w_ada, const float *cond, float *m,
                          int64_t n_out, int32_t d_cond, void *stream);
 
-/* Per row l of x [rows, cols] (x_dtype): h = LN(x_l)(1 + scale) + shift in fp32,
+/* The gated AdaLN with its activation quantiser folded in ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "Int8 양자화"):
+ * per row l of x [rows, cols] (x_dtype): h = LN(x_l)(1 + scale) + shift in fp32,
  * then per-row int8 quantisation of h: q_out int8 [rows, cols], s_out fp32 [rows].
  * shift, scale: fp32 [cols]. cols % 256 == 0, cols <= 8192. */
 int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift,
@@ -309,26 +330,31 @@ int h3k_ln_modulate_quant(const void *x, int x_dtype, const float *shift,
 int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols,
                      int8_t *q_out, float *s_out, void *stream);
 
-/* The int8 GEMM main loop with a raw epilogue: c[m, n] = sum_k a[m, k] * b[n, k] in
+/* The int8 GEMM of the W8A8 projections ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", section "Int8 양자화": native int8 MLP and
+ * QKV) with a raw epilogue: c[m, n] = sum_k a[m, k] * b[n, k] in
  * int32 (exact). a int8 [M, K], b int8 [N, K], c int32 [M, N]; device. N % 256 == 0,
  * K % 128 == 0, M >= 1. */
 int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream);
 
-/* Horizontal pairing of x [T*Hg*Wg, d] (x_dtype) into xr and xr_copy
+/* Token reduction ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", the "속도 및 품질 트레이드오프" table: horizontal video tokens
+ * paired in the middle blocks): horizontal pairing of x [T*Hg*Wg, d] (x_dtype) into xr and xr_copy
  * [T*Hg*(Wg/2), d]: xr[t,h,j] = (x[t,h,2j] + x[t,h,2j+1]) / 2 (fp32 add, rounded once). */
 int h3k_token_pair(const void *x, void *xr, void *xr_copy, int x_dtype, int32_t T,
                    int32_t Hg, int32_t Wg, int32_t d, void *stream);
 
-/* x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out[t,h,j] - xr_in[t,h,j]) for s in {0,1},
+/* The end of token reduction (same passage): both members of each pair receive the
+ * reduced blocks' update, x[t,h,2j+s] = x_pre[t,h,2j+s] + (xr_out[t,h,j] - xr_in[t,h,j]) for s in {0,1},
  * in place on x_pre (fp32 arithmetic, rounded once). */
 int h3k_token_unpair(void *x_pre, const void *xr_out, const void *xr_in, int x_dtype,
                      int32_t T, int32_t Hg, int32_t Wg, int32_t d, void *stream);
 
-/* Thread-local message describing the last failed call on this thread ("" if none). */
+/* Thread-local message describing the last failed call on this thread ("" if none).
+ * Plumbing of this library (no counterpart on the pages). */
 const char *h3k_last_error(void);
 
-/* ---- profiling: per-kernel HIP event timing inside block and stack calls ---- */
+/* ---- profiling: per-kernel HIP event timing inside block and stack calls (plumbing of
+ * this library, for the per-kernel measurements; no counterpart on the pages) ---- */
 enum {
   H3K_K_ADALN = 0, H3K_K_ROPE_TABLE, H3K_K_LN_QUANT, H3K_K_GEMM_QKV, H3K_K_ATTENTION,
   H3K_K_ROWQUANT_O, H3K_K_GEMM_O, H3K_K_GEMM_UP, H3K_K_ROWQUANT_G, H3K_K_GEMM_DOWN,

@@ -301,3 +301,22 @@ def test_noalloc_validation():
     src = open(HEADER).read()
     assert re.search(r"#define H3K_NOALLOC_MAX_BYTES \(64u << 20\)", src)
     assert h3k.NOALLOC_MAX_BYTES == 64 << 20
+
+
+def test_token_count_rule():
+    """L must be a multiple of 8 (refused with a message naming the rule); any such L is
+    accepted, including ones that leave partial 256-token GEMM tiles and partial key tiles."""
+    dm = tiny_dims(grid=(1, 1, 6))
+    assert _block(dm, 6) == h3k.EUNSUPPORTED and "multiple of 8" in h3k.last_error()
+    for grid in [(1, 1, 8), (3, 5, 8), (2, 3, 12), (1, 9, 40)]:  # 8, 120, 72, 360 tokens
+        dm = tiny_dims(grid=grid)
+        L = grid[0] * grid[1] * grid[2]
+        assert h3k.workspace_bytes(dm, L, 0) > 0
+    lib = h3k.lib()
+    assert lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, 2, 60, 64, 0.1, h3k.DT_F16, 0, None) == h3k.EUNSUPPORTED
+    assert "multiple of 8" in h3k.last_error()
+    # pairing needs L / 2 a multiple of 8 as well
+    arr = (h3k.BlockWeightsC * 2)(*[h3k.BlockWeightsC(*([FAKE] * 9 + [None] * 4)) for _ in range(2)])
+    dm = tiny_dims(grid=(1, 3, 8))  # 24 tokens, 12 after pairing
+    rc = lib.h3k_stack_forward(FAKE, FAKE, FAKE, arr, 2, C.byref(dm), 24, 0, 1, 0, FAKE, 1 << 40, None)
+    assert rc == h3k.EUNSUPPORTED and "L/2" in h3k.last_error()
