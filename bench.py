@@ -251,6 +251,10 @@ def main():
                     help="skip sampling the engine clock under load (profiled runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB on the device twice (counter calibration) and exit")
+    ap.add_argument("--stack-step", action="store_true",
+                    help="time the 50-block stack step (L=16384, token pairing in the middle blocks) "
+                         "instead of one block: warm-up, plain and event-timed loops as for a block "
+                         "(for profiling the whole step); prints its own JSON line")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured with rocprofv3 counters")
     args = ap.parse_args()
@@ -277,6 +281,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 2}))
+        return
+    if args.stack_step:
+        stack_step(args, S, h3k, torch)
         return
     wl = S.WORKLOADS[args.workload]
     flags = {"w8a8": 0, "w8a8_attn_bf16": h3k.F_ATTN_BF16, "bf16gemm": h3k.F_BF16_GEMM,
@@ -408,6 +415,40 @@ def main():
             log("oracle on the host: other workloads")
             result["cpu_baselines_other_workloads"] = cpu_baselines(S, h3k, torch, cb, bw)
     print(json.dumps(result))
+
+
+def stack_step(args, S, h3k, torch):
+    """The 50-block W8A8 stack at L=16384 with horizontal token pairing in its middle
+    blocks, run as `warmup` untimed steps, `steps` timed steps and `steps` steps with the
+    library's event records (the loop structure of the block measurement, so one profile
+    summary reads both)."""
+    wl = S.WORKLOADS["stack50_l16384"]
+    tr = tuple(wl.tr_range)
+    blocks = []
+    for b in range(wl.n_blocks):
+        wb = S.block_weights_bf16(wl, b, device="cuda")
+        blocks.append(h3k.quantize_block(wb))
+        del wb
+    x = S.activations(wl, device="cuda")
+    c = S.conditioning(wl, device="cuda")
+    dims = h3k.dims_of(wl)
+    ws = h3k.alloc_workspace(h3k.stack_workspace_bytes(dims, wl.L, *tr))
+    y = torch.empty_like(x)
+    step = lambda: h3k.stack_forward(x, c, blocks, dims, tr[0], tr[1], 0, ws, y)  # noqa: E731
+    log(f"stack step {wl.name} pairing {tr}: {args.warmup} warm-up and {args.steps} timed steps")
+    t = _time_steps(torch, step, args.steps, args.warmup)
+    h3k.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = h3k.profile_read()
+    h3k.profile_enable(False)
+    kern = {k: {"launches_per_step": n / args.steps, "ms_per_step": round(tt / args.steps, 3)}
+            for k, (n, tt) in prof.items() if n}
+    print(json.dumps({"metric": f"ms per denoising step ({wl.n_blocks} W8A8 blocks, L={wl.L}, "
+                                f"token pairing in blocks [{tr[0]},{tr[1]}))",
+                      "value": round(t * 1e3, 2), "unit": "ms", "steps": args.steps,
+                      "warmup": args.warmup, "higher_is_better": False, "kernels": kern}))
 
 
 def measured_traffic(path, workload, kernel):

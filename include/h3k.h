@@ -93,7 +93,10 @@ enum {
    * attention runs on fp16 matrix-core operands (P rounded to fp16), with O stored as fp16
    * for its int8 quantiser (bf16 when H3K_F_BF16_OUT consumes it). This flag stores Q, K,
    * V, P and O as bf16 instead (the same instruction rate and bytes, 8 significant bits
-   * instead of 11). Not combinable with H3K_F_FP32_DEBUG. */
+   * instead of 11). fp16 holds magnitudes up to 65504: an element of Q * log2(e)/sqrt(Dh),
+   * K or V beyond that is stored as +-inf and the rows of attention it touches are not
+   * finite; such data takes this flag (bf16 has the fp32 range). Not combinable with
+   * H3K_F_FP32_DEBUG. */
   H3K_F_ATTN_BF16 = 64u,
   /* h3k_attention only: q carries the base-2 softmax scale (see h3k_attention) */
   H3K_F_Q_BASE2 = 128u

@@ -121,6 +121,15 @@ def test_attention_twin_layouts_bruteforce(dtype):
     assert np.array_equal(o, store(o))
     assert np.max(np.abs(o - store(ref)) / np.abs(ref)) <= ulp
     assert np.allclose(o, ref, rtol=ulp / 2 * 1.0001, atol=0)
+    # base-2 logits: q carrying scale * log2(e) gives the same attention (16-bit dtypes only)
+    ob = np.zeros((n, h * dh))
+    rc = R.h3k_ref_attention(q * (scale * math.log2(math.e)), k, v, ob, h, n, dh, scale, dtype, R.F_Q_BASE2)
+    if dtype == R.DT_F32:
+        assert rc == R.EINVAL
+    else:
+        assert rc == R.OK
+        assert np.array_equal(ob, store(ob))
+        assert np.max(np.abs(ob - store(ref)) / np.abs(ref)) <= ulp
     assert R.h3k_ref_attention(q, k, v, o, h, n, dh, 0.0, dtype, 0) == R.EINVAL
     assert R.h3k_ref_attention(q, k, v, o, h, n + 1, dh, scale, dtype, 0) == R.EINVAL
     assert R.h3k_ref_attention(q, k, v, o, h, n, dh, scale, 9, 0) == R.EINVAL

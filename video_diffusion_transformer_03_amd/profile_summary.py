@@ -10,13 +10,13 @@ Reads the CSV files rocprofv3 writes (`--output-format csv`):
     KiB per dispatch);
   - the same two counters on a plain device copy of known size (bench.py --copy-calibration: 2 x 1 GiB),
     which gives the factor each counter's KiB must be scaled by to read true bytes.
-Writes `profiles/kernels_<workload>.txt` (durations, HBM bytes per launch) and
-`profiles/traffic.json` (per-kernel HBM bytes per launch, with a hash of the kernel sources
+Writes `profiles/kernels_<name>.txt` (durations, time per step, HBM bytes per launch;
+<name> defaults to the workload) and, unless --no-traffic, `profiles/traffic.json` (per-kernel HBM bytes per launch, with a hash of the kernel sources
 so a later change to a kernel marks its numbers stale).
 
 With --sq DIR (a `--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY
 SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE` run of the same command)
-it also writes `profiles/sq_<workload>.txt`: per kernel the fraction of SIMD cycles the matrix
+it also writes `profiles/sq_<name>.txt`: per kernel the fraction of SIMD cycles the matrix
 cores were busy, the fraction of wave time spent waiting, LDS bank-conflict cycles per LDS
 instruction and LDS-active cycles per CU cycle.
 """
@@ -91,21 +91,32 @@ def _one(pattern: str) -> str:
 
 
 def kernel_stats(d: str, steps: int, warmup: int):
-    """{kernel: (calls, mean ns over the timed dispatches, total ns)} from the per-dispatch
-    trace. The profiled command runs `warmup` untimed steps first; a kernel launched n times
-    in all is averaged over its last n * steps / (steps + warmup) dispatches, the ones of the
-    timed steps (kernels launched once outside the steps are averaged over all)."""
+    """{(kernel, grid threads): (calls, mean ns over the timed dispatches, total ns, outside
+    the steps?)} from the per-dispatch trace (one kernel launched on several grid sizes,
+    such as a row quantiser used on weights and on activations, counts once per size).
+    The profiled bench runs `warmup` untimed steps, then `steps` plain steps and `steps`
+    steps with event records (2 * steps timed steps in all); every step starts with the
+    AdaLN kernel. A kernel launched k times per step (k * (warmup + 2 * steps) dispatches
+    from the first AdaLN launch on) is averaged over its last k * 2 * steps dispatches; any
+    other kernel (set-up work such as weight quantisation) over all of its dispatches,
+    flagged True."""
     per = defaultdict(list)
     for r in csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))):
-        per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]),
-                                      int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        per[(r["Kernel_Name"], str(grid))].append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    starts = [t for (name, _), v in per.items() if "adaln_kernel" in name for t, _ in v]
+    t0 = min(starts) if starts else -1
+    per_cmd = warmup + 2 * steps
     out = {}
-    for name, v in per.items():
+    for key, v in per.items():
         v.sort()
         n = len(v)
-        timed = n * steps // (steps + warmup) if n % (steps + warmup) == 0 else n
+        n_in = sum(1 for t, _ in v if t >= t0)
+        whole = n_in == 0 or n_in % per_cmd != 0
+        timed = n if whole else n_in // per_cmd * 2 * steps
         durs = [t for _, t in v[n - timed:]]
-        out[name] = (n, sum(durs) / len(durs), float(sum(t for _, t in v)))
+        out[key] = (n_in if not whole else n, sum(durs) / len(durs), float(sum(t for _, t in v)), whole)
     return out
 
 
@@ -134,13 +145,18 @@ def main():
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--steps", type=int, required=True, help="timed steps of the profiled run")
+    ap.add_argument("--steps", type=int, required=True, help="--steps of the profiled bench run")
     ap.add_argument("--warmup", type=int, default=2, help="untimed steps before them")
     ap.add_argument("--cmd", required=True, help="the command lines that produced the inputs")
     ap.add_argument("--out", default="profiles")
+    ap.add_argument("--name", default=None,
+                    help="file-name tag of the summaries (default: the workload name)")
+    ap.add_argument("--no-traffic", action="store_true",
+                    help="do not write traffic.json (a variant of the measured workload)")
     ap.add_argument("--sq", default=None, help="directory of the SQ counter run (optional)")
     ap.add_argument("--sq-cmd", default="", help="the command line of the SQ counter run")
     a = ap.parse_args()
+    a.name = a.name or a.workload
 
     stats = kernel_stats(a.ktrace, a.steps, a.warmup)
     fetch = counter_by_kernel(a.fetch, "FETCH_SIZE")
@@ -151,29 +167,36 @@ def main():
     lines = [f"# Kernel durations and HBM traffic per launch, workload {a.workload}", "",
              "Commands:", *[f"    {c}" for c in a.cmd.split(" ;; ")], "",
              f"Copy calibration (plain 1 GiB device copy): FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {fw:.3f}", "",
-             f"Durations: mean over the dispatches of the {a.steps} timed steps ({a.warmup} warm-up steps excluded).", "",
-             f"{'kernel':58s} {'calls':>6s} {'avg us':>10s} {'read MB':>9s} {'write MB':>9s}"]
+             f"Durations: mean over the dispatches of the bench's 2 x {a.steps} timed steps (plain and event-timed "
+             f"loops; its {a.warmup} warm-up steps excluded); * = launched outside the steps, mean of all dispatches.", "",
+             f"{'kernel':58s} {'calls':>6s} {'avg us':>10s} {'ms/step':>9s} {'read MB':>9s} {'write MB':>9s}"]
     traffic = {"workload": a.workload, "copy_factor": {"fetch": ff, "write": fw},
                "sources": {f: source_hash(f) for f, _ in KINDS.values()}, "kernels": {}}
     rows = []
-    for name, (calls, avg_ns, tot_ns) in stats.items():
+    grids = defaultdict(int)
+    for name, _ in stats:
+        grids[name] += 1
+    for (name, grid), (calls, avg_ns, tot_ns, whole) in stats.items():
         if not is_ours(name):
             continue
-        f_kib = [v for (k, _), v in fetch.items() if k == name]
-        w_kib = [v for (k, _), v in write.items() if k == name]
-        rd = max(f_kib) * 1024 * ff if f_kib else float("nan")
-        wr = max(w_kib) * 1024 * fw if w_kib else float("nan")
-        rows.append((tot_ns, name, calls, avg_ns, rd, wr))
-    for tot_ns, name, calls, avg_ns, rd, wr in sorted(rows, reverse=True):
-        lines.append(f"{short_name(name)[:58]:58s} {calls:6d} {avg_ns / 1e3:10.1f} {rd / 1e6:9.1f} {wr / 1e6:9.1f}")
+        rd = fetch.get((name, grid), float("nan")) * 1024 * ff
+        wr = write.get((name, grid), float("nan")) * 1024 * fw
+        rows.append((tot_ns, name, grid, calls, avg_ns, rd, wr, whole))
+    for tot_ns, name, grid, calls, avg_ns, rd, wr, whole in sorted(rows, reverse=True):
+        sfx = (f" [{grid}]" if grids[name] > 1 else "") + (" *" if whole else "")
+        label = short_name(name)[:58 - len(sfx)] + sfx
+        # launches per step x mean duration (kernels launched outside the steps: blank)
+        per_step = "" if whole else f"{calls / (a.warmup + 2 * a.steps) * avg_ns / 1e6:9.3f}"
+        lines.append(f"{label:58s} {calls:6d} {avg_ns / 1e3:10.1f} {per_step:>9s} {rd / 1e6:9.1f} {wr / 1e6:9.1f}")
         for kind, (src, key) in KINDS.items():
             if key in name:
                 traffic["kernels"].setdefault(short_name(name), {"kind": kind, "source": src,
                                                                  "read_bytes": rd, "write_bytes": wr,
                                                                  "avg_us": avg_ns / 1e3})
     os.makedirs(a.out, exist_ok=True)
-    open(os.path.join(a.out, f"kernels_{a.workload}.txt"), "w").write("\n".join(lines) + "\n")
-    json.dump(traffic, open(os.path.join(a.out, "traffic.json"), "w"), indent=1)
+    open(os.path.join(a.out, f"kernels_{a.name}.txt"), "w").write("\n".join(lines) + "\n")
+    if not a.no_traffic:
+        json.dump(traffic, open(os.path.join(a.out, "traffic.json"), "w"), indent=1)
     print("\n".join(lines))
     if a.sq:
         sq_summary(a)
@@ -204,7 +227,7 @@ def sq_summary(a):
         rows.append((cyc, name, mfma, wait, confl, ldsa))
     for cyc, name, mfma, wait, confl, ldsa in sorted(rows, reverse=True):
         lines.append(f"{short_name(name)[:58]:58s} {mfma:10.3f} {wait:10.3f} {confl:15.3f} {ldsa:11.3f}")
-    open(os.path.join(a.out, f"sq_{a.workload}.txt"), "w").write("\n".join(lines) + "\n")
+    open(os.path.join(a.out, f"sq_{a.name}.txt"), "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
