@@ -427,7 +427,7 @@ def stack_step(args, S, h3k, torch):
     blocks = []
     for b in range(wl.n_blocks):
         wb = S.block_weights_bf16(wl, b, device="cuda")
-        blocks.append(h3k.quantize_block(wb))
+        blocks.append(h3k.quantize_block(wb, rowmajor=False))
         del wb
     x = S.activations(wl, device="cuda")
     c = S.conditioning(wl, device="cuda")
@@ -537,7 +537,7 @@ def extras(S, h3k, torch):
     blocks = []
     for b in range(wl.n_blocks):
         wb = S.block_weights_bf16(wl, b, device="cuda")
-        blocks.append(h3k.quantize_block(wb))
+        blocks.append(h3k.quantize_block(wb, rowmajor=False))
         del wb
     x = S.activations(wl, device="cuda")
     c = S.conditioning(wl, device="cuda")
@@ -627,7 +627,7 @@ def extras(S, h3k, torch):
     for L, grid in grids.items():
         log(f"sequence scaling L={L}")
         wl = dataclasses.replace(base, name=f"block_l{L}", grid=grid)
-        bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"))
+        bw = h3k.quantize_block(S.block_weights_bf16(wl, 0, device="cuda"), rowmajor=False)
         x = S.activations(wl, device="cuda")
         c = S.conditioning(wl, device="cuda")
         dims = h3k.dims_of(wl)

@@ -133,6 +133,13 @@ typedef struct {
   const uint16_t *wb_o;
   const uint16_t *wb_up;
   const uint16_t *wb_down;
+  const int8_t *wt_qkv;    /* optional: the same int8 codes in the tiled layout of
+                              h3k_tile_weights. When set, that W8A8 projection reads
+                              these (a faster kernel) and its row-major w_* may be NULL;
+                              results are bit-identical either way                    */
+  const int8_t *wt_o;
+  const int8_t *wt_up;
+  const int8_t *wt_down;
 } h3k_block_weights;
 
 /* Byte offsets of the intermediates inside a block workspace (for inspection). Arrays
@@ -339,6 +346,19 @@ int h3k_row_quantize(const void *x, int x_dtype, int64_t rows, int32_t cols,
  * K % 128 == 0, M >= 1. */
 int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream);
+
+/* Layout change of int8 weights q [n_out, k_in] (row-major, e.g. from
+ * h3k_quantize_weights) into q_tiled (same byte count), the operand order of the block's
+ * W8A8 GEMMs: 16 x 64 tiles (16 output channels x 64 bytes of K), tile (nb, kb) at byte
+ * 1024 (nb (k_in / 64) + kb), and inside a tile lane l's 16 bytes at 16 l: channel
+ * 16 nb + l % 16, bytes 64 kb + 16 (l / 16) .. + 15. A permutation: nothing is computed.
+ * q, q_tiled device, not overlapping; n_out % 16 == 0, k_in % 64 == 0. */
+int h3k_tile_weights(const int8_t *q, int64_t n_out, int64_t k_in, int8_t *q_tiled, void *stream);
+
+/* h3k_gemm_i8_i32 with b given in the tiled layout of h3k_tile_weights (the kernel the
+ * block uses for tiled weights). Same result, sizes and errors. */
+int h3k_gemm_i8_i32_tiled(const int8_t *a, const int8_t *b_tiled, int32_t *c, int64_t M,
+                          int64_t N, int64_t K, void *stream);
 
 /* Token reduction ("h3-metal: Apple Silicon을 위한 네이티브 MiniMax-H3 추론", the "속도 및 품질 트레이드오프" table: horizontal video tokens
  * paired in the middle blocks): horizontal pairing of x [T*Hg*Wg, d] (x_dtype) into xr and xr_copy

@@ -115,6 +115,8 @@ def _block(dm, L, flags=0, x=FAKE, out=FAKE, cond=FAKE, ws=FAKE, ws_bytes=1 << 4
     (dict(flags=h3k.F_BF16_MLP | h3k.F_FP32_DEBUG), h3k.EUNSUPPORTED),
     (dict(flags=256), h3k.EINVAL),                              # unknown flag bit
     (dict(flags=h3k.F_ATTN_BF16 | h3k.F_FP32_DEBUG), h3k.EUNSUPPORTED),
+    # a W8A8 projection with neither row-major nor tiled codes
+    (dict(w=h3k.BlockWeightsC(*([FAKE] * 3 + [None] + [FAKE] * 5 + [None] * 8))), h3k.EINVAL),
 ])
 def test_block_validation(case, code):
     dm = tiny_dims(**case.pop("dm", {}))
@@ -149,6 +151,15 @@ def test_component_validation():
     assert lib.h3k_quantize_weights(None, h3k.DT_BF16, 4, 8, FAKE, FAKE, None) == h3k.EINVAL
     assert lib.h3k_gemm_i8_i32(FAKE, FAKE, FAKE, 16, 100, 128, None) == h3k.EUNSUPPORTED
     assert lib.h3k_gemm_i8_i32(FAKE, FAKE, FAKE, 0, 256, 128, None) == h3k.EINVAL
+    assert lib.h3k_gemm_i8_i32_tiled(FAKE, FAKE, FAKE, 16, 100, 128, None) == h3k.EUNSUPPORTED
+    assert lib.h3k_gemm_i8_i32_tiled(FAKE, FAKE, FAKE, 16, 256, 96, None) == h3k.EUNSUPPORTED
+    assert lib.h3k_gemm_i8_i32_tiled(FAKE, None, FAKE, 16, 256, 128, None) == h3k.EINVAL
+    other = FAKE + (1 << 20)
+    assert lib.h3k_tile_weights(FAKE, 24, 64, other, None) == h3k.EINVAL     # n_out % 16
+    assert lib.h3k_tile_weights(FAKE, 16, 100, other, None) == h3k.EINVAL    # k_in % 64
+    assert lib.h3k_tile_weights(FAKE, 16, 64, FAKE + 512, None) == h3k.EINVAL  # overlap
+    assert lib.h3k_tile_weights(FAKE + 8, 16, 64, other, None) == h3k.EINVAL   # misaligned
+    assert lib.h3k_tile_weights(None, 16, 64, other, None) == h3k.EINVAL
     att = lambda *a: lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, *a, None)  # noqa: E731
     assert att(4, 64, 96, 0.1, h3k.DT_F16, 0) == h3k.EUNSUPPORTED          # head_dim
     assert att(4, 60, 64, 0.1, h3k.DT_BF16, 0) == h3k.EUNSUPPORTED         # L % 8

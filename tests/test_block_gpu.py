@@ -120,6 +120,29 @@ def test_block_zero_gates_identity(flags):
     assert torch.equal(r["out"], r["x"])
 
 
+@pytest.mark.parametrize("name,flags", [("tiny", 0), ("tiny", h3k.F_FP32_DEBUG), ("tiny", h3k.F_ATTN_BF16),
+                                        ("tiny", h3k.F_BF16_OUT), ("tiny", h3k.F_BF16_QKV | h3k.F_BF16_OUT),
+                                        ("ragged", 0), ("ragged", h3k.F_FP32_DEBUG)])
+def test_block_tiled_weights_bitwise(name, flags):
+    """Tiled weights (the one-wave-per-SIMD GEMM) and row-major weights (the ping-pong GEMM)
+    give bit-identical blocks: both accumulate exactly in int32 and share the epilogues."""
+    wl = S.WORKLOADS["tiny"] if name == "tiny" else _wl("block_l4096", grid=(2, 36, 40))
+    gen = "cpu" if name == "tiny" else "cuda"
+    wb = {k: v.to("cuda") for k, v in S.block_weights_bf16(wl, 0, device=gen).items()}
+    keep = bool(flags & BF16_ANY)
+    bw_t = h3k.quantize_block(wb, keep_bf16=keep, tiled=True, rowmajor=False)
+    bw_r = h3k.quantize_block(wb, keep_bf16=keep, tiled=False, rowmajor=True)
+    assert bw_t.w_qkv is None and bw_r.wt_qkv is None
+    xdt = torch.float32 if flags & h3k.F_FP32_DEBUG else torch.bfloat16
+    x = S.activations(wl, device=gen).to("cuda").to(xdt)
+    c = S.conditioning(wl, device=gen).to("cuda")
+    dims = h3k.dims_of(wl)
+    out_t = h3k.block_forward(x, c, bw_t, dims, flags)
+    out_r = h3k.block_forward(x, c, bw_r, dims, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out_r)
+
+
 def test_block_inplace_and_deterministic():
     wl = S.WORKLOADS["tiny"]
     r = run_gpu(wl)

@@ -115,6 +115,45 @@ def test_gemm_i8_extremes():
     assert np.array_equal(c.astype(np.int64), O.int8_matmul(a.numpy(), b.numpy()))
 
 
+# ----------------------------------------------------------------------------- tiled weights
+def _tiled_ref(b: np.ndarray) -> np.ndarray:
+    """The tiled layout written out with numpy: tile (nb, kb) holds, at 16 l, the 16 bytes of
+    channel 16 nb + l % 16 at K bytes 64 kb + 16 (l // 16); tiles nb-major."""
+    N, K = b.shape
+    return b.reshape(N // 16, 16, K // 64, 4, 16).transpose(0, 2, 3, 1, 4).reshape(N, K)
+
+
+@pytest.mark.parametrize("N,K", [(16, 64), (48, 192), (256, 5120), (5120, 20480)])
+def test_tile_weights_layout(N, K):
+    g = _gen(N + K)
+    b = torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8)
+    t = h3k.tile_weights(b.cuda()).cpu().numpy()
+    assert np.array_equal(t, _tiled_ref(b.numpy()))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (100, 768, 640), (1000, 512, 5120),
+                                   (4096, 1536, 1024), (333, 256, 20480),
+                                   (4100, 4352, 256), (8200, 4096, 128)])
+def test_gemm_i8_tiled_exact(M, N, K):
+    """The one-wave-per-SIMD kernel on tiled weights: exact int32, ragged last M-tile, odd
+    and single stage counts (K = 640, 128), more tiles than compute units."""
+    g = _gen(M * 5 + N)
+    a = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int8)
+    b = torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8)
+    c = h3k.gemm_i8_i32_tiled(a.cuda(), h3k.tile_weights(b.cuda())).cpu().numpy()
+    assert np.array_equal(c.astype(np.int64), O.int8_matmul(a.numpy(), b.numpy()))
+
+
+def test_gemm_i8_tiled_extremes():
+    K = 20480
+    a = torch.full((17, K), -127, dtype=torch.int8)
+    b = torch.full((256, K), 127, dtype=torch.int8)
+    b[1, ::2] = -127
+    c = h3k.gemm_i8_i32_tiled(a.cuda(), h3k.tile_weights(b.cuda())).cpu().numpy()
+    assert np.all(c[:, 0] == -127 * 127 * K) and np.all(c[:, 1] == 0)
+    assert np.array_equal(c.astype(np.int64), O.int8_matmul(a.numpy(), b.numpy()))
+
+
 # ----------------------------------------------------------------------------- attention
 # unit roundoff (half the spacing above 1) of the 16-bit types
 U16 = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}

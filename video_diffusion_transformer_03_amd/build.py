@@ -25,7 +25,10 @@ FLAGS = [
 # Per-source flags. Attention takes row maxima of matrix-core results, which the compiler
 # would otherwise quiet (a self-max per value, against signalling NaNs) before each max;
 # its inputs are finite and -inf is still honoured.
-EXTRA = {"k_attn.hip": ["-fno-honor-nans"]}
+# The GEMM epilogues are shared by two GEMM kernels whose results must agree bit for bit;
+# contraction of a * b + c into one rounding is decided per source expression (not by the
+# backend, where the choice can depend on the surrounding kernel).
+EXTRA = {"k_attn.hip": ["-fno-honor-nans"], "k_gemm.hip": ["-ffp-contract=on"]}
 
 
 def _compile(src: str, build_dir: str) -> str:

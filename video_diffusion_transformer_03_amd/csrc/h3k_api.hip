@@ -169,22 +169,22 @@ int check_weights(const char *fn, const h3k_block_weights *w, uint32_t flags) {
   if (p.qkv) {
     H3K_CHECK_PTR(w->wb_qkv);
   } else {
-    H3K_CHECK_PTR(w->w_qkv);
+    if (!w->w_qkv && !w->wt_qkv) return fail(H3K_EINVAL, "%s: w_qkv and wt_qkv are both NULL", fn);
     H3K_CHECK_PTR(w->s_qkv);
   }
   if (p.out) {
     H3K_CHECK_PTR(w->wb_o);
   } else {
-    H3K_CHECK_PTR(w->w_o);
+    if (!w->w_o && !w->wt_o) return fail(H3K_EINVAL, "%s: w_o and wt_o are both NULL", fn);
     H3K_CHECK_PTR(w->s_o);
   }
   if (p.mlp) {
     H3K_CHECK_PTR(w->wb_up);
     H3K_CHECK_PTR(w->wb_down);
   } else {
-    H3K_CHECK_PTR(w->w_up);
+    if (!w->w_up && !w->wt_up) return fail(H3K_EINVAL, "%s: w_up and wt_up are both NULL", fn);
     H3K_CHECK_PTR(w->s_up);
-    H3K_CHECK_PTR(w->w_down);
+    if (!w->w_down && !w->wt_down) return fail(H3K_EINVAL, "%s: w_down and wt_down are both NULL", fn);
     H3K_CHECK_PTR(w->s_down);
   }
   return H3K_OK;
@@ -267,6 +267,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.qkv;
     a.A = p.qkv ? (const void *)at<uint16_t>(ws, lay.h) : (const void *)at<int8_t>(ws, lay.qa);
     a.B = p.qkv ? (const void *)w->wb_qkv : (const void *)w->w_qkv;
+    a.Bt = p.qkv ? nullptr : w->wt_qkv;
     a.N = 3 * d;
     a.K = d;
     a.sa = at<float>(ws, lay.s_a);
@@ -310,6 +311,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.out;
     a.A = p.out ? (const void *)at<uint16_t>(ws, lay.o) : (const void *)at<int8_t>(ws, lay.qo);
     a.B = p.out ? (const void *)w->wb_o : (const void *)w->w_o;
+    a.Bt = p.out ? nullptr : w->wt_o;
     a.N = d;
     a.K = d;
     a.sa = at<float>(ws, lay.s_o);
@@ -337,6 +339,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.mlp;
     a.A = p.mlp ? (const void *)at<uint16_t>(ws, lay.h2) : (const void *)at<int8_t>(ws, lay.qa2);
     a.B = p.mlp ? (const void *)w->wb_up : (const void *)w->w_up;
+    a.Bt = p.mlp ? nullptr : w->wt_up;
     a.N = F;
     a.K = d;
     a.sa = at<float>(ws, lay.s_a2);
@@ -360,6 +363,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.mlp;
     a.A = p.mlp ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
     a.B = p.mlp ? (const void *)w->wb_down : (const void *)w->w_down;
+    a.Bt = p.mlp ? nullptr : w->wt_down;
     a.N = d;
     a.K = F;
     a.sa = at<float>(ws, lay.s_g);
@@ -801,6 +805,44 @@ int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int
   GemmArgs g{};
   g.A = a;
   g.B = b;
+  g.M = M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.c32 = c;
+  hipError_t e = launch_gemm(EPI_RAW_I32, g, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_tile_weights(const int8_t *q, int64_t n_out, int64_t k_in, int8_t *q_tiled, void *stream) {
+  const char *fn = "h3k_tile_weights";
+  H3K_CHECK_PTR(q);
+  H3K_CHECK_PTR(q_tiled);
+  if (n_out <= 0 || k_in <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (n_out % 16 || k_in % 64)
+    return fail(H3K_EINVAL, "%s: need n_out %% 16 == 0 and k_in %% 64 == 0", fn);
+  if (n_out > (1 << 20) || k_in > (1 << 20)) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
+  const uintptr_t a0 = (uintptr_t)q, a1 = a0 + (uintptr_t)(n_out * k_in);
+  const uintptr_t b0 = (uintptr_t)q_tiled, b1 = b0 + (uintptr_t)(n_out * k_in);
+  if (a0 < b1 && b0 < a1) return fail(H3K_EINVAL, "%s: q and q_tiled overlap", fn);
+  if ((a0 | b0) & 15) return fail(H3K_EINVAL, "%s: q and q_tiled must be 16-byte aligned", fn);
+  hipError_t e = launch_tile_weights(q, n_out, k_in, q_tiled, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(H3K_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return H3K_OK;
+}
+
+int h3k_gemm_i8_i32_tiled(const int8_t *a, const int8_t *b_tiled, int32_t *c, int64_t M,
+                          int64_t N, int64_t K, void *stream) {
+  const char *fn = "h3k_gemm_i8_i32_tiled";
+  H3K_CHECK_PTR(a);
+  H3K_CHECK_PTR(b_tiled);
+  H3K_CHECK_PTR(c);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(H3K_EINVAL, "%s: sizes must be positive", fn);
+  if (N % 256 || K % 128) return fail(H3K_EUNSUPPORTED, "%s: need N %% 256 == 0 and K %% 128 == 0", fn);
+  if (N > (1 << 20) || K > (1 << 20) || M > ((int64_t)1 << 26)) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
+  GemmArgs g{};
+  g.A = a;
+  g.Bt = b_tiled;
   g.M = M;
   g.N = (int)N;
   g.K = (int)K;

@@ -180,6 +180,9 @@ enum EpiKind { EPI_RAW_I32 = 0, EPI_QKV = 1, EPI_GELU = 2, EPI_RESID = 3 };
 struct GemmArgs {
   const void *A;       // int8 or bf16 [M, K]
   const void *B;       // int8 or bf16 [N, K]
+  // int8 weights in the tiled layout of h3k_tile_weights; when set (int8 operands), the
+  // one-wave-per-SIMD kernel reads them and B is not used
+  const int8_t *Bt = nullptr;
   int64_t M;
   int N, K;            // K in elements
   bool bf16_ops;       // bf16 operands (fp32 accumulation, no dequant scales)
@@ -202,6 +205,8 @@ struct GemmArgs {
   const float *gate;
 };
 hipError_t launch_gemm(EpiKind kind, const GemmArgs &a, hipStream_t s);
+// int8 weights [N, K] row-major -> the tiled layout (N % 16 == 0, K % 64 == 0)
+hipError_t launch_tile_weights(const int8_t *q, int64_t N, int64_t K, int8_t *qt, hipStream_t s);
 
 // Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per device
 // (the attribute is per device); `done` holds one bit per device id (< 64).

@@ -154,6 +154,9 @@ constexpr int kStageSwz = 64 * 128;
 template <int EPI>
 constexpr bool kSwzStage = EPI != EPI_QKV;
 
+__device__ __forceinline__ float fma_e(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_e(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
 // Epilogue of one wave's TN x TM block of 16x16 accumulator tiles. acc[i][j][r] = C[m][n]
 // with m = token m_base + 16 j + (lane & 15) and n = channel n_base + 16 i + 4 (lane >> 4) + r.
 // Loads use token rows clamped to M - 1; only the stores test m < M.
@@ -358,8 +361,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, AccT (&acc)[TN]
             for (int p = 0; p < 2; ++p) {
               const CS cs = c.cs[j][p];
               const E u0 = y[2 * p], u1 = y[2 * p + 1];
-              y[2 * p] = u0 * cs.x - u1 * cs.y;
-              y[2 * p + 1] = u0 * cs.y + u1 * cs.x;
+              // one fused multiply-add each, in a fixed order: left to the compiler, the two
+              // products of a difference can be fused either way, and the choice differed
+              // between kernels instantiating this epilogue (one ulp where they cancel)
+              y[2 * p] = fma_e(u0, (E)cs.x, -(u1 * (E)cs.y));
+              y[2 * p + 1] = fma_e(u0, (E)cs.y, u1 * (E)cs.x);
             }
             if (sec == 0) {
 #pragma unroll
@@ -597,6 +603,220 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
 #undef H3K_PP_READ
 #undef H3K_PP_MFMA
 
+// ------------------------------------------------------------------ one-wave-per-SIMD kernel
+// The same 256 x 256 work-group tile and tile order with four waves, one per SIMD. Wave w
+// owns weight rows [64 w, 64 w + 64) of the tile and all 256 tokens: 4 x 16 accumulator
+// tiles, 256 registers, held in the accumulation registers (AGPRs) by issuing the MFMAs as
+// inline assembly whose accumulator operand is constrained to them (left to the compiler,
+// that layout turned into register moves around every MFMA).
+//
+// Operands. The weights come in the tiled layout of h3k_tile_weights: each MFMA fragment
+// (16 rows x 64 bytes of K) is one contiguous kilobyte in which lane l's 16 bytes sit at
+// offset 16 l, so a fragment is one whole-line 16-byte-per-lane load straight into
+// registers; every weight row belongs to one wave, so nothing is loaded twice. Only the
+// tokens go through LDS, in a ring of W4_NS stages of 128 bytes of K (the copies and the
+// fragment layout of the ping-pong kernel): that halves the LDS writes per multiply, which
+// run at a quarter of the read rate, and cuts the fragment reads per multiply by a third.
+//
+// Schedule of stage s (K steps 2 s and 2 s + 1), inside each wave:
+//   step 2 s:   64 MFMAs; after the four that use token fragment j, fragment j of step
+//               2 s + 1 is read into the same registers; the eight weight fragments of
+//               stage s + 1 are loaded (A ring of two stages, by parity);
+//   barrier:    each wave first waits for its copies of stage s + 1 (issued two stages
+//               earlier), so after it stage s + 1 is complete and stage s - 1 is free;
+//   step 2 s+1: 64 MFMAs; fragment j of step 2 s + 2 (stage s + 1) read likewise; the copies
+//               of stage s + W4_NS - 1 go into the buffer stage s - 1 left.
+// Every stage issues the same loads: past the last stage they re-read the last stage into
+// registers and a buffer that nothing reads as data, so the body has no branches (a branch
+// there made the compiler spill). After the last stage the next tile's first stages are
+// copied and its first weight fragments loaded before the epilogue, so their latency
+// overlaps the epilogue's. The epilogue runs as four 64-token slices through the generic
+// one, staging in the buffer the next tile fills last.
+constexpr int W4_NS = 4;               // LDS stages of the token operand
+constexpr int W4_STG = 256 * PP_SB;    // 32 KB: 256 token rows x 128 bytes of K
+
+template <int EPI>
+constexpr int w4_stage_bytes() { return kSwzStage<EPI> ? kStageSwz : kStageBytes; }
+template <int EPI>
+constexpr int w4_lds_bytes() {
+  return W4_NS * W4_STG > (W4_NS - 1) * W4_STG + 4 * w4_stage_bytes<EPI>()
+             ? W4_NS * W4_STG
+             : (W4_NS - 1) * W4_STG + 4 * w4_stage_bytes<EPI>();
+}
+
+// acc += w x^T on the matrix cores, accumulator in AGPRs; the zero form starts a tile
+__device__ __forceinline__ void mma_i8_agpr(v4i &acc, const v4i &w, const v4i &x) {
+  asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(w), "v"(x));
+}
+__device__ __forceinline__ void mma_i8_agpr_zero(v4i &acc, const v4i &w, const v4i &x) {
+  asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(acc) : "v"(w), "v"(x));
+}
+
+template <int EPI, bool OUTF32, bool RESF32, bool OH>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const GemmArgs a) {
+  constexpr int NS = W4_NS;
+  constexpr bool SWZ = kSwzStage<EPI>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ntiles = (int64_t)(a.N / 256) * ((a.M + 255) / 256);
+  const int K = a.K, ksteps = K / 64, ns = K / PP_SB;
+  // copy lane: row cr of an 8-row group, global chunk cc (stored at chunk position lane % 8)
+  const int cr = lane >> 3, cc = (lane & 7) ^ cr;
+  const int frag_off = (lane & 15) * PP_SB + (((lane >> 4) ^ (lane & 7)) * 16);
+  uint8_t *stage_ep = smem + (NS - 1) * W4_STG + wave * w4_stage_bytes<EPI>();
+
+  int64_t t = blockIdx.x, m0;
+  int n0;
+  tile_origin<256, 256>(a, t, m0, n0);
+  // Buffer resources based at the tile's first token row and at the wave's first weight
+  // fragment row, so 32-bit offsets suffice: token rows past M read row M - 1 (they only
+  // feed accumulator rows that are never stored).
+  __amdgpu_buffer_rsrc_t xrs, wrs;
+  uint32_t xo[8];
+  auto setup = [&](int64_t tm0, int tn0) {
+    xrs = __builtin_amdgcn_make_buffer_rsrc((void *)((const int8_t *)a.A + tm0 * K), (short)0,
+                                            (int)0xffffffffu, 0x00020000);
+    wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.Bt + (int64_t)(tn0 / 16 + 4 * wave) * ksteps * 1024), (short)0,
+        (int)0xffffffffu, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t m = tm0 + (wave + 4 * q) * 8 + cr;
+      xo[q] = (uint32_t)(((m < a.M ? m : a.M - 1) - tm0) * K + cc * 16);
+    }
+  };
+  v4i A[2][2][4];  // weight fragments [stage parity][step in stage][16-row block]
+  auto load_a = [&](int p, int h, int i, int st) {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(
+        wrs, (uint32_t)(lane * 16), (uint32_t)((i * ksteps + 2 * st + h) * 1024), 0);
+    if (p == 0) A[0][h][i] = v; else A[1][h][i] = v;
+  };
+  auto copy = [&](int q, int st) {  // 8 token rows of stage st (one kilobyte of LDS)
+    uint8_t *dst = smem + (st % NS) * W4_STG + (wave + 4 * q) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void *)dst,
+                                             16, xo[q] + (uint32_t)st * PP_SB, 0, 0, 0);
+  };
+  // the first stages of a tile: copies of stages 0 .. NS-2, weight fragments of stage 0
+  auto prologue = [&]() {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) {
+      const int sc = st < ns ? st : ns - 1;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) copy(q, sc);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_a(0, h, i, 0);
+  };
+  v4i acc[4][4][4];  // [64-token slice g][16-row weight block i][token block j within g]
+  v4i B[16];
+
+  auto stage = [&](int s, auto P, auto FIRST) {
+    constexpr int p = decltype(P)::value;
+    constexpr bool first = decltype(FIRST)::value;
+    const uint8_t *cur = smem + (s % NS) * W4_STG;
+    const uint8_t *nxt = smem + ((s + 1) % NS) * W4_STG;
+    const int sa = s + 1 < ns ? s + 1 : ns - 1;            // weight fragments of stage s+1
+    const int sc = s + NS - 1 < ns ? s + NS - 1 : ns - 1;  // token copies of stage s+NS-1
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (first) mma_i8_agpr_zero(acc[j >> 2][i][j & 3], A[p][0][i], B[j]);
+        else mma_i8_agpr(acc[j >> 2][i][j & 3], A[p][0][i], B[j]);
+      }
+      B[j] = *(const v4i *)(cur + (frag_off ^ 64) + j * 16 * PP_SB);
+      if (j < 8) load_a(p ^ 1, j >> 2, j & 3, sa);
+    }
+    // this wave's copies of stage s+1 are complete: after them it issued the weight
+    // fragments of stage s+1 (8) and, for each stage in between, copies and fragments (16)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 + 16 * (NS - 3)));
+    H3K_PP_SYNC();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mma_i8_agpr(acc[j >> 2][i][j & 3], A[p][1][i], B[j]);
+      B[j] = *(const v4i *)(nxt + frag_off + j * 16 * PP_SB);
+      if (j & 1) copy(j >> 1, sc);
+    }
+  };
+
+  setup(m0, n0);
+  prologue();
+  for (;;) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    H3K_PP_SYNC();
+#pragma unroll
+    for (int j = 0; j < 16; ++j) B[j] = *(const v4i *)(smem + frag_off + j * 16 * PP_SB);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using F0 = std::integral_constant<bool, false>;
+    stage(0, P0{}, std::integral_constant<bool, true>{});
+    int s = 1;
+    if (ns > 1) {
+      stage(1, P1{}, F0{});
+      s = 2;
+    }
+    for (; s + 1 < ns; s += 2) {
+      stage(s, P0{}, F0{});
+      stage(s + 1, P1{}, F0{});
+    }
+    if (s < ns) stage(s, P0{}, F0{});
+    // the last MFMAs' results are read by the epilogue: wait states for the matrix pipe
+    asm volatile("s_nop 15\n s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
+    // every wave is done with this tile's stages before the next tile's copies land
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    H3K_PP_SYNC();
+    const int64_t tn = t + gridDim.x;
+    const bool more = tn < ntiles;
+    int64_t m0n = 0;
+    int n0n = 0;
+    if (more) {
+      tile_origin<256, 256>(a, tn, m0n, n0n);
+      setup(m0n, n0n);
+      prologue();
+    }
+    static_for<4>([&](auto G) {
+      constexpr int g = G;
+      // an ordering point per slice: its accumulators are read after the wait states above
+      // and after the previous slice's stores, not all at once (which would spill)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[g][i][j]));
+      gemm_epilogue<4, 4, false, EPI, OUTF32, RESF32, OH, SWZ>(a, acc[g], n0 + 64 * wave,
+                                                               m0 + 64 * g, lane, stage_ep);
+    });
+    if (!more) break;
+    t = tn;
+    m0 = m0n;
+    n0 = n0n;
+  }
+}
+
+// int8 weights [N, K] -> tiled: 16-byte chunk c of the output holds row
+// 16 (c / 64 / (K / 64)) + (c % 64) % 16, bytes 64 ((c / 64) % (K / 64)) + 16 ((c % 64) / 16) ..+15
+__global__ __launch_bounds__(256) void tile_weights_kernel(const int8_t *__restrict__ q, int64_t N,
+                                                           int64_t K, int8_t *__restrict__ qt) {
+  const int64_t KB = K / 64, chunks = N * K / 16;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t l = c & 63, tile = c >> 6;
+    const int64_t nb = tile / KB, kb = tile - nb * KB;
+    const int64_t row = nb * 16 + (l & 15), col = kb * 64 + (l >> 4) * 16;
+    *(uint4 *)(qt + c * 16) = *(const uint4 *)(q + row * K + col);
+  }
+}
+
+hipError_t launch_tile_weights(const int8_t *q, int64_t N, int64_t K, int8_t *qt, hipStream_t s) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 64) return hipErrorInvalidValue;
+  const int64_t chunks = N * K / 16;
+  const int64_t blocks = (chunks + 255) / 256 < 8192 ? (chunks + 255) / 256 : 8192;
+  tile_weights_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(q, N, K, qt);
+  return hipGetLastError();
+}
+
 // compute units of the current device, queried once per device
 static hipError_t compute_units(int *n) {
   static std::atomic<int> cached[64];  // zero-initialised (static storage)
@@ -635,8 +855,28 @@ static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int EPI, bool OUTF32, bool RESF32, bool OH>
+static hipError_t run_gemm_w4(const GemmArgs &a, hipStream_t s) {
+  auto kern = gemm_w4_kernel<EPI, OUTF32, RESF32, OH>;
+  constexpr size_t lds = (size_t)w4_lds_bytes<EPI>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static std::atomic<uint64_t> lds_set{0};
+  if (hipError_t e = ensure_dynamic_lds((const void *)kern, (int)lds, lds_set); e != hipSuccess)
+    return e;
+  const int64_t nwg = ((a.M + 255) / 256) * (a.N / 256);
+  int n_cu = 0;
+  if (hipError_t e = compute_units(&n_cu); e != hipSuccess) return e;
+  const int64_t full = n_cu >= 8 ? (n_cu & ~7) : n_cu;  // keeps tile % 8 == XCD
+  const int64_t grid = nwg < full ? nwg : full;
+  kern<<<dim3((unsigned)grid), dim3(256), lds, s>>>(a);
+  return hipGetLastError();
+}
+
 template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH = false>
 static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
+  if constexpr (!BF16) {
+    if (a.Bt) return run_gemm_w4<EPI, OUTF32, RESF32, OH>(a, s);
+  }
   return run_gemm_pp<BF16, EPI, OUTF32, RESF32, OH>(a, s);
 }
 // instantiated type combinations (operands -> outputs):

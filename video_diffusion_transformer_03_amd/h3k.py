@@ -47,7 +47,7 @@ class Dims(C.Structure):
 class BlockWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "w_ada", "w_qkv", "s_qkv", "w_o", "s_o", "w_up", "s_up", "w_down", "s_down",
-        "wb_qkv", "wb_o", "wb_up", "wb_down")]
+        "wb_qkv", "wb_o", "wb_up", "wb_down", "wt_qkv", "wt_o", "wt_up", "wt_down")]
 
 
 class WsLayout(C.Structure):
@@ -86,6 +86,8 @@ def lib() -> C.CDLL:
             "h3k_ln_modulate_quant": (C.c_int, [vp, C.c_int, vp, vp, i64, i32, f32, vp, vp, vp]),
             "h3k_row_quantize": (C.c_int, [vp, C.c_int, i64, i32, vp, vp, vp]),
             "h3k_gemm_i8_i32": (C.c_int, [vp, vp, vp, i64, i64, i64, vp]),
+            "h3k_gemm_i8_i32_tiled": (C.c_int, [vp, vp, vp, i64, i64, i64, vp]),
+            "h3k_tile_weights": (C.c_int, [vp, i64, i64, vp, vp]),
             "h3k_token_pair": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, i32, vp]),
             "h3k_token_unpair": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, i32, vp]),
             "h3k_last_error": (C.c_char_p, []),
@@ -207,11 +209,16 @@ class BlockWeights:
     wb_o: Optional[torch.Tensor] = None
     wb_up: Optional[torch.Tensor] = None
     wb_down: Optional[torch.Tensor] = None
+    wt_qkv: Optional[torch.Tensor] = None
+    wt_o: Optional[torch.Tensor] = None
+    wt_up: Optional[torch.Tensor] = None
+    wt_down: Optional[torch.Tensor] = None
 
     def specs(self, dims: "Dims", flags: int = 0) -> list:
         """(tensor, name, dtype, shape) of every field: the tensors the flags' path reads are
-        required: w_ada bf16 [6d, d_cond]; int8 codes [N, K] with fp32 scales [N] for the W8A8
-        projections; bf16 [N, K] originals for the bf16 ones. The others are checked if set."""
+        required: w_ada bf16 [6d, d_cond]; int8 codes [N, K] (row-major w_*, or tiled wt_*)
+        with fp32 scales [N] for the W8A8 projections; bf16 [N, K] originals for the bf16
+        ones. The others are checked if set."""
         d, F = dims.d, dims.d_ff
         shapes = {"qkv": (3 * d, d), "o": (d, d), "up": (F, d), "down": (d, F)}
         bf16_proj = {"qkv": bool(flags & (F_BF16_GEMM | F_BF16_QKV)),
@@ -222,9 +229,12 @@ class BlockWeights:
         for k, shp in shapes.items():
             get_q = self.__dict__.get if bf16_proj[k] else (lambda f: self._req(f))
             get_b = (lambda f: self._req(f)) if bf16_proj[k] else self.__dict__.get
-            sp["w_" + k] = (get_q("w_" + k), "w_" + k, torch.int8, shp)
+            tiled = self.__dict__.get("wt_" + k) is not None
+            sp["w_" + k] = (self.__dict__.get("w_" + k) if tiled else get_q("w_" + k), "w_" + k,
+                            torch.int8, shp)
             sp["s_" + k] = (get_q("s_" + k), "s_" + k, torch.float32, shp[:1])
             sp["wb_" + k] = (get_b("wb_" + k), "wb_" + k, torch.bfloat16, shp)
+            sp["wt_" + k] = (self.__dict__.get("wt_" + k), "wt_" + k, torch.int8, shp)
         return [sp[f] for f, _ in BlockWeightsC._fields_]
 
     def c_struct(self, dims: Optional["Dims"] = None, flags: int = 0) -> BlockWeightsC:
@@ -253,13 +263,35 @@ def quantize_weights(w: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.
     return q, s
 
 
-def quantize_block(wb: Dict[str, torch.Tensor], keep_bf16: bool = False, stream=None) -> BlockWeights:
-    """BlockWeights from dense bf16 device weights {w_ada, w_qkv, w_o, w_up, w_down}."""
+def tile_weights(q: torch.Tensor, stream=None) -> torch.Tensor:
+    """int8 weights [N, K] (row-major) in the tiled layout of h3k_tile_weights, as an int8
+    tensor of the same shape (its bytes are the tiles in order, not rows)."""
+    if q.dim() != 2:
+        raise ValueError("q must be 2-D [n_out, k_in]")
+    n, k = q.shape
+    pq = _dev(q, "q", torch.int8, (n, k))
+    out = torch.empty_like(q)
+    _check(lib().h3k_tile_weights(pq, n, k, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def quantize_block(wb: Dict[str, torch.Tensor], keep_bf16: bool = False, tiled: bool = True,
+                   rowmajor: bool = True, stream=None) -> BlockWeights:
+    """BlockWeights from dense bf16 device weights {w_ada, w_qkv, w_o, w_up, w_down}: int8
+    codes and scales, with the codes also in the tiled layout (tiled, the block's faster
+    GEMM path) and/or row-major (rowmajor: what h3k_quantize_weights returns, and what the
+    row-major GEMM path reads); keep_bf16 keeps the dense originals for the bf16 flags."""
+    if not (tiled or rowmajor):
+        raise ValueError("quantize_block: tiled and rowmajor cannot both be False")
     out = BlockWeights(w_ada=wb["w_ada"])
     for k in ("w_qkv", "w_o", "w_up", "w_down"):
         q, s = quantize_weights(wb[k], stream)
-        setattr(out, k, q)
         setattr(out, "s" + k[1:], s)
+        if tiled:
+            setattr(out, "wt" + k[1:], tile_weights(q, stream))
+        if rowmajor:
+            setattr(out, k, q)
+        del q
         if keep_bf16:
             setattr(out, "wb" + k[1:], wb[k])
     return out
@@ -512,6 +544,18 @@ def gemm_i8_i32(a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
     pa, pb = _ptrs((a, "a", torch.int8, None), (b, "b", torch.int8, (N, K)))
     c = torch.empty((M, N), dtype=torch.int32, device=a.device)
     _check(lib().h3k_gemm_i8_i32(pa, pb, c.data_ptr(), M, N, K, _stream(stream)))
+    return c
+
+
+def gemm_i8_i32_tiled(a: torch.Tensor, b_tiled: torch.Tensor, stream=None) -> torch.Tensor:
+    """gemm_i8_i32 with b in the tiled layout (tile_weights)."""
+    if a.dim() != 2 or b_tiled.dim() != 2:
+        raise ValueError("a and b_tiled must be 2-D")
+    M, K = a.shape
+    N = b_tiled.shape[0]
+    pa, pb = _ptrs((a, "a", torch.int8, None), (b_tiled, "b_tiled", torch.int8, (N, K)))
+    c = torch.empty((M, N), dtype=torch.int32, device=a.device)
+    _check(lib().h3k_gemm_i8_i32_tiled(pa, pb, c.data_ptr(), M, N, K, _stream(stream)))
     return c
 
 

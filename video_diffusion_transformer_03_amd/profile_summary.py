@@ -36,7 +36,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # kernel kind -> (source file, substring of the mangled kernel name, extra selector)
 KINDS = {
     "attention": ("k_attn.hip", "attn_v2_kernel"),
-    "gemm": ("k_gemm.hip", "gemm_pp_kernel"),
+    "gemm": ("k_gemm.hip", "gemm_"),
     "rows": ("k_rows.hip", "row_kernel"),
     "adaln": ("k_rows.hip", "adaln_kernel"),
 }
