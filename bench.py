@@ -324,6 +324,26 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = L * args.steps / (t1 - t0)
+    # the same step with bf16 attention operands (the configuration's literal "bf16 flash
+    # attention"; the default stores Q, K, V, P and O as fp16 at the same bytes and rate)
+    bf16_attn = None
+    if args.variant == "w8a8":
+        fb = flags | h3k.F_ATTN_BF16
+        wsb = h3k.alloc_workspace(h3k.workspace_bytes(dims, L, fb))
+        tb = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, fb, wsb, out), args.steps,
+                         args.warmup)
+        h3k.profile_enable(True)
+        for _ in range(args.steps):
+            h3k.block_forward(x, c, bw, dims, fb, wsb, out)
+        torch.cuda.synchronize()
+        pb = h3k.profile_read()
+        h3k.profile_enable(False)
+        na, ta = pb["attention"]
+        wk = kernel_work(wl, L)["attention"][1]
+        bf16_attn = {"ms_per_step": round(tb * 1e3, 4), "value": round(L / tb, 1),
+                     "attention_ms": round(ta / na, 5),
+                     "attention_frac": round(wk / (ta / na * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+        del wsb
     sclk = None if args.no_clock else clock_under_load(
         torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, out))
 
@@ -398,6 +418,8 @@ def main():
             "gemm_int8_frac": round(gemm_ops / (gemm_ms * 1e-3) / 1e12 / pk8, 4),
             "attention_frac": round(work["attention"][1] / (kernels["attention"]["ms_per_step"] * 1e-3) / 1e12 / pk16, 4)}
     # a plain torch device copy, for comparison (not a ceiling: the row kernels beat it)
+    if bf16_attn is not None:
+        result["with_bf16_attention"] = bf16_attn
     result["torch_copy_GBps"] = round(copy_gbps, 1)
     result["kernels"] = kernels
     if not args.no_extras and args.variant == "w8a8" and args.workload == "block_l16384":
