@@ -324,8 +324,8 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     value = L * args.steps / (t1 - t0)
-    # the same step with bf16 attention operands (the configuration's literal "bf16 flash
-    # attention"; the default stores Q, K, V, P and O as fp16 at the same bytes and rate)
+    # the same step with bf16 attention operands, reported beside the fp16 default (which
+    # stores Q, K, V, P and O as fp16 at the same bytes and instruction rate)
     bf16_attn = None
     if args.variant == "w8a8":
         fb = flags | h3k.F_ATTN_BF16

@@ -148,7 +148,8 @@ void plan(const h3k_dims *dm, int64_t L, uint32_t flags, h3k_ws_layout *w) {
   w->q = take(H * Lz * Dh * T);
   w->k = take(H * Lz * Dh * T);
   w->vt = take(H * Lz * Dh * T);
-  // O, x1 and g in the activation type (bf16; fp32 on the debug path)
+  // O (the attention's output type: fp16 or bf16), x1 and g (bf16): two bytes each, four on
+  // the debug path
   w->o = take(Lz * d * T);
   w->x1 = take(Lz * d * T);
   w->g = take(Lz * F * T);

@@ -10,6 +10,12 @@
 // Both instructions take 16 bytes of K per lane per operand, so one byte-addressed tile
 // pipeline serves both: a K step is 64 bytes (64 int8 or 32 bf16 elements).
 //
+// Two kernels share the epilogues. gemm_w4_kernel (int8 weights in the tiled layout of
+// h3k_tile_weights, the block's path): one wave per SIMD, accumulators in AGPRs, weights
+// straight to registers, tokens through LDS. gemm_pp_kernel (row-major weights, bf16
+// operands, the raw int8 GEMM entry point): eight waves in two ping-pong groups, both
+// operands through LDS. Their results are bit-identical.
+//
 // The matrix-core output is computed transposed (weights are the MFMA "A" operand): a
 // lane then holds four consecutive output channels of one token, which is what the
 // fused epilogues want -- RoPE rotates channel pairs (2i, 2i+1) inside one lane, and the
