@@ -14,7 +14,8 @@ and with the same meaning, with these differences:
   - a block's weights are any object or mapping with the field names of
     h3k_block_weights (w_ada; w_qkv, s_qkv, w_o, s_o, w_up, s_up, w_down, s_down as int8
     codes and fp32 scales; wb_qkv, wb_o, wb_up, wb_down as the dense matrices for the
-    bf16 projections, else None);
+    bf16 projections, else None); the tiled copies of the codes (wt_*), a layout the GPU
+    GEMM reads, are not read: the twin needs the row-major codes;
   - workspace and stream arguments are accepted and ignored.
 The return codes are those of the C ABI. The twin checks the method's own consistency
 conditions (H3K_EINVAL: sizes that do not fit together, a bad pairing range, a
