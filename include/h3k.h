@@ -140,6 +140,13 @@ typedef struct {
   const int8_t *wt_o;
   const int8_t *wt_up;
   const int8_t *wt_down;
+  const uint16_t *wbt_qkv; /* optional: the bf16 originals in the tiled layout (the bytes of
+                              each [N, K] bf16 matrix through h3k_tile_weights with
+                              k_in = 2K); a bf16 projection reads these when set, and its
+                              wb_* may then be NULL; bit-identical results either way   */
+  const uint16_t *wbt_o;
+  const uint16_t *wbt_up;
+  const uint16_t *wbt_down;
 } h3k_block_weights;
 
 /* Byte offsets of the intermediates inside a block workspace (for inspection). Arrays
@@ -352,7 +359,8 @@ int h3k_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int
  * W8A8 GEMMs: 16 x 64 tiles (16 output channels x 64 bytes of K), tile (nb, kb) at byte
  * 1024 (nb (k_in / 64) + kb), and inside a tile lane l's 16 bytes at 16 l: channel
  * 16 nb + l % 16, bytes 64 kb + 16 (l / 16) .. + 15. A permutation: nothing is computed.
- * q, q_tiled device, not overlapping; n_out % 16 == 0, k_in % 64 == 0. */
+ * bf16 weights [n_out, K] are tiled as their bytes (k_in = 2K). q, q_tiled device, not
+ * overlapping; n_out % 16 == 0, k_in % 64 == 0. */
 int h3k_tile_weights(const int8_t *q, int64_t n_out, int64_t k_in, int8_t *q_tiled, void *stream);
 
 /* h3k_gemm_i8_i32 with b given in the tiled layout of h3k_tile_weights (the kernel the

@@ -122,10 +122,13 @@ def test_block_zero_gates_identity(flags):
 
 @pytest.mark.parametrize("name,flags", [("tiny", 0), ("tiny", h3k.F_FP32_DEBUG), ("tiny", h3k.F_ATTN_BF16),
                                         ("tiny", h3k.F_BF16_OUT), ("tiny", h3k.F_BF16_QKV | h3k.F_BF16_OUT),
-                                        ("ragged", 0), ("ragged", h3k.F_FP32_DEBUG)])
+                                        ("tiny", h3k.F_BF16_GEMM),
+                                        ("ragged", 0), ("ragged", h3k.F_FP32_DEBUG),
+                                        ("ragged", h3k.F_BF16_QKV | h3k.F_BF16_OUT)])
 def test_block_tiled_weights_bitwise(name, flags):
     """Tiled weights (the one-wave-per-SIMD GEMM) and row-major weights (the ping-pong GEMM)
-    give bit-identical blocks: both accumulate exactly in int32 and share the epilogues."""
+    give bit-identical blocks: int8 products accumulate exactly in int32; bf16 products
+    accumulate in fp32 in the same K order in both kernels; the epilogues are shared."""
     wl = S.WORKLOADS["tiny"] if name == "tiny" else _wl("block_l4096", grid=(2, 36, 40))
     gen = "cpu" if name == "tiny" else "cuda"
     wb = {k: v.to("cuda") for k, v in S.block_weights_bf16(wl, 0, device=gen).items()}
@@ -133,6 +136,8 @@ def test_block_tiled_weights_bitwise(name, flags):
     bw_t = h3k.quantize_block(wb, keep_bf16=keep, tiled=True, rowmajor=False)
     bw_r = h3k.quantize_block(wb, keep_bf16=keep, tiled=False, rowmajor=True)
     assert bw_t.w_qkv is None and bw_r.wt_qkv is None
+    if keep:
+        assert bw_t.wb_qkv is None and bw_t.wbt_qkv is not None and bw_r.wbt_qkv is None
     xdt = torch.float32 if flags & h3k.F_FP32_DEBUG else torch.bfloat16
     x = S.activations(wl, device=gen).to("cuda").to(xdt)
     c = S.conditioning(wl, device=gen).to("cuda")

@@ -168,20 +168,20 @@ int check_weights(const char *fn, const h3k_block_weights *w, uint32_t flags) {
   H3K_CHECK_PTR(w->w_ada);
   const Prec p(flags);
   if (p.qkv) {
-    H3K_CHECK_PTR(w->wb_qkv);
+    if (!w->wb_qkv && !w->wbt_qkv) return fail(H3K_EINVAL, "%s: wb_qkv and wbt_qkv are both NULL", fn);
   } else {
     if (!w->w_qkv && !w->wt_qkv) return fail(H3K_EINVAL, "%s: w_qkv and wt_qkv are both NULL", fn);
     H3K_CHECK_PTR(w->s_qkv);
   }
   if (p.out) {
-    H3K_CHECK_PTR(w->wb_o);
+    if (!w->wb_o && !w->wbt_o) return fail(H3K_EINVAL, "%s: wb_o and wbt_o are both NULL", fn);
   } else {
     if (!w->w_o && !w->wt_o) return fail(H3K_EINVAL, "%s: w_o and wt_o are both NULL", fn);
     H3K_CHECK_PTR(w->s_o);
   }
   if (p.mlp) {
-    H3K_CHECK_PTR(w->wb_up);
-    H3K_CHECK_PTR(w->wb_down);
+    if (!w->wb_up && !w->wbt_up) return fail(H3K_EINVAL, "%s: wb_up and wbt_up are both NULL", fn);
+    if (!w->wb_down && !w->wbt_down) return fail(H3K_EINVAL, "%s: wb_down and wbt_down are both NULL", fn);
   } else {
     if (!w->w_up && !w->wt_up) return fail(H3K_EINVAL, "%s: w_up and wt_up are both NULL", fn);
     H3K_CHECK_PTR(w->s_up);
@@ -268,7 +268,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.qkv;
     a.A = p.qkv ? (const void *)at<uint16_t>(ws, lay.h) : (const void *)at<int8_t>(ws, lay.qa);
     a.B = p.qkv ? (const void *)w->wb_qkv : (const void *)w->w_qkv;
-    a.Bt = p.qkv ? nullptr : w->wt_qkv;
+    a.Bt = p.qkv ? (const int8_t *)w->wbt_qkv : w->wt_qkv;
     a.N = 3 * d;
     a.K = d;
     a.sa = at<float>(ws, lay.s_a);
@@ -312,7 +312,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.out;
     a.A = p.out ? (const void *)at<uint16_t>(ws, lay.o) : (const void *)at<int8_t>(ws, lay.qo);
     a.B = p.out ? (const void *)w->wb_o : (const void *)w->w_o;
-    a.Bt = p.out ? nullptr : w->wt_o;
+    a.Bt = p.out ? (const int8_t *)w->wbt_o : w->wt_o;
     a.N = d;
     a.K = d;
     a.sa = at<float>(ws, lay.s_o);
@@ -340,7 +340,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.mlp;
     a.A = p.mlp ? (const void *)at<uint16_t>(ws, lay.h2) : (const void *)at<int8_t>(ws, lay.qa2);
     a.B = p.mlp ? (const void *)w->wb_up : (const void *)w->w_up;
-    a.Bt = p.mlp ? nullptr : w->wt_up;
+    a.Bt = p.mlp ? (const int8_t *)w->wbt_up : w->wt_up;
     a.N = F;
     a.K = d;
     a.sa = at<float>(ws, lay.s_a2);
@@ -364,7 +364,7 @@ int block_impl(const char *fn, const void *x_in, void *x_out, const float *cond,
     a.bf16_ops = p.mlp;
     a.A = p.mlp ? (const void *)at<uint16_t>(ws, lay.g) : (const void *)at<int8_t>(ws, lay.qg);
     a.B = p.mlp ? (const void *)w->wb_down : (const void *)w->w_down;
-    a.Bt = p.mlp ? nullptr : w->wt_down;
+    a.Bt = p.mlp ? (const int8_t *)w->wbt_down : w->wt_down;
     a.N = d;
     a.K = F;
     a.sa = at<float>(ws, lay.s_g);

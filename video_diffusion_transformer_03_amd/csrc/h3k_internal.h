@@ -180,8 +180,8 @@ enum EpiKind { EPI_RAW_I32 = 0, EPI_QKV = 1, EPI_GELU = 2, EPI_RESID = 3 };
 struct GemmArgs {
   const void *A;       // int8 or bf16 [M, K]
   const void *B;       // int8 or bf16 [N, K]
-  // int8 weights in the tiled layout of h3k_tile_weights; when set (int8 operands), the
-  // one-wave-per-SIMD kernel reads them and B is not used
+  // weights in the tiled layout of h3k_tile_weights (int8 codes, or the bytes of bf16
+  // weights); when set, the one-wave-per-SIMD kernel reads them and B is not used
   const int8_t *Bt = nullptr;
   int64_t M;
   int N, K;            // K in elements

@@ -650,22 +650,30 @@ constexpr int w4_lds_bytes() {
              : (W4_NS - 1) * W4_STG + 4 * w4_stage_bytes<EPI>();
 }
 
-// acc += w x^T on the matrix cores, accumulator in AGPRs; the zero form starts a tile
-__device__ __forceinline__ void mma_i8_agpr(v4i &acc, const v4i &w, const v4i &x) {
+// acc += w x^T on the matrix cores, accumulator in AGPRs (int8 -> int32, or bf16 -> fp32
+// with the same 16 bytes of K per lane); the zero form starts a tile
+__device__ __forceinline__ void mma_agpr(v4i &acc, const v4i &w, const v4i &x) {
   asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(w), "v"(x));
 }
-__device__ __forceinline__ void mma_i8_agpr_zero(v4i &acc, const v4i &w, const v4i &x) {
+__device__ __forceinline__ void mma_agpr_zero(v4i &acc, const v4i &w, const v4i &x) {
   asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(acc) : "v"(w), "v"(x));
 }
+__device__ __forceinline__ void mma_agpr(v4f &acc, const v4i &w, const v4i &x) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(w), "v"(x));
+}
+__device__ __forceinline__ void mma_agpr_zero(v4f &acc, const v4i &w, const v4i &x) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(w), "v"(x));
+}
 
-template <int EPI, bool OUTF32, bool RESF32, bool OH>
+template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH>
 __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const GemmArgs a) {
+  using AccT = typename std::conditional<BF16, v4f, v4i>::type;
   constexpr int NS = W4_NS;
   constexpr bool SWZ = kSwzStage<EPI>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ntiles = (int64_t)(a.N / 256) * ((a.M + 255) / 256);
-  const int K = a.K, ksteps = K / 64, ns = K / PP_SB;
+  const int K = a.K * (BF16 ? 2 : 1), ksteps = K / 64, ns = K / PP_SB;  // K in bytes
   // copy lane: row cr of an 8-row group, global chunk cc (stored at chunk position lane % 8)
   const int cr = lane >> 3, cc = (lane & 7) ^ cr;
   const int frag_off = (lane & 15) * PP_SB + (((lane >> 4) ^ (lane & 7)) * 16);
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) load_a(0, h, i, 0);
   };
-  v4i acc[4][4][4];  // [64-token slice g][16-row weight block i][token block j within g]
+  AccT acc[4][4][4];  // [64-token slice g][16-row weight block i][token block j within g]
   v4i B[16];
 
   auto stage = [&](int s, auto P, auto FIRST) {
@@ -729,8 +737,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const GemmArgs a) {
     for (int j = 0; j < 16; ++j) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (first) mma_i8_agpr_zero(acc[j >> 2][i][j & 3], A[p][0][i], B[j]);
-        else mma_i8_agpr(acc[j >> 2][i][j & 3], A[p][0][i], B[j]);
+        if constexpr (first) mma_agpr_zero(acc[j >> 2][i][j & 3], A[p][0][i], B[j]);
+        else mma_agpr(acc[j >> 2][i][j & 3], A[p][0][i], B[j]);
       }
       B[j] = *(const v4i *)(cur + (frag_off ^ 64) + j * 16 * PP_SB);
       if (j < 8) load_a(p ^ 1, j >> 2, j & 3, sa);
@@ -742,7 +750,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mma_i8_agpr(acc[j >> 2][i][j & 3], A[p][1][i], B[j]);
+      for (int i = 0; i < 4; ++i) mma_agpr(acc[j >> 2][i][j & 3], A[p][1][i], B[j]);
       B[j] = *(const v4i *)(nxt + frag_off + j * 16 * PP_SB);
       if (j & 1) copy(j >> 1, sc);
     }
@@ -791,7 +799,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const GemmArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[g][i][j]));
-      gemm_epilogue<4, 4, false, EPI, OUTF32, RESF32, OH, SWZ>(a, acc[g], n0 + 64 * wave,
+      gemm_epilogue<4, 4, BF16, EPI, OUTF32, RESF32, OH, SWZ>(a, acc[g], n0 + 64 * wave,
                                                                m0 + 64 * g, lane, stage_ep);
     });
     if (!more) break;
@@ -861,9 +869,9 @@ static hipError_t run_gemm_pp(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI, bool OUTF32, bool RESF32, bool OH>
+template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH>
 static hipError_t run_gemm_w4(const GemmArgs &a, hipStream_t s) {
-  auto kern = gemm_w4_kernel<EPI, OUTF32, RESF32, OH>;
+  auto kern = gemm_w4_kernel<BF16, EPI, OUTF32, RESF32, OH>;
   constexpr size_t lds = (size_t)w4_lds_bytes<EPI>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   static std::atomic<uint64_t> lds_set{0};
@@ -880,9 +888,7 @@ static hipError_t run_gemm_w4(const GemmArgs &a, hipStream_t s) {
 
 template <bool BF16, int EPI, bool OUTF32, bool RESF32, bool OH = false>
 static hipError_t gemm_tiles(const GemmArgs &a, hipStream_t s) {
-  if constexpr (!BF16) {
-    if (a.Bt) return run_gemm_w4<EPI, OUTF32, RESF32, OH>(a, s);
-  }
+  if (a.Bt) return run_gemm_w4<BF16, EPI, OUTF32, RESF32, OH>(a, s);
   return run_gemm_pp<BF16, EPI, OUTF32, RESF32, OH>(a, s);
 }
 // instantiated type combinations (operands -> outputs):

@@ -47,7 +47,8 @@ class Dims(C.Structure):
 class BlockWeightsC(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "w_ada", "w_qkv", "s_qkv", "w_o", "s_o", "w_up", "s_up", "w_down", "s_down",
-        "wb_qkv", "wb_o", "wb_up", "wb_down", "wt_qkv", "wt_o", "wt_up", "wt_down")]
+        "wb_qkv", "wb_o", "wb_up", "wb_down", "wt_qkv", "wt_o", "wt_up", "wt_down",
+        "wbt_qkv", "wbt_o", "wbt_up", "wbt_down")]
 
 
 class WsLayout(C.Structure):
@@ -213,12 +214,16 @@ class BlockWeights:
     wt_o: Optional[torch.Tensor] = None
     wt_up: Optional[torch.Tensor] = None
     wt_down: Optional[torch.Tensor] = None
+    wbt_qkv: Optional[torch.Tensor] = None
+    wbt_o: Optional[torch.Tensor] = None
+    wbt_up: Optional[torch.Tensor] = None
+    wbt_down: Optional[torch.Tensor] = None
 
     def specs(self, dims: "Dims", flags: int = 0) -> list:
         """(tensor, name, dtype, shape) of every field: the tensors the flags' path reads are
         required: w_ada bf16 [6d, d_cond]; int8 codes [N, K] (row-major w_*, or tiled wt_*)
-        with fp32 scales [N] for the W8A8 projections; bf16 [N, K] originals for the bf16
-        ones. The others are checked if set."""
+        with fp32 scales [N] for the W8A8 projections; bf16 [N, K] originals (row-major wb_*,
+        or tiled wbt_*) for the bf16 ones. The others are checked if set."""
         d, F = dims.d, dims.d_ff
         shapes = {"qkv": (3 * d, d), "o": (d, d), "up": (F, d), "down": (d, F)}
         bf16_proj = {"qkv": bool(flags & (F_BF16_GEMM | F_BF16_QKV)),
@@ -230,11 +235,14 @@ class BlockWeights:
             get_q = self.__dict__.get if bf16_proj[k] else (lambda f: self._req(f))
             get_b = (lambda f: self._req(f)) if bf16_proj[k] else self.__dict__.get
             tiled = self.__dict__.get("wt_" + k) is not None
+            btiled = self.__dict__.get("wbt_" + k) is not None
             sp["w_" + k] = (self.__dict__.get("w_" + k) if tiled else get_q("w_" + k), "w_" + k,
                             torch.int8, shp)
             sp["s_" + k] = (get_q("s_" + k), "s_" + k, torch.float32, shp[:1])
-            sp["wb_" + k] = (get_b("wb_" + k), "wb_" + k, torch.bfloat16, shp)
+            sp["wb_" + k] = (self.__dict__.get("wb_" + k) if btiled else get_b("wb_" + k), "wb_" + k,
+                             torch.bfloat16, shp)
             sp["wt_" + k] = (self.__dict__.get("wt_" + k), "wt_" + k, torch.int8, shp)
+            sp["wbt_" + k] = (self.__dict__.get("wbt_" + k), "wbt_" + k, torch.bfloat16, shp)
         return [sp[f] for f, _ in BlockWeightsC._fields_]
 
     def c_struct(self, dims: Optional["Dims"] = None, flags: int = 0) -> BlockWeightsC:
@@ -264,14 +272,16 @@ def quantize_weights(w: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.
 
 
 def tile_weights(q: torch.Tensor, stream=None) -> torch.Tensor:
-    """int8 weights [N, K] (row-major) in the tiled layout of h3k_tile_weights, as an int8
-    tensor of the same shape (its bytes are the tiles in order, not rows)."""
+    """Weights [N, K] (row-major int8 codes, or bf16) in the tiled layout of
+    h3k_tile_weights, as a tensor of the same dtype and shape (its bytes are the tiles in
+    order, not rows; bf16 is tiled as its bytes)."""
     if q.dim() != 2:
         raise ValueError("q must be 2-D [n_out, k_in]")
     n, k = q.shape
-    pq = _dev(q, "q", torch.int8, (n, k))
+    pq = _dev(q, "q", (torch.int8, torch.bfloat16), (n, k))
     out = torch.empty_like(q)
-    _check(lib().h3k_tile_weights(pq, n, k, out.data_ptr(), _stream(stream)))
+    kb = k * q.element_size()
+    _check(lib().h3k_tile_weights(pq, n, kb, out.data_ptr(), _stream(stream)))
     return out
 
 
@@ -293,7 +303,10 @@ def quantize_block(wb: Dict[str, torch.Tensor], keep_bf16: bool = False, tiled: 
             setattr(out, k, q)
         del q
         if keep_bf16:
-            setattr(out, "wb" + k[1:], wb[k])
+            if tiled:
+                setattr(out, "wbt" + k[1:], tile_weights(wb[k], stream))
+            if rowmajor:
+                setattr(out, "wb" + k[1:], wb[k])
     return out
 
 
