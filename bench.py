@@ -211,8 +211,12 @@ def weight_bytes(wl):
     return out
 
 
-def clock_under_load(torch, fn, n=40):
-    """Median engine clock (MHz) sampled while n calls of fn run, or None if unreadable."""
+def clock_under_load(torch, fn, n=12, cycles=int(6e7)):
+    """Shader clock (MHz) sustained while n calls of fn run: a one-wave spin kernel
+    (torch.cuda._sleep, which waits for `cycles` ticks of the shader clock counter) runs on
+    a side stream of default priority alongside them, timed with events on that stream.
+    cycles / elapsed is the mean engine clock over the spin. Also returns the median of the
+    SMI clock readings sampled meanwhile (a coarser figure). None where unavailable."""
     import threading
     samples, stop = [], threading.Event()
 
@@ -223,17 +227,31 @@ def clock_under_load(torch, fn, n=40):
             except Exception:
                 return
             time.sleep(0.01)
-    th = threading.Thread(target=sample)
-    for _ in range(n):
-        fn()
-    th.start()
-    for _ in range(n):
+    for _ in range(2):
         fn()
     torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    th = threading.Thread(target=sample)
+    th.start()
+    spin_mhz = None
+    try:
+        with torch.cuda.stream(side):
+            e0.record(side)
+            torch.cuda._sleep(cycles)
+            e1.record(side)
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        spin_mhz = round(cycles / (ms * 1e-3) / 1e6, 1) if ms > 0 else None
+    except (AttributeError, RuntimeError):
+        spin_mhz = None
     stop.set()
     th.join()
     samples = sorted(v for v in samples if v > 0)
-    return samples[len(samples) // 2] if samples else None
+    return spin_mhz, (samples[len(samples) // 2] if samples else None)
 
 
 def main():
@@ -344,7 +362,7 @@ def main():
                      "attention_ms": round(ta / na, 5),
                      "attention_frac": round(wk / (ta / na * 1e-3) / 1e12 / PEAK["bf16"], 4)}
         del wsb
-    sclk = None if args.no_clock else clock_under_load(
+    sclk, smi_mhz = (None, None) if args.no_clock else clock_under_load(
         torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, out))
 
     work = kernel_work(wl, L)
@@ -404,7 +422,9 @@ def main():
                         "compute_units": props.multi_processor_count,
                         "hbm_gib": round(props.total_memory / 2**30, 1),
                         "max_clock_mhz": round(getattr(props, "clock_rate", 0) / 1000.0, 1) or None,
-                        "clock_under_load_mhz": sclk}
+                        "clock_under_load_mhz": sclk,
+                        "clock_method": "shader-clock spin kernel beside the block loop (cycles / time)",
+                        "smi_clock_sample_mhz": smi_mhz}
     if int8 and sclk:
         # the dense peaks recomputed at the clock observed under this load: CUs x clock x
         # 8192 int8 ops (4096 16-bit flops) per clock per CU
