@@ -214,28 +214,16 @@ def weight_bytes(wl):
 def clock_under_load(torch, fn, n=12, cycles=int(6e7)):
     """Shader clock (MHz) sustained while n calls of fn run: a one-wave spin kernel
     (torch.cuda._sleep, which waits for `cycles` ticks of the shader clock counter) runs on
-    a side stream of default priority alongside them, timed with events on that stream.
-    cycles / elapsed is the mean engine clock over the spin. Also returns the median of the
-    SMI clock readings sampled meanwhile (a coarser figure). None where unavailable."""
-    import threading
-    samples, stop = [], threading.Event()
-
-    def sample():
-        while not stop.is_set():
-            try:
-                samples.append(float(torch.cuda.clock_rate()))
-            except Exception:
-                return
-            time.sleep(0.01)
+    a side stream of default priority alongside them, timed with events on that stream;
+    cycles / elapsed is the mean engine clock over the spin. None where unavailable. (The
+    SMI clock reading, sampled instead, proved unreliable: it read anything from 166 to
+    2095 MHz under the same load.)"""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    th = threading.Thread(target=sample)
-    th.start()
-    spin_mhz = None
     try:
         with torch.cuda.stream(side):
             e0.record(side)
@@ -245,13 +233,9 @@ def clock_under_load(torch, fn, n=12, cycles=int(6e7)):
             fn()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        spin_mhz = round(cycles / (ms * 1e-3) / 1e6, 1) if ms > 0 else None
     except (AttributeError, RuntimeError):
-        spin_mhz = None
-    stop.set()
-    th.join()
-    samples = sorted(v for v in samples if v > 0)
-    return spin_mhz, (samples[len(samples) // 2] if samples else None)
+        return None
+    return round(cycles / (ms * 1e-3) / 1e6, 1) if ms > 0 else None
 
 
 def main():
@@ -345,7 +329,7 @@ def main():
     # the same step with bf16 attention operands, reported beside the fp16 default (which
     # stores Q, K, V, P and O as fp16 at the same bytes and instruction rate)
     bf16_attn = None
-    if args.variant == "w8a8":
+    if args.variant == "w8a8" and not args.no_extras:
         fb = flags | h3k.F_ATTN_BF16
         wsb = h3k.alloc_workspace(h3k.workspace_bytes(dims, L, fb))
         tb = _time_steps(torch, lambda: h3k.block_forward(x, c, bw, dims, fb, wsb, out), args.steps,
@@ -362,7 +346,7 @@ def main():
                      "attention_ms": round(ta / na, 5),
                      "attention_frac": round(wk / (ta / na * 1e-3) / 1e12 / PEAK["bf16"], 4)}
         del wsb
-    sclk, smi_mhz = (None, None) if args.no_clock else clock_under_load(
+    sclk = None if args.no_clock else clock_under_load(
         torch, lambda: h3k.block_forward(x, c, bw, dims, flags, ws, out))
 
     work = kernel_work(wl, L)
@@ -423,8 +407,7 @@ def main():
                         "hbm_gib": round(props.total_memory / 2**30, 1),
                         "max_clock_mhz": round(getattr(props, "clock_rate", 0) / 1000.0, 1) or None,
                         "clock_under_load_mhz": sclk,
-                        "clock_method": "shader-clock spin kernel beside the block loop (cycles / time)",
-                        "smi_clock_sample_mhz": smi_mhz}
+                        "clock_method": "shader-clock spin kernel beside the block loop (cycles / time)"}
     if int8 and sclk:
         # the dense peaks recomputed at the clock observed under this load: CUs x clock x
         # 8192 int8 ops (4096 16-bit flops) per clock per CU
