@@ -88,6 +88,40 @@ def test_stack_graph_replays_tiny(tr):
     del g
 
 
+_GRAPH_FIRST = """
+import dataclasses, torch
+import synth_inputs as S
+from video_diffusion_transformer_03_amd import h3k
+wl = dataclasses.replace(S.WORKLOADS["tiny"], n_blocks=2)
+blocks = [h3k.quantize_block({k: v.cuda() for k, v in S.block_weights_bf16(wl, b).items()})
+          for b in range(2)]
+x = S.activations(wl).cuda(); c = S.conditioning(wl).cuda(); dims = h3k.dims_of(wl)
+torch.cuda.synchronize()
+g = h3k.stack_graph(x, c, blocks, dims, 0, 2)   # the first launch of every block kernel is recorded
+outs = []
+for _ in range(3):
+    outs.append(g.launch().clone())
+    torch.cuda.synchronize()
+eager = h3k.stack_forward(x, c, blocks, dims, 0, 2)
+torch.cuda.synchronize()
+assert all(torch.equal(o, eager) for o in outs)
+print("OK")
+"""
+
+
+def test_stack_graph_first_in_fresh_process():
+    """Recording a stack step before any block kernel has run in the process (each kernel's
+    one-time set-up then happens under stream capture) gives a graph equal to the eager
+    step on every replay."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _GRAPH_FIRST], cwd=root, capture_output=True, text=True,
+                       timeout=600, env=dict(os.environ, PYTHONPATH=root))
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stderr[-3000:]
+
+
 def _compose(wl, x, c, blocks, tr, on_block=None):
     """The stack composed from single-block calls (the same kernels, one call each)."""
     T, Hg, Wg = wl.grid
