@@ -610,7 +610,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const GemmArgs a) {
 #undef H3K_PP_MFMA
 
 // ------------------------------------------------------------------ one-wave-per-SIMD kernel
-// The same 256 x 256 work-group tile and tile order with four waves, one per SIMD. Wave w
+// int8 operands (int32 accumulators) or bf16 ones (fp32 accumulators; the same 16 bytes of K
+// per lane and fragment, so the same byte pipeline). The same 256 x 256 work-group tile and
+// tile order as the ping-pong kernel, with four waves, one per SIMD. Wave w
 // owns weight rows [64 w, 64 w + 64) of the tile and all 256 tokens: 4 x 16 accumulator
 // tiles, 256 registers, held in the accumulation registers (AGPRs) by issuing the MFMAs as
 // inline assembly whose accumulator operand is constrained to them (left to the compiler,
