@@ -638,8 +638,10 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   }
 
   // copy lanes: K instructions wave and wave + 8 (rows 4i .. 4i+3), V^T instructions wave
-  // and wave + 8 (rows 8i .. 8i+7). Keys past L read key L-1 (K) or the last valid 8-key
-  // chunk (V^T; L % 8 == 0); their scores are masked, so p = 0 meets finite values.
+  // and wave + 8 (rows 8i .. 8i+7). Keys past L (the partial last tile) read the next
+  // head's K rows, the next V^T row's first columns (L % 8 == 0: a 16-byte chunk never
+  // straddles rows) or, past the end of the tensor, zeros (below); their scores are
+  // masked, so p = 0 meets finite values.
   int kkey[2], kcol[2], vrow[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -652,45 +654,40 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
 // Buffer (MUBUF) copies rather than global_load_lds: for the latter the compiler assumes a
 // pending copy may also count against lgkmcnt and waits for every outstanding LDS read at
 // each fragment use, which would undo the read-ahead of the phases below. Byte offsets
-// within a head are at most 256 L - 16, below 2^32 for L <= 2^24 (the entry points' limit).
+// within a head are at most 256 L + 16 KB, below 2^32 for L <= 2^24 (the entry points'
+// limit). Each resource ends where its tensor ends (or 4 GB on, whichever is nearer): the
+// hardware returns zeros for bytes past it, so the partial last tile's copies need no
+// clamping and none reads past the allocation. Only the last head can reach the end, and
+// its bytes to the end (256 L) fit in 32 bits.
+  const uint64_t kv_end = (uint64_t)(H - head) * (uint64_t)L * (DH * 2);
+  const int kv_rec = (int)(uint32_t)(kv_end < 0xffffffffull ? kv_end : 0xffffffffull);
   const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, (int)0xffffffffu, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void *)Kh, (short)0, kv_rec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, (int)0xffffffffu, 0x00020000);
-  // Per-lane byte offsets of a full tile's copies, tile 0; a full tile adds its start as the
-  // instructions' scalar offset, so these copies cost no vector instructions. Only the last
-  // partial tiles take the clamped path.
+      __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, kv_rec, 0x00020000);
+  // Per-lane byte offsets of tile 0's copies; tile u adds its start as the instructions'
+  // scalar offset, so the copies cost no vector instructions and take no branch.
   uint32_t kvo[2], vvo[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     kvo[q] = ((uint32_t)kkey[q] * DH + (uint32_t)kcol[q]) * 2;
     vvo[q] = ((uint32_t)vrow[q] * Lu + (uint32_t)vcol) * 2;
   }
-  const int nfull = (int)(L / BK);  // key tiles 0 .. nfull - 1 hold BK valid keys
-  // piece 0, 1: K rows of copy instruction wave + 8 piece; piece 2, 3: V^T rows likewise
+  // piece 0, 1: K rows of copy instruction wave + 8 piece; piece 2, 3: V^T rows likewise.
+  // Stage u holds K tile u and V^T tile u - 1 (stage 0: tile 0); stages past the last tile
+  // repeat it into buffers no later stage's reads use.
   auto copy_piece = [&](int u, int piece) {
     uint8_t *dst = smem + (u % NB) * STAGE;
-    if (piece < 2 && u < nfull) {
+    if (piece < 2) {
+      const uint32_t kt = (uint32_t)(u < nkt ? u : nkt - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,
           (__attribute__((address_space(3))) void *)(dst + (wave + 8 * piece) * 1024), 16,
-          kvo[piece], (uint32_t)u * (BK * DH * 2), 0, 0);
-    } else if (piece >= 2 && (u >= 1 ? u - 1 : 0) < nfull) {
-      const uint32_t vt = u >= 1 ? (uint32_t)(u - 1) : 0u;  // V^T tile u - 1 (stage 0: tile 0)
+          kvo[piece], kt * (BK * DH * 2), 0, 0);
+    } else {
+      const uint32_t vt = (uint32_t)(u < 1 ? 0 : (u - 1 < nkt ? u - 1 : nkt - 1));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs,
           (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * (piece - 2)) * 1024),
           16, vvo[piece - 2], vt * (BK * 2), 0, 0);
-    } else if (piece < 2) {
-      const uint32_t kt0 = (uint32_t)(u < nkt ? u : nkt - 1) * BK;
-      const uint32_t key = min(kt0 + (uint32_t)kkey[piece], Lu - 1u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs,
-          (__attribute__((address_space(3))) void *)(dst + (wave + 8 * piece) * 1024), 16,
-          (key * DH + kcol[piece]) * 2, 0, 0, 0);
-    } else {
-      const uint32_t vt0 = (uint32_t)(u >= 1 ? u - 1 : 0) * BK;
-      const uint32_t col = min(vt0 + (uint32_t)vcol, Lu - 8u);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs,
-          (__attribute__((address_space(3))) void *)(dst + K_BYTES + (wave + 8 * (piece - 2)) * 1024),
-          16, ((uint32_t)vrow[piece - 2] * Lu + col) * 2, 0, 0, 0);
     }
   };
 #define H3K_V2_COPY(u_)                                                                        \
@@ -738,7 +735,8 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   // iteration j reads stage j + 1. Its copies of stage j + DIST go to the buffer of stage
   // j + DIST - NB <= j, last read in iteration j - 1 (or the prologue); the wave's copy of
   // stage j + 2 is complete at the barrier ending iteration j (DIST - 2 younger stages may
-  // still be in flight).
+  // still be in flight). Every iteration copies, also past the last stage read (nkt), so
+  // the count holds throughout.
 #define H3K_V2_ITER(CUR, NXT, j_, MASK)                                                        \
   {                                                                                            \
     const int jj = (j_);                                                                       \
@@ -751,16 +749,12 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
           cq[qt] = v4f{-m[qt], -m[qt], -m[qt], -m[qt]};                                        \
       }                                                                                        \
     }                                                                                          \
-    phase_s_exp<F16, QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, sl2, [&](int pc) {                   \
-      if (jj + DIST <= nkt) copy_piece(jj + DIST, pc);                                         \
-    });                                                                                        \
+    phase_s_exp<F16, QPRE>(NXT, CUR, pb, qf, sb_, koff, m, cq, sl2,                            \
+                           [&](int pc) { copy_piece(jj + DIST, pc); });                        \
     if (MASK) mask_tile(NXT, g, (int)min((int64_t)BK, L - (int64_t)(jj + 1) * BK));            \
     const bool grow_ = phase_pv_max<F16, QPRE>(o, pb, NXT, CUR, sb_, voff, m, mnew, sl2);           \
     pend = rescale_decision<QPRE, true>(grow_, mnew, m, alpha, shift, sl2);                    \
-    if (jj + DIST <= nkt)                                                                      \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                       \
-    else                                                                                       \
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));                                         \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(COPIES * (DIST - 2)));                         \
     H3K_PP_SYNC();                                                                             \
   }
 #define H3K_V2_LAST(CUR)                                                                       \
@@ -794,6 +788,8 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
     H3K_V2_ITER(sb, sa, j + 1, true);
   }
   H3K_V2_LAST(sa);
+  // the copies of the stages past nkt land before the work-group ends
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 #undef H3K_V2_ITER
 #undef H3K_V2_LAST
 #undef H3K_V2_COPY
