@@ -48,8 +48,9 @@
  *   - Token counts: L (and L / 2 where tokens are paired) must be a multiple of 8, else
  *     H3K_EUNSUPPORTED: the transposed V rows and the attention's key tiles move 8 tokens
  *     per 16-byte access. A grid whose product is not a multiple of 8 is padded by the
- *     caller. Any L that is a multiple of 8 is supported: partial 256-token GEMM tiles and
- *     partial 64-key attention tiles are masked.
+ *     caller. Any L that is a multiple of 8 and below 2^24 is supported: partial 256-token
+ *     GEMM tiles and partial 64-key attention tiles are masked. (Below 2^24 tokens a head's
+ *     K and V^T fit the 32-bit byte range of the attention's buffer loads.)
  */
 #ifndef H3K_H
 #define H3K_H
@@ -246,7 +247,7 @@ int h3k_block_forward_grid(const void *x_in, void *x_out, const float *cond,
  * stores Q that way, so that scores leave the matrix cores as base-2 exponents), and
  * softmax_scale is not applied again. Errors: H3K_EINVAL (null or misaligned pointers,
  * n_heads or L < 1, softmax_scale <= 0, unknown dtype or flags, H3K_F_Q_BASE2 with
- * H3K_DT_F32), H3K_EUNSUPPORTED (head_dim, L % 8, L > 2^24, n_heads > 65535). */
+ * H3K_DT_F32), H3K_EUNSUPPORTED (head_dim, L % 8, L >= 2^24, n_heads > 65535). */
 int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t n_heads,
                   int64_t L, int32_t head_dim, double softmax_scale, int dtype,
                   uint32_t flags, void *stream);

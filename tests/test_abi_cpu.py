@@ -315,8 +315,9 @@ def test_noalloc_validation():
 
 
 def test_token_count_rule():
-    """L must be a multiple of 8 (refused with a message naming the rule); any such L is
-    accepted, including ones that leave partial 256-token GEMM tiles and partial key tiles."""
+    """L must be a multiple of 8 (refused with a message naming the rule) and below 2^24; any
+    such L is accepted, including ones that leave partial 256-token GEMM tiles and partial key
+    tiles."""
     dm = tiny_dims(grid=(1, 1, 6))
     assert _block(dm, 6) == h3k.EUNSUPPORTED and "multiple of 8" in h3k.last_error()
     for grid in [(1, 1, 8), (3, 5, 8), (2, 3, 12), (1, 9, 40)]:  # 8, 120, 72, 360 tokens
@@ -326,6 +327,11 @@ def test_token_count_rule():
     lib = h3k.lib()
     assert lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, 2, 60, 64, 0.1, h3k.DT_F16, 0, None) == h3k.EUNSUPPORTED
     assert "multiple of 8" in h3k.last_error()
+    # and below 2^24 (a head's K and V^T then fit the attention loads' 32-bit byte range)
+    assert lib.h3k_attention(FAKE, FAKE, FAKE, FAKE, 1, 1 << 24, 128, 0.1, h3k.DT_F16, 0, None) == h3k.EUNSUPPORTED
+    assert "too large" in h3k.last_error()
+    assert _block(tiny_dims(grid=(1, 4096, 4096)), 1 << 24) == h3k.EUNSUPPORTED
+    assert "2^24" in h3k.last_error()
     # pairing needs L / 2 a multiple of 8 as well
     arr = (h3k.BlockWeightsC * 2)(*[h3k.BlockWeightsC(*([FAKE] * 9 + [None] * 4)) for _ in range(2)])
     dm = tiny_dims(grid=(1, 3, 8))  # 24 tokens, 12 after pairing

@@ -106,7 +106,7 @@ int check_dims(const char *fn, const h3k_dims *dm, int64_t L) {
   if (dm->d_cond % 8 || dm->d_cond > 8192)
     return fail(H3K_EUNSUPPORTED, "%s: d_cond must be a multiple of 8 and <= 8192", fn);
   if (L % 8) return fail(H3K_EUNSUPPORTED, "%s: L must be a multiple of 8", fn);
-  if (L > (int64_t)1 << 24) return fail(H3K_EUNSUPPORTED, "%s: L > 2^24 unsupported", fn);
+  if (L >= (int64_t)1 << 24) return fail(H3K_EUNSUPPORTED, "%s: L >= 2^24 unsupported", fn);
   return H3K_OK;
 }
 
@@ -543,7 +543,7 @@ int h3k_attention(const void *q, const void *k, const void *v, void *o, int32_t 
   if (n_heads <= 0 || L <= 0) return fail(H3K_EINVAL, "%s: n_heads and L must be positive", fn);
   if (head_dim != 64 && head_dim != 128) return fail(H3K_EUNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
   if (L % 8) return fail(H3K_EUNSUPPORTED, "%s: L must be a multiple of 8", fn);
-  if (L > (int64_t)1 << 24 || n_heads > 65535) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
+  if (L >= (int64_t)1 << 24 || n_heads > 65535) return fail(H3K_EUNSUPPORTED, "%s: sizes too large", fn);
   if (!(softmax_scale > 0.0)) return fail(H3K_EINVAL, "%s: softmax_scale must be positive", fn);
   hipStream_t s = (hipStream_t)stream;
   Launch l(H3K_K_ATTENTION, s, flags);

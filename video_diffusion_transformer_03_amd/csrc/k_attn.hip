@@ -653,12 +653,12 @@ __global__ __launch_bounds__(512) void attn_v2_kernel(const uint16_t *__restrict
   const int vcol = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
 // Buffer (MUBUF) copies rather than global_load_lds: for the latter the compiler assumes a
 // pending copy may also count against lgkmcnt and waits for every outstanding LDS read at
-// each fragment use, which would undo the read-ahead of the phases below. Byte offsets
-// within a head are at most 256 L + 16 KB, below 2^32 for L <= 2^24 (the entry points'
-// limit). Each resource ends where its tensor ends (or 4 GB on, whichever is nearer): the
-// hardware returns zeros for bytes past it, so the partial last tile's copies need no
-// clamping and none reads past the allocation. Only the last head can reach the end, and
-// its bytes to the end (256 L) fit in 32 bits.
+// each fragment use, which would undo the read-ahead of the phases below. Each resource
+// ends where its tensor ends, or 2^32 - 1 bytes on, whichever is nearer: the hardware
+// returns zeros for bytes past it, so the partial last tile's copies need no clamping and
+// none reads past the allocation. The entry points take L < 2^24, so a key or V^T column
+// below L lies below byte 256 L <= 2^32 - 2048 of its head (inside either bound), and the
+// last tile's copies, which reach at most byte 2^32 - 1, do not wrap the 32-bit offset.
   const uint64_t kv_end = (uint64_t)(H - head) * (uint64_t)L * (DH * 2);
   const int kv_rec = (int)(uint32_t)(kv_end < 0xffffffffull ? kv_end : 0xffffffffull);
   const __amdgpu_buffer_rsrc_t krs =
