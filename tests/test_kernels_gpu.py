@@ -195,6 +195,32 @@ def test_attention_16bit(H, L, Dh, dtype):
     check_rows(np64(o).reshape(L, H, Dh), _oracle_attn(q, k, vt), dtype, f"attention {dtype} H={H} L={L} Dh={Dh}")
 
 
+def _guarded(t, n_guard=16384):
+    """t on the GPU as a view of the start of a larger buffer whose remaining n_guard
+    elements (32 KB in a 16-bit dtype) hold NaN."""
+    buf = torch.full((t.numel() + n_guard,), float("nan"), dtype=t.dtype, device="cuda")
+    buf[:t.numel()] = t.reshape(-1).cuda()
+    return buf[:t.numel()].view(t.shape)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("H,L,Dh", [(1, 72, 128), (3, 200, 128), (2, 8, 64)])
+def test_attention_reads_stay_inside_the_tensors(H, L, Dh, dtype):
+    # The partial last key tile's keys past L read the next head's K rows and V^T's next row
+    # (finite values, weight 0) or, past the end of a tensor, zeros. Each tensor is followed
+    # by NaN in memory: had a load read past the tensor, a V^T NaN would reach O through
+    # 0 * NaN (K is masked by selection, so O checks V^T; Q rows past L are never stored).
+    q = randn((H, L, Dh), 81, 1.0, dtype)
+    k = randn((H, L, Dh), 82, 1.0, dtype)
+    vt = randn((H, Dh, L), 83, 1.0, dtype)
+    for flags, qm in [(0, 1.0), (h3k.F_Q_BASE2, math.log2(math.e) / math.sqrt(Dh))]:
+        qq = (q.float() * qm).to(dtype)
+        o = h3k.attention(_guarded(qq), _guarded(k), _guarded(vt), flags=flags)
+        assert bool(torch.isfinite(o).all())
+        check_rows(np64(o).reshape(L, H, Dh), _oracle_attn(qq, k, vt, 1.0 / qm), dtype,
+                   f"guarded {dtype} H={H} L={L} Dh={Dh} flags={flags}")
+
+
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("Dh", [64, 128])
 @pytest.mark.parametrize("base2", [False, True])
