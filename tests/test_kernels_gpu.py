@@ -61,8 +61,11 @@ def test_adaln_modulation(n_out, dc):
 
 
 # ----------------------------------------------------------------------------- LN + quant
+# widths that fill a lane's vectors (5120, 8192) and ones that leave the last vectors empty
+# (256; 6144 over four waves per row)
 @pytest.mark.parametrize("rows,cols,dtype", [(300, 256, torch.bfloat16), (257, 5120, torch.bfloat16),
-                                             (64, 8192, torch.bfloat16), (100, 5120, torch.float32)])
+                                             (64, 8192, torch.bfloat16), (100, 5120, torch.float32),
+                                             (77, 6144, torch.bfloat16)])
 def test_ln_modulate_quant(rows, cols, dtype):
     x = randn((rows, cols), 5, 1.0, dtype)
     x[:, 7] *= 20  # outlier channel
@@ -80,7 +83,8 @@ def test_ln_modulate_quant(rows, cols, dtype):
 # ----------------------------------------------------------------------------- row quant
 @pytest.mark.parametrize("rows,cols,dtype", [(129, 5120, torch.bfloat16), (33, 20480, torch.bfloat16),
                                              (50, 1024, torch.float32), (5, 32768, torch.bfloat16),
-                                             (129, 5120, torch.float16), (7, 20480, torch.float16)])
+                                             (129, 5120, torch.float16), (7, 20480, torch.float16),
+                                             (65, 1000, torch.bfloat16), (9, 9000, torch.float16)])
 def test_row_quantize(rows, cols, dtype):
     x = randn((rows, cols), 8, 3.0, dtype)
     x[2] = 0
