@@ -259,6 +259,20 @@ def test_block_ragged_full_width_sampled(flags, tol):
     check_forced(wl, r, rows, got, f"l2880 ragged flags={flags}")
 
 
+@pytest.mark.parametrize("flags,tol", [(0, TOL), (h3k.F_FP32_DEBUG, FP32_TOL)])
+def test_block_max_width(flags, tol):
+    # the largest widths the entry points take: d = 8192 (64 heads of 128), F = 32768 (the
+    # down projection's K), d_cond = 8192; 264 tokens leave a partial 256-token GEMM tile and
+    # a partial 64-key attention tile. Whole output against the oracle.
+    wl = _wl("block_l4096", d=8192, n_heads=64, d_ff=32768, d_cond=8192, grid=(1, 3, 88))
+    assert wl.L == 264
+    r = run_gpu(wl, flags, gen_device="cuda")
+    got = np64(r["out"])
+    err = rel_l2(got, oracle_full(wl, r, "w8a8"))
+    print(f"max width d=8192 F=32768 flags={flags}: rel-L2 {err:.3e}")
+    assert err <= tol
+
+
 @pytest.mark.parametrize("name,n_rows", [("block_l4096", 32), ("block_l16384", 24), ("block_l65536", 8)])
 def test_block_fp32_sampled(name, n_rows):
     # the fp32 debug path at each full-size workload (L = 65536: fp64 attention over 65536 keys

@@ -50,7 +50,7 @@ def test_quantize_golden_ties():
 
 
 # ----------------------------------------------------------------------------- AdaLN
-@pytest.mark.parametrize("n_out,dc", [(6 * 256, 256), (6 * 5120, 5120), (40, 8)])
+@pytest.mark.parametrize("n_out,dc", [(6 * 256, 256), (6 * 5120, 5120), (40, 8), (6 * 8192, 8192)])
 def test_adaln_modulation(n_out, dc):
     w = randn((n_out, dc), 3, 0.02)
     c = randn((dc,), 4, 1.0, torch.float32)
